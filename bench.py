@@ -1,0 +1,242 @@
+"""Benchmark of the whole hot path on synthetic Wan2.1-shaped inputs.
+
+One step = one pass of every stage over one batch already resident in HBM:
+cluster Q, cluster K (+V), centroid scores and pi, exact set + shared sample,
+fused exact+sampled attention, un-permute.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--exact 0.08] [--sample 0.08] [--no-cpu-baseline] [--sweep]
+
+value = effective TFLOP/s of the step: algorithmic attention flops (4 d per
+computed (query, column) pair over the exact and sampled columns, padding
+excluded) divided by the whole step's time.  The roofline entry is for the
+attention kernel alone, timed with HIP events on the stream it runs on.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
+METRIC = "ms/call + effective TFLOP/s (% bf16 MFMA peak), 14B-shaped 720p attention"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan14b_720p")
+    ap.add_argument("--exact", type=float, default=0.08)
+    ap.add_argument("--sample", type=float, default=0.08)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time the attention at every budget of the workload")
+    return ap.parse_args()
+
+
+def attention_flops(d, q_offsets, k_offsets, exact_groups, n_exact, n_sample):
+    """4 d sum_i n^q_i (|E_i| + n_sample_i), from the lists the step produced."""
+    import numpy as np
+    qo = q_offsets.cpu().numpy().astype(np.int64)
+    ko = k_offsets.cpu().numpy().astype(np.int64)
+    eg = exact_groups.cpu().numpy()
+    ne = n_exact.cpu().numpy()
+    ns = n_sample.cpu().numpy().astype(np.int64)
+    nq = np.diff(qo, axis=-1)
+    nk = np.diff(ko, axis=-1)
+    B, H, Cq, Ck = eg.shape
+    exact_keys = np.zeros((B, H, Cq), np.int64)
+    for b in range(B):
+        for h in range(H):
+            valid = np.arange(Ck)[None, :] < ne[b, h][:, None]
+            g = np.where(valid, eg[b, h], 0)
+            exact_keys[b, h] = (nk[b, h][g] * valid).sum(-1)
+    cols = exact_keys + ns
+    return float(4 * d * (nq * cols).sum()), float((nq * cols).sum())
+
+
+def cpu_baseline(w, q, k, v, E, m, seed):
+    """The oracle as it stands on one head of the workload: every stage on the whole
+    head except attention, which runs on a sample of query groups and is scaled to all
+    groups of the head by its share of the head's attention flops."""
+    import numpy as np
+    import oracle
+    d, N, Cq, Ck = w["d"], w["N"], w["Cq"], w["Ck"]
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    qh = q[:, :1].float().numpy()
+    kh = k[:, :1].float().numpy()
+    vh = v[:, :1].float().numpy()
+    t0 = time.perf_counter()
+    cq = oracle.cluster(qh, Cq, w["iters"])
+    ck = oracle.cluster(kh, Ck, w["iters"], companion=vh)
+    S, _ = oracle.probs(cq["centroids"], ck["centroids"], ck["offsets"], scale)
+    sel = oracle.select_sample(S, ck["offsets"], N, E, m, seed=seed)
+    t_pre = time.perf_counter() - t0
+    nq = np.diff(cq["offsets"][0, 0])
+    nk = np.diff(ck["offsets"][0, 0])
+    cols = np.array([nk[sel["exact_groups"][0, 0, i, :sel["n_exact"][0, 0, i]]].sum() + sel["n_sample"][0, 0, i]
+                     for i in range(Cq)], np.int64)
+    work = nq * cols
+    threads = oracle.num_threads()
+    order = np.argsort(-work)
+    pick = [i for i in order if work[i] > 0][:max(1, min(threads, Cq))]
+    gm = np.zeros((1, 1, Cq), np.uint8)
+    gm[0, 0, pick] = 1
+    t1 = time.perf_counter()
+    o_p, lse_p = oracle.attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
+                                  sel, m, scale, group_mask=gm)
+    t_att = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    oracle.unpermute(o_p, lse_p, cq["perm"])
+    t_un = time.perf_counter() - t2
+    frac = work[pick].sum() / work.sum()
+    t_head = t_pre + t_att / frac + t_un
+    flops_head = 4.0 * d * work.sum()
+    return {"value": flops_head / t_head / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": (f"1 of {w['H']} heads of {w.get('name')}: clustering, scores, selection and "
+                       f"un-permute on the whole head ({t_pre + t_un:.1f} s); attention on the "
+                       f"{len(pick)} heaviest query groups ({frac * 100:.1f} % of the head's attention flops, "
+                       f"{t_att:.1f} s) scaled to the head; fp64 C with OpenMP"),
+            "seconds_measured": round(t_pre + t_att + t_un, 2), "seconds_per_head_est": round(t_head, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_means_amd import isg
+    from block_sparse_attention_means_amd.synth import make_workload
+    from block_sparse_attention_means_amd.workloads import WORKLOADS, budget_keys
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = dict(WORKLOADS[args.workload])
+    w["name"] = args.workload
+    B, H, N, d = w.get("B", 1), w["H"], w["N"], w["d"]
+    E, m = budget_keys(args.exact, N), budget_keys(args.sample, N)
+    t0 = time.perf_counter()
+    q, k, v, _ = make_workload(w, seed=args.seed)
+    print(f"# inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    scale = isg.default_scale(d)
+    stream = torch.cuda.current_stream()
+    ws_c = torch.empty(isg.cluster_workspace_size(B, H, N, d, max(w["Cq"], w["Ck"])), device=dev, dtype=torch.uint8)
+    ws_a = torch.empty(isg.attention_workspace_size(B, H, N, w["Cq"], w["Ck"]), device=dev, dtype=torch.uint8)
+    stages = ["cluster_q", "cluster_k", "probs", "select_sample", "attention", "unpermute"]
+    ev = {s: [] for s in stages}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
+        if record:
+            marks[0].record(stream)
+        cq = isg.isg_cluster(qg, w["Cq"], w["iters"], workspace=ws_c)
+        if record:
+            marks[1].record(stream)
+        ck = isg.isg_cluster(kg, w["Ck"], w["iters"], companion=vg, workspace=ws_c)
+        if record:
+            marks[2].record(stream)
+        S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+        if record:
+            marks[3].record(stream)
+        sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, seed=args.seed)
+        if record:
+            marks[4].record(stream)
+        o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
+                                       ck["offsets"], sel, scale, workspace=ws_a)
+        if record:
+            marks[5].record(stream)
+        o, lse = isg.isg_unpermute(o_p, lse_p, cq["perm"])
+        if record:
+            marks[6].record(stream)
+            for si, s in enumerate(stages):
+                ev[s].append((marks[si], marks[si + 1]))
+        return cq, ck, sel, o
+
+    for _ in range(args.warmup):
+        cq, ck, sel, o = step(False)
+    torch.cuda.synchronize()
+    flops, pairs = attention_flops(d, cq["offsets"], ck["offsets"], sel["exact_groups"], sel["n_exact"],
+                                   sel["n_sample"])
+    print(f"# warmup done; attention {flops / 1e12:.2f} TFLOP per call", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
+    att_ms = stage_ms["attention"]
+    att_tflops = flops / (att_ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w["dtype"] == "bf16" else PEAK_FP32_TFLOPS
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w["dtype"],
+        "data": "synthetic (seeded Gaussian-mixture Q/K with 3-D locality bias, V ~ N(0,1); no model weights)",
+        "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "Cq": w["Cq"], "Ck": w["Ck"],
+                   "kmeans_iters": w["iters"], "exact_share": args.exact, "sample_share": args.sample,
+                   "exact_keys": E, "m": m, "seed": args.seed},
+        "attention_ms": round(att_ms, 3),
+        "attention_tflops": round(att_tflops, 2),
+        "attention_tflop_per_call": round(flops / 1e12, 4),
+        "stage_ms": {s: round(t, 3) for s, t in stage_ms.items()},
+        "roofline": {"bound": "mfma" if w["dtype"] == "bf16" else "alu", "achieved": round(att_tflops, 2),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(att_tflops / peak, 4), "traffic": None,
+                     "kernel": "isg_attention (attn_bf16_kernel + column-list and tile-table prep)"},
+    }
+    if args.sweep:
+        sweep = {}
+        for (es, ss) in w["sweep"]:
+            E2, m2 = budget_keys(es, N), budget_keys(ss, N)
+            S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+            sel2 = isg.isg_select_sample(S, ck["offsets"], N, E2, m2, seed=args.seed)
+            f2, _ = attention_flops(d, cq["offsets"], ck["offsets"], sel2["exact_groups"], sel2["n_exact"],
+                                    sel2["n_sample"])
+            for _ in range(2):
+                isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
+                                  sel2, scale, workspace=ws_a)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(5):
+                isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
+                                  sel2, scale, workspace=ws_a)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / 5
+            sweep[f"{int(es * 100)}+{int(ss * 100)}%"] = {"attention_ms": round(ms, 3),
+                                                           "tflops": round(f2 / ms / 1e9, 2),
+                                                           "frac_peak": round(f2 / ms / 1e9 / peak, 4)}
+        result["attention_sweep"] = sweep
+    if not args.no_cpu_baseline:
+        print("# timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, E, m, args.seed)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,108 @@
+// Internal helpers shared by the libisg translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "isg.h"
+
+// ---------------------------------------------------------------- host side
+isg_status isg_fail(isg_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+isg_status isg_check_launch(const char *what);
+
+#define ISG_REQUIRE(cond, status, ...)                     \
+    do {                                                   \
+        if (!(cond)) return isg_fail((status), __VA_ARGS__); \
+    } while (0)
+
+static inline size_t isg_align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ---------------------------------------------------------------- device side
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 <-> fp32 (bit-level, round to nearest even; inputs are finite).
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)
+{
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float *p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float *p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t *p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+
+// Map a launch-order block id to a logical tile id so that consecutive logical
+// tiles run on the same XCD (work-groups are dealt to the 8 XCDs round robin).
+// nblocks must be a multiple of 8.
+__device__ __forceinline__ int xcd_logical_block(int p, int nblocks)
+{
+    return (p & 7) * (nblocks >> 3) + (p >> 3);
+}
+
+// Exclusive block scan over `n` ints held in shared memory `a` (in place), using
+// `tmp` (>= blockDim.x ints) as scratch.  Returns the total.  All threads call it.
+__device__ __forceinline__ int block_exclusive_scan_int(int *a, int n, int *tmp)
+{
+    const int T = blockDim.x, tid = threadIdx.x;
+    const int per = (n + T - 1) / T;
+    const int lo = tid * per, hi = min(n, lo + per);
+    int s = 0;
+    for (int k = lo; k < hi; ++k) s += a[k];
+    tmp[tid] = s;
+    __syncthreads();
+    for (int off = 1; off < T; off <<= 1) {
+        int v = tid >= off ? tmp[tid - off] : 0;
+        __syncthreads();
+        tmp[tid] += v;
+        __syncthreads();
+    }
+    int run = tmp[tid] - s;
+    for (int k = lo; k < hi; ++k) {
+        int v = a[k];
+        a[k] = run;
+        run += v;
+    }
+    int total = tmp[T - 1];
+    __syncthreads();
+    return total;
+}
+
+__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t *a, int n, uint64_t *tmp)
+{
+    const int T = blockDim.x, tid = threadIdx.x;
+    const int per = (n + T - 1) / T;
+    const int lo = tid * per, hi = min(n, lo + per);
+    uint64_t s = 0;
+    for (int k = lo; k < hi; ++k) s += a[k];
+    tmp[tid] = s;
+    __syncthreads();
+    for (int off = 1; off < T; off <<= 1) {
+        uint64_t v = tid >= off ? tmp[tid - off] : 0;
+        __syncthreads();
+        tmp[tid] += v;
+        __syncthreads();
+    }
+    uint64_t run = tmp[tid] - s;
+    for (int k = lo; k < hi; ++k) {
+        uint64_t v = a[k];
+        a[k] = run;
+        run += v;
+    }
+    uint64_t total = tmp[T - 1];
+    __syncthreads();
+    return total;
+}

@@ -1,0 +1,325 @@
+// isg_probs and isg_select_sample.
+//
+// Pages: InstaGen, thelatestinai.com page, Figure 3(b)-(c) (centroid scores give
+// each key group a probability pi per query group; the top key group is always
+// kept; the rest is sampled in proportion to pi and weighted by 1/pi); Paper
+// Reading AI Learner page, abstract (exact set of the top-scoring keys plus a
+// sample drawn in proportion to estimated attention, reweighted by the inverse
+// sampling probability, one sample per query cluster); acceptodds.com page,
+// abstract (the sample size is a direct budget).
+//
+// Everything that decides an integer (scores, ranking, proposal weights, draws)
+// uses explicitly rounded fp32 operations or integers, so the lists and sample
+// indices are reproducible bit for bit by any implementation of the same
+// definition.  This file is compiled with -ffp-contract=off.
+#include <cmath>
+
+#include "isg_internal.h"
+
+namespace {
+
+constexpr int kMaxGroups = 1024;
+constexpr int kThreads = 256;
+
+// S_ij = fma-chain(cq_i . ck_j) * scale (fp32, k ascending); pi from S in fp64.
+__global__ __launch_bounds__(kThreads) void probs_kernel(const float *cq, const float *ck,
+                                                         const int32_t *k_offsets, int Cq, int Ck, int d,
+                                                         float scale, float *scores, float *pi)
+{
+    extern __shared__ float qs[];  // d floats
+    __shared__ double red[kThreads];
+    __shared__ float redf[kThreads];
+    const int64_t gi = blockIdx.x;  // bh*Cq + i
+    const int64_t bh = gi / Cq;
+    const float *qi = cq + gi * d;
+    for (int k = threadIdx.x; k < d; k += kThreads) qs[k] = qi[k];
+    __syncthreads();
+    const int32_t *ko = k_offsets + bh * (Ck + 1);
+    float *S = scores + gi * Ck;
+    float lmax = -INFINITY;
+    for (int j = threadIdx.x; j < Ck; j += kThreads) {
+        const float *kj = ck + (bh * Ck + j) * d;
+        float acc = 0.0f;
+        for (int k = 0; k < d; ++k) acc = __fmaf_rn(qs[k], kj[k], acc);
+        const float s = __fmul_rn(acc, scale);
+        S[j] = s;
+        if (ko[j + 1] > ko[j]) lmax = fmaxf(lmax, s);
+    }
+    if (!pi) return;
+    redf[threadIdx.x] = lmax;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (threadIdx.x < off) redf[threadIdx.x] = fmaxf(redf[threadIdx.x], redf[threadIdx.x + off]);
+        __syncthreads();
+    }
+    const double mx = (double)redf[0];
+    double part = 0.0;
+    for (int j = threadIdx.x; j < Ck; j += kThreads) {
+        const int nj = ko[j + 1] - ko[j];
+        if (nj > 0) part += (double)nj * exp((double)S[j] - mx);
+    }
+    red[threadIdx.x] = part;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        __syncthreads();
+    }
+    const double tot = red[0];
+    for (int j = threadIdx.x; j < Ck; j += kThreads) {
+        const int nj = ko[j + 1] - ko[j];
+        pi[gi * Ck + j] = nj > 0 ? (float)((double)nj * exp((double)S[j] - mx) / tot) : 0.0f;
+    }
+}
+
+struct ProposalTable {
+    uint32_t v[256];
+};
+
+// Philox4x64-10 (Salmon et al., SC'11): per round, products of words 0 and 2
+// with the two multipliers; new words (hi1^w1^k0, lo1, hi0^w3^k1, lo0); Weyl key
+// bump between rounds.
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1)
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ULL, M1 = 0xCA5A826395121157ULL;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ULL, W1 = 0xBB67AE8584CAA73BULL;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+        const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+        const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+        k0 += W0; k1 += W1;
+    }
+}
+
+// floor((hi * 2^64 + lo) * T / 2^128)
+__device__ __forceinline__ uint64_t scale128(uint64_t hi, uint64_t lo, uint64_t T)
+{
+    const uint64_t a1 = __umul64hi(hi, T), a0 = hi * T;
+    const uint64_t b1 = __umul64hi(lo, T);
+    const uint64_t mid = a0 + b1;
+    return a1 + (mid < a0 ? 1 : 0);
+}
+
+struct SelShared {
+    int order[kMaxGroups];
+    int n[kMaxGroups];
+    float S[kMaxGroups];
+    int votes[kMaxGroups];
+    int flag[kMaxGroups];   // 1 = exact
+    int buf[kMaxGroups];    // scan scratch (ints)
+    int tmp[kThreads];
+    uint64_t W[kMaxGroups];      // compacted skipped weights -> exclusive prefix
+    uint64_t tmp64[kThreads];
+    int sk_group[kMaxGroups];    // compacted skipped group ids (ascending)
+    uint32_t sk_u[kMaxGroups];
+    float red_f[kThreads];
+    int red_i[kThreads];
+};
+
+__device__ __forceinline__ bool rank_before(const SelShared &sh, int a, int b, int mode, int Ck)
+{
+    const bool ea = a < Ck && sh.n[a] > 0, eb = b < Ck && sh.n[b] > 0;
+    if (ea != eb) return ea;
+    if (!ea) return a < b;
+    if (mode == ISG_SAMPLE_VOTES && sh.votes[a] != sh.votes[b]) return sh.votes[a] > sh.votes[b];
+    if (sh.S[a] != sh.S[b]) return sh.S[a] > sh.S[b];
+    return a < b;
+}
+
+__global__ __launch_bounds__(kThreads) void select_sample_kernel(
+    const float *scores, const int32_t *k_offsets, const int32_t *votes, int H, int Cq, int Ck,
+    int exact_keys, int m, int mode, uint64_t seed, uint64_t call_id, ProposalTable tbl,
+    int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx, float *sample_bias, int32_t *n_sample)
+{
+    __shared__ SelShared sh;
+    const int tid = threadIdx.x;
+    const int64_t gi = blockIdx.x;
+    const int64_t bh = gi / Cq;
+    const int i = (int)(gi % Cq), h = (int)(bh % H), b = (int)(bh / H);
+    const int32_t *ko = k_offsets + bh * (Ck + 1);
+    int P2 = 1;
+    while (P2 < Ck) P2 <<= 1;
+    for (int j = tid; j < P2; j += kThreads) {
+        sh.order[j] = j;
+        if (j < Ck) {
+            sh.n[j] = ko[j + 1] - ko[j];
+            sh.S[j] = scores[gi * Ck + j];
+            sh.votes[j] = votes ? votes[gi * Ck + j] : 0;
+            sh.flag[j] = 0;
+        }
+    }
+    __syncthreads();
+    // bitonic sort of group ids by rank_before
+    for (int size = 2; size <= P2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int p = tid; p < P2 / 2; p += kThreads) {
+                const int lo = 2 * p - (p & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = (lo & size) == 0;
+                const int a = sh.order[lo], c = sh.order[hi];
+                const bool swap = up ? rank_before(sh, c, a, mode, Ck) : rank_before(sh, a, c, mode, Ck);
+                if (swap) { sh.order[lo] = c; sh.order[hi] = a; }
+            }
+            __syncthreads();
+        }
+    }
+    // running key count along the order; the first group is always taken
+    for (int p = tid; p < Ck; p += kThreads) {
+        const int j = sh.order[p];
+        sh.buf[p] = sh.n[j];
+    }
+    __syncthreads();
+    block_exclusive_scan_int(sh.buf, Ck, sh.tmp);
+    for (int p = tid; p < Ck; p += kThreads) {
+        const int j = sh.order[p];
+        const int incl = sh.buf[p] + sh.n[j];
+        if (sh.n[j] > 0 && (p == 0 || incl <= exact_keys)) sh.flag[j] = 1;
+    }
+    __syncthreads();
+    // exact groups ascending
+    for (int j = tid; j < Ck; j += kThreads) sh.buf[j] = sh.flag[j];
+    __syncthreads();
+    const int ne = block_exclusive_scan_int(sh.buf, Ck, sh.tmp);
+    int32_t *eg = exact_groups + gi * Ck;
+    for (int j = tid; j < Ck; j += kThreads) {
+        if (sh.flag[j]) eg[sh.buf[j]] = j;
+        if (j >= ne) eg[j] = -1;
+    }
+    if (tid == 0) n_exact[gi] = ne;
+    __syncthreads();
+    // skipped groups ascending, their key count M and largest score
+    for (int j = tid; j < Ck; j += kThreads) sh.buf[j] = (sh.n[j] > 0 && !sh.flag[j]) ? 1 : 0;
+    __syncthreads();
+    int lcount = 0;
+    float lmax = -INFINITY;
+    for (int j = tid; j < Ck; j += kThreads)
+        if (sh.n[j] > 0 && !sh.flag[j]) { lcount += sh.n[j]; lmax = fmaxf(lmax, sh.S[j]); }
+    sh.red_i[tid] = lcount;
+    sh.red_f[tid] = lmax;
+    __syncthreads();
+    for (int off = kThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) {
+            sh.red_i[tid] += sh.red_i[tid + off];
+            sh.red_f[tid] = fmaxf(sh.red_f[tid], sh.red_f[tid + off]);
+        }
+        __syncthreads();
+    }
+    const int M = sh.red_i[0];
+    const float smax = sh.red_f[0];
+    const int nsk = block_exclusive_scan_int(sh.buf, Ck, sh.tmp);
+    for (int j = tid; j < Ck; j += kThreads)
+        if (sh.n[j] > 0 && !sh.flag[j]) sh.sk_group[sh.buf[j]] = j;
+    __syncthreads();
+    int32_t *si = sample_idx + gi * (int64_t)m;
+    float *sb = sample_bias + gi * (int64_t)m;
+    if (M == 0) {
+        if (tid == 0) n_sample[gi] = 0;
+        return;
+    }
+    if (M <= m) {
+        // enumerate every skipped key once, offset 0
+        for (int s = tid; s < nsk; s += kThreads) sh.buf[s] = sh.n[sh.sk_group[s]];
+        __syncthreads();
+        block_exclusive_scan_int(sh.buf, nsk, sh.tmp);
+        for (int t = tid; t < M; t += kThreads) {
+            int lo = 0, hi = nsk - 1;  // last s with buf[s] <= t
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sh.buf[mid] <= t) lo = mid; else hi = mid - 1;
+            }
+            si[t] = ko[sh.sk_group[lo]] + (t - sh.buf[lo]);
+            sb[t] = 0.0f;
+        }
+        if (tid == 0) n_sample[gi] = M;
+        return;
+    }
+    // proposal weights W = n u, exclusive prefix in ascending group order
+    for (int s = tid; s < nsk; s += kThreads) {
+        const int j = sh.sk_group[s];
+        uint32_t u = 1;
+        if (mode != ISG_SAMPLE_UNIFORM) {
+            const float diff = __fsub_rn(smax, sh.S[j]);
+            const float prod = __fmul_rn(diff, 369.32993f);  // 256 * log2(e)
+            int a = (int)rintf(prod);
+            a = min(max(a, 0), 7936);
+            const int shft = min(a >> 8, 31);
+            u = tbl.v[a & 255] >> shft;
+            if (u < 1) u = 1;
+        }
+        sh.sk_u[s] = u;
+        sh.W[s] = (uint64_t)sh.n[j] * u;
+    }
+    __syncthreads();
+    const uint64_t T = block_exclusive_scan_u64(sh.W, nsk, sh.tmp64);
+    const double lnT = log((double)T), lnm = log((double)m);
+    for (int t2 = 2 * tid; t2 < m; t2 += 2 * kThreads) {
+        uint64_t c[4] = {(uint64_t)(t2 / 2) + 1, (uint64_t)i, (uint64_t)h, (uint64_t)b};
+        philox4x64_10(c, seed, call_id);
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const int t = t2 + w;
+            if (t >= m) break;
+            const uint64_t z = scale128(c[2 * w], c[2 * w + 1], T);
+            int lo = 0, hi = nsk - 1;  // last s with W[s] <= z
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (sh.W[mid] <= z) lo = mid; else hi = mid - 1;
+            }
+            const int j = sh.sk_group[lo];
+            const uint32_t u = sh.sk_u[lo];
+            si[t] = ko[j] + (int)((z - sh.W[lo]) / u);
+            sb[t] = (float)(lnT - log((double)u) - lnm);
+        }
+    }
+    if (tid == 0) n_sample[gi] = m;
+}
+
+}  // namespace
+
+extern "C" isg_status isg_probs(void *stream, const float *cq, const float *ck, const int32_t *k_offsets,
+                                int B, int H, int Cq, int Ck, int d, float scale, float *scores, float *pi)
+{
+    ISG_REQUIRE(cq && ck && k_offsets && scores, ISG_E_ARG, "isg_probs: null pointer argument");
+    ISG_REQUIRE(B >= 1 && H >= 1, ISG_E_ARG, "isg_probs: B, H must be >= 1");
+    ISG_REQUIRE(Cq >= 1 && Cq <= kMaxGroups && Ck >= 1 && Ck <= kMaxGroups, ISG_E_ARG,
+                "isg_probs: Cq, Ck must be in [1, %d] (got %d, %d)", kMaxGroups, Cq, Ck);
+    ISG_REQUIRE(d >= 1 && d <= 1024, ISG_E_ARG, "isg_probs: d must be in [1, 1024]");
+    ISG_REQUIRE(std::isfinite(scale), ISG_E_ARG, "isg_probs: scale must be finite");
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t G = (int64_t)B * H * Cq;
+    ISG_REQUIRE(G <= 0x7fffffff, ISG_E_ARG, "isg_probs: too many groups");
+    probs_kernel<<<(unsigned)G, kThreads, d * sizeof(float), st>>>(cq, ck, k_offsets, Cq, Ck, d, scale, scores,
+                                                                   pi);
+    return isg_check_launch("isg_probs");
+}
+
+extern "C" isg_status isg_select_sample(void *stream, const float *scores, const int32_t *k_offsets,
+                                        const int32_t *votes, int B, int H, int Cq, int Ck, int N,
+                                        int exact_keys, int m, int mode, uint64_t seed, uint64_t call_id,
+                                        int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx,
+                                        float *sample_bias, int32_t *n_sample)
+{
+    ISG_REQUIRE(scores && k_offsets && exact_groups && n_exact && n_sample, ISG_E_ARG,
+                "isg_select_sample: null pointer argument");
+    ISG_REQUIRE(m == 0 || (sample_idx && sample_bias), ISG_E_ARG,
+                "isg_select_sample: sample_idx / sample_bias required when m > 0");
+    ISG_REQUIRE(B >= 1 && H >= 1 && N >= 1, ISG_E_ARG, "isg_select_sample: B, H, N must be >= 1");
+    ISG_REQUIRE(Cq >= 1 && Ck >= 1 && Ck <= kMaxGroups, ISG_E_ARG,
+                "isg_select_sample: need Cq >= 1 and 1 <= Ck <= %d (got %d, %d)", kMaxGroups, Cq, Ck);
+    ISG_REQUIRE(exact_keys >= 0, ISG_E_ARG, "isg_select_sample: exact_keys must be >= 0");
+    ISG_REQUIRE(m >= 0 && m <= N, ISG_E_ARG, "isg_select_sample: need 0 <= m <= N (got m=%d, N=%d)", m, N);
+    ISG_REQUIRE(mode == ISG_SAMPLE_IMPORTANCE || mode == ISG_SAMPLE_UNIFORM || mode == ISG_SAMPLE_VOTES,
+                ISG_E_ARG, "isg_select_sample: unknown mode %d", mode);
+    ISG_REQUIRE((mode == ISG_SAMPLE_VOTES) == (votes != nullptr), ISG_E_ARG,
+                "isg_select_sample: votes must be given exactly in votes mode");
+    const int64_t G = (int64_t)B * H * Cq;
+    ISG_REQUIRE(G <= 0x7fffffff, ISG_E_ARG, "isg_select_sample: too many groups");
+    ProposalTable tbl;
+    isg_proposal_table(tbl.v);
+    hipStream_t st = (hipStream_t)stream;
+    select_sample_kernel<<<(unsigned)G, kThreads, 0, st>>>(scores, k_offsets, votes, H, Cq, Ck, exact_keys, m,
+                                                           mode, seed, call_id, tbl, exact_groups, n_exact,
+                                                           sample_idx, sample_bias, n_sample);
+    return isg_check_launch("isg_select_sample");
+}

@@ -1,0 +1,234 @@
+"""Thin Python binding of libisg (include/isg.h): argument marshalling only.
+
+Every step runs in the HIP library; torch provides device memory and the
+stream.  There is no CPU path: without the built library, or with tensors that
+are not on a GPU, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libisg.so")
+
+ISG_F32, ISG_BF16 = 0, 1
+MODES = {"importance": 0, "uniform": 1, "votes": 2}
+EXPORTS = ["isg_last_error", "isg_version", "isg_proposal_table", "isg_cluster_workspace_size",
+           "isg_cluster", "isg_probs", "isg_select_sample", "isg_attention_workspace_size",
+           "isg_attention", "isg_unpermute"]
+
+_lib = None
+
+
+class IsgError(RuntimeError):
+    pass
+
+
+def lib():
+    """Load the in-tree libisg.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise IsgError(f"libisg.so not built at {LIB_PATH}; run __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        _declare(L)
+        _lib = L
+    return _lib
+
+
+_p, _i, _u64, _f, _sz = C.c_void_p, C.c_int, C.c_uint64, C.c_float, C.c_size_t
+
+
+def _declare(L):
+    L.isg_last_error.restype = C.c_char_p
+    L.isg_version.restype = _i
+    L.isg_proposal_table.argtypes = [_p]
+    L.isg_cluster_workspace_size.argtypes = [_i] * 5
+    L.isg_cluster_workspace_size.restype = _sz
+    L.isg_cluster.argtypes = [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz]
+    L.isg_probs.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]
+    L.isg_select_sample.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _u64, _u64,
+                                    _p, _p, _p, _p, _p]
+    L.isg_attention_workspace_size.argtypes = [_i] * 5
+    L.isg_attention_workspace_size.restype = _sz
+    L.isg_attention.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
+                                _i, _f, _p, _p, _p, _sz]
+    L.isg_unpermute.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p]
+    for name in ["isg_cluster", "isg_probs", "isg_select_sample", "isg_attention", "isg_unpermute"]:
+        getattr(L, name).restype = _i
+
+
+def _check(status, what):
+    if status != 0:
+        msg = lib().isg_last_error().decode(errors="replace")
+        raise IsgError(f"{what} failed with status {status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dev(t, name):
+    if not (isinstance(t, torch.Tensor) and t.is_cuda):
+        raise IsgError(f"{name} must be a GPU tensor")
+    return t
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return ISG_BF16
+    if t.dtype == torch.float32:
+        return ISG_F32
+    raise IsgError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _i64x3(vals):
+    return (C.c_int64 * 3)(*[int(v) for v in vals])
+
+
+def version() -> int:
+    return lib().isg_version()
+
+
+def proposal_table():
+    out = (C.c_uint32 * 256)()
+    lib().isg_proposal_table(out)
+    return list(out)
+
+
+def cluster_workspace_size(B, H, N, d, C_):
+    return int(lib().isg_cluster_workspace_size(B, H, N, d, C_))
+
+
+def attention_workspace_size(B, H, N, Cq, Ck):
+    return int(lib().isg_attention_workspace_size(B, H, N, Cq, Ck))
+
+
+def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, workspace=None, stream=None):
+    """k-means + stable permutation per head of x [B,H,N,d] (d contiguous, any other strides)."""
+    _dev(x, "x")
+    B, H, N, d = x.shape
+    if x.stride(3) != 1:
+        raise IsgError("x must have a contiguous last dimension")
+    dev = x.device
+    cent = (init.to(device=dev, dtype=torch.float32).contiguous().clone() if init is not None
+            else torch.empty((B, H, C_, d), device=dev, dtype=torch.float32))
+    labels = torch.empty((B, H, N), device=dev, dtype=torch.int32)
+    perm = torch.empty_like(labels)
+    offsets = torch.empty((B, H, C_ + 1), device=dev, dtype=torch.int32)
+    x_perm = torch.empty((B, H, N, d), device=dev, dtype=x.dtype) if want_perm else None
+    comp_perm = None
+    if companion is not None:
+        _dev(companion, "companion")
+        if companion.shape != x.shape or companion.stride() != x.stride() or companion.dtype != x.dtype:
+            raise IsgError("companion must match x in shape, strides and dtype")
+        comp_perm = torch.empty((B, H, N, d), device=dev, dtype=x.dtype)
+    need = cluster_workspace_size(B, H, N, d, C_)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    st = lib().isg_cluster(_stream(stream), _ptr(x), _dtype(x), _i64x3(x.stride()[:3]), B, H, N, d, C_, iters,
+                           0 if init is None else 1, _ptr(companion), _ptr(cent), _ptr(labels), _ptr(perm),
+                           _ptr(offsets), _ptr(x_perm), _ptr(comp_perm), _ptr(ws), ws.numel())
+    _check(st, "isg_cluster")
+    return dict(centroids=cent, labels=labels, perm=perm, offsets=offsets, x_perm=x_perm,
+                companion_perm=comp_perm)
+
+
+def isg_probs(cq, ck, k_offsets, scale, *, want_pi=True, stream=None):
+    _dev(cq, "cq"); _dev(ck, "ck"); _dev(k_offsets, "k_offsets")
+    B, H, Cq, d = cq.shape
+    Ck = ck.shape[2]
+    scores = torch.empty((B, H, Cq, Ck), device=cq.device, dtype=torch.float32)
+    pi = torch.empty_like(scores) if want_pi else None
+    st = lib().isg_probs(_stream(stream), _ptr(cq.contiguous()), _ptr(ck.contiguous()),
+                         _ptr(k_offsets.contiguous()), B, H, Cq, Ck, d, float(scale), _ptr(scores), _ptr(pi))
+    _check(st, "isg_probs")
+    return scores, pi
+
+
+def isg_select_sample(scores, k_offsets, N, exact_keys, m, *, mode="importance", seed=0, call_id=0,
+                      votes=None, stream=None):
+    _dev(scores, "scores"); _dev(k_offsets, "k_offsets")
+    B, H, Cq, Ck = scores.shape
+    dev = scores.device
+    mm = max(int(m), 1)
+    out = dict(exact_groups=torch.empty((B, H, Cq, Ck), device=dev, dtype=torch.int32),
+               n_exact=torch.empty((B, H, Cq), device=dev, dtype=torch.int32),
+               sample_idx=torch.empty((B, H, Cq, mm), device=dev, dtype=torch.int32),
+               sample_bias=torch.empty((B, H, Cq, mm), device=dev, dtype=torch.float32),
+               n_sample=torch.empty((B, H, Cq), device=dev, dtype=torch.int32), m=int(m))
+    st = lib().isg_select_sample(_stream(stream), _ptr(scores.contiguous()), _ptr(k_offsets.contiguous()),
+                                 _ptr(None if votes is None else votes.contiguous()), B, H, Cq, Ck, N,
+                                 int(exact_keys), int(m), MODES[mode] if isinstance(mode, str) else int(mode),
+                                 C.c_uint64(seed), C.c_uint64(call_id), _ptr(out["exact_groups"]),
+                                 _ptr(out["n_exact"]), _ptr(out["sample_idx"]), _ptr(out["sample_bias"]),
+                                 _ptr(out["n_sample"]))
+    _check(st, "isg_select_sample")
+    return out
+
+
+def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, want_lse=True, out=None, workspace=None,
+                  stream=None):
+    for n, t in (("q_p", q_p), ("k_p", k_p), ("v_p", v_p)):
+        _dev(t, n)
+        if not t.is_contiguous():
+            raise IsgError(f"{n} must be contiguous [B,H,N,d]")
+    B, H, N, d = q_p.shape
+    Cq = q_offsets.shape[-1] - 1
+    Ck = k_offsets.shape[-1] - 1
+    o_p = out if out is not None else torch.empty_like(q_p)
+    lse_p = torch.empty((B, H, N), device=q_p.device, dtype=torch.float32) if want_lse else None
+    need = attention_workspace_size(B, H, N, Cq, Ck)
+    ws = workspace if workspace is not None else torch.empty(need, device=q_p.device, dtype=torch.uint8)
+    m = sel["sample_idx"].shape[-1] if sel.get("m") is None else sel["m"]
+    st = lib().isg_attention(_stream(stream), _ptr(q_p), _ptr(k_p), _ptr(v_p), _dtype(q_p), B, H, N, d, Cq, Ck,
+                             _ptr(q_offsets.contiguous()), _ptr(k_offsets.contiguous()),
+                             _ptr(sel["exact_groups"]), _ptr(sel["n_exact"]), _ptr(sel["sample_idx"]),
+                             _ptr(sel["sample_bias"]), _ptr(sel["n_sample"]), int(m), float(scale), _ptr(o_p),
+                             _ptr(lse_p), _ptr(ws), ws.numel())
+    _check(st, "isg_attention")
+    return o_p, lse_p
+
+
+def isg_unpermute(o_p, lse_p, perm_q, *, out=None, lse_out=None, stream=None):
+    _dev(o_p, "o_p"); _dev(perm_q, "perm_q")
+    B, H, N, d = o_p.shape
+    o = out if out is not None else torch.empty_like(o_p)
+    if o.stride(3) != 1:
+        raise IsgError("out must have a contiguous last dimension")
+    lse = None
+    if lse_p is not None:
+        lse = lse_out if lse_out is not None else torch.empty_like(lse_p)
+    st = lib().isg_unpermute(_stream(stream), _ptr(o_p), _ptr(lse_p), _ptr(perm_q.contiguous()), _dtype(o_p),
+                             B, H, N, d, _ptr(o), _i64x3(o.stride()[:3]), _ptr(lse))
+    _check(st, "isg_unpermute")
+    return o, lse
+
+
+def default_scale(d: int) -> float:
+    """1/sqrt(d) rounded to fp32 (the softmax scale of standard attention)."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+
+
+def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0, call_id=0, scale=None,
+             stream=None):
+    """All steps on one batch: cluster Q, cluster K (+V), probs, select/sample,
+    attention, unpermute.  Returns every intermediate (all on the GPU)."""
+    d = q.shape[-1]
+    scale = default_scale(d) if scale is None else scale
+    cq = isg_cluster(q, Cq, iters, stream=stream)
+    ck = isg_cluster(k, Ck, iters, companion=v, stream=stream)
+    scores, pi = isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, stream=stream)
+    sel = isg_select_sample(scores, ck["offsets"], q.shape[2], exact_keys, m, mode=mode, seed=seed,
+                            call_id=call_id, stream=stream)
+    o_p, lse_p = isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
+                               sel, scale, stream=stream)
+    o, lse = isg_unpermute(o_p, lse_p, cq["perm"], stream=stream)
+    return dict(cq=cq, ck=ck, scores=scores, pi=pi, sel=sel, o_p=o_p, lse_p=lse_p, o=o, lse=lse, scale=scale)

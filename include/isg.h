@@ -1,0 +1,200 @@
+/*
+ * isg.h -- C ABI of libisg: group-shared importance-sampled permuted
+ * block-sparse attention (InstaGen) on AMD Instinct MI355X (gfx950).
+ *
+ * The method (InstaGen, thelatestinai.com page, Figure 3; Paper Reading AI
+ * Learner page, abstract): cluster queries and keys of each head, permute the
+ * tokens so every cluster is contiguous, turn centroid scores into a
+ * probability pi per (query group, key group), compute the top key groups of
+ * every query group exactly, represent the remaining keys by one sample per
+ * query group drawn in proportion to the estimated attention and reweighted by
+ * the inverse sampling probability, and run one attention over the exact and
+ * sampled keys.  The entry points below are the steps of that path, in order:
+ *
+ *   isg_cluster (Q)  isg_cluster (K, companion V)  isg_probs
+ *   isg_select_sample  isg_attention  isg_unpermute
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named as device pointers must be device memory (hipMalloc or a
+ *    torch CUDA tensor) owned by the caller; the library never frees them and
+ *    keeps no reference after the call returns.  Scratch comes from the
+ *    caller's `workspace`, sized by the matching *_workspace_size().
+ *  - `stream` is a hipStream_t passed as void* (NULL = default stream).  Every
+ *    call only enqueues work on it and returns; nothing synchronises the host.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    failed check returns a non-zero isg_status, launches nothing, and
+ *    isg_last_error() (thread-local) describes it.  Nothing throws across the
+ *    ABI.  Device-side contents (labels, offsets, lists) are trusted: they must
+ *    come from the previous steps or satisfy the same invariants.
+ *  - Tensors are row-major; "[B,H,N,d]" means d is contiguous.  Integer outputs
+ *    (labels, permutations, offsets, exact lists, sample indices) are bitwise
+ *    deterministic; float outputs are deterministic run to run (no float
+ *    atomics).  Calls that overlap on one stream are ordered; the functions
+ *    keep no global mutable state and are reentrant.
+ *  - dtypes: ISG_F32 or ISG_BF16 for Q/K/V and the attention output; every
+ *    accumulation is fp32 or wider.
+ */
+#ifndef ISG_H
+#define ISG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    ISG_OK = 0,
+    ISG_E_ARG = 1,          /* null pointer, bad shape, budget out of range */
+    ISG_E_DTYPE = 2,        /* dtype not supported by this entry point */
+    ISG_E_UNSUPPORTED = 3,  /* shape supported by the method but not built (e.g. d) */
+    ISG_E_WORKSPACE = 4,    /* workspace missing or too small */
+    ISG_E_HIP = 5           /* HIP runtime / launch error */
+} isg_status;
+
+typedef enum { ISG_F32 = 0, ISG_BF16 = 1 } isg_dtype;
+
+typedef enum {
+    ISG_SAMPLE_IMPORTANCE = 0,  /* proposal ~ n_j exp(S_ij) (quantised), the pages' main mode */
+    ISG_SAMPLE_UNIFORM = 1,     /* every skipped key equally likely */
+    ISG_SAMPLE_VOTES = 2        /* exact set ranked by per-query PQ votes, importance sample */
+} isg_sample_mode;
+
+/* Thread-local description of the last failure of an isg_* call on this thread. */
+const char *isg_last_error(void);
+
+/* ABI version (incremented on incompatible change). */
+int isg_version(void);
+
+/* The integer proposal weights used by isg_select_sample in importance mode:
+ * out[k] = round(2^31 * 2^(-k/256)), k = 0..255 (host only, no GPU needed). */
+void isg_proposal_table(uint32_t out[256]);
+
+/* ------------------------------------------------------------------------ */
+/* isg_cluster -- k-means (Lloyd) per head, then a stable permutation.
+ * Pages: InstaGen, thelatestinai.com page, Figure 3(a) (queries and keys are
+ * clustered into groups) and Figure 2 (Cq = 100, Ck = 500).  The pages do not
+ * fix the algorithm; this is Euclidean Lloyd k-means on the raw vectors:
+ *   init (init_mode 0): c_j = x_{floor(j*N/C)}; init_mode 1: centroids as given;
+ *   `iters` rounds of: label_t = argmin_j |x_t - c_j|^2 (ties -> lowest j),
+ *                      c_j = mean of its members (empty cluster keeps c_j);
+ *   perm = tokens stably sorted by the last labels; offsets = prefix of counts;
+ *   x_perm[r] = x[perm[r]], companion_perm[r] = companion[perm[r]].
+ * The labels are the assignment of the last round and the centroids are the
+ * means of those groups.  The argmin is decided on fp32 distances, re-decided in
+ * fp64 between the two best candidates whenever they are closer than the fp32
+ * error bound.
+ *
+ * x           device, dtype dt, element (b,h,t,k) at x[b*xs[0] + h*xs[1] + t*xs[2] + k]
+ *             (xs = x_strides, in elements; k contiguous).  [B,N,H,d] and
+ *             sub-vectors (product-quantisation subspaces) are expressible.
+ * companion   device or NULL, same dtype and strides as x (V when x is K).
+ * B,H,N,d,C   1 <= C <= min(N, 4096), d in {16, 64, 128}; iters >= 1.
+ * centroids   device fp32 [B,H,C,d]; read when init_mode = 1, always written.
+ * labels      device int32 [B,H,N] (written).
+ * perm        device int32 [B,H,N] (written): perm[r] = token at sorted row r.
+ * offsets     device int32 [B,H,C+1] (written): group j = rows [off[j], off[j+1]).
+ * x_perm      device or NULL, dtype dt, contiguous [B,H,N,d] (written).
+ * companion_perm  device or NULL (must be non-NULL iff companion is), [B,H,N,d].
+ * workspace   device, >= isg_cluster_workspace_size(B,H,N,d,C) bytes. */
+size_t isg_cluster_workspace_size(int B, int H, int N, int d, int C);
+isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
+                       int B, int H, int N, int d, int C, int iters, int init_mode,
+                       const void *companion, float *centroids, int32_t *labels, int32_t *perm,
+                       int32_t *offsets, void *x_perm, void *companion_perm,
+                       void *workspace, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------ */
+/* isg_probs -- centroid scores and pi.
+ * Pages: InstaGen, thelatestinai.com page, Figure 3(b) (centroid scores give
+ * each key group a probability pi of being used by each query group); Paper
+ * Reading AI Learner page, abstract (in proportion to estimated attention).
+ *   S_ij  = (fp32 fused multiply-add chain over k = 0..d-1 of cq_ik*ck_jk) * scale
+ *           -- this exact fp32 order is part of the contract;
+ *   pi_ij = n_j e^{S_ij} / sum_j' n_j' e^{S_ij'} over non-empty groups (0 if empty),
+ *           with n_j = k_offsets[j+1] - k_offsets[j].
+ * cq [B,H,Cq,d], ck [B,H,Ck,d] device fp32; k_offsets device int32 [B,H,Ck+1];
+ * scores device fp32 [B,H,Cq,Ck] (written); pi device fp32 [B,H,Cq,Ck] or NULL.
+ * Cq, Ck in [1, 1024]; d in [1, 1024]. */
+isg_status isg_probs(void *stream, const float *cq, const float *ck, const int32_t *k_offsets,
+                     int B, int H, int Cq, int Ck, int d, float scale, float *scores, float *pi);
+
+/* ------------------------------------------------------------------------ */
+/* isg_select_sample -- exact set and the shared sample of each query group.
+ * Pages: Paper Reading AI Learner page, abstract (the top-scoring keys form an
+ * exact set computed in full; the rest is represented by a sample drawn in
+ * proportion to estimated attention, reweighted by the inverse sampling
+ * probability; one sample per query cluster shared by its queries);
+ * thelatestinai.com page, Figure 3(c) (the top key group is always kept);
+ * acceptodds.com page, abstract (the sample size is a direct budget).
+ *
+ * Exact set of query group i: non-empty key groups ordered by (S_ij desc,
+ * j asc) -- in ISG_SAMPLE_VOTES mode by (votes desc, S desc, j asc) -- the
+ * first always, then the following ones while the running key count stays
+ * <= exact_keys, stopping at the first that would exceed it.  Written as group
+ * ids ascending, -1 padded: exact_groups [B,H,Cq,Ck], n_exact [B,H,Cq].
+ *
+ * Sample: the skipped region is every non-empty group not in the exact set
+ * (M keys).  M = 0: no sample.  M <= m: every skipped key once (ascending
+ * group, then row), offset 0.  Otherwise m i.i.d. draws with replacement: draw
+ * t takes group j with probability n_j u_ij / T_i and a row uniformly inside
+ * it; u_ij = max(1, tbl[a & 255] >> (a >> 8)) with a = clamp(rint((Smax_i - S_ij)
+ * * 369.32993f), 0, 7936) in fp32 (importance) or u = 1 (uniform), tbl from
+ * isg_proposal_table, Smax_i the largest score over the skipped groups.  The
+ * offset is ln(T_i) - ln(u_ij) - ln(m) = ln(1 / (m p)), p the per-key draw
+ * probability.  Randomness: Philox4x64-10, key (seed, call_id), counter
+ * (floor(t/2) + 1, i, h, b); words 2(t%2), 2(t%2)+1 form a 128-bit r and the
+ * draw position is floor(r T / 2^128).  sample_idx [B,H,Cq,m] holds rows of
+ * the permuted K (absolute row within the head), sample_bias [B,H,Cq,m] the
+ * offsets, n_sample [B,H,Cq] the count (entries past it are not written).
+ *
+ * scores device fp32 [B,H,Cq,Ck]; k_offsets device int32 [B,H,Ck+1];
+ * votes device int32 [B,H,Cq,Ck], required iff mode = ISG_SAMPLE_VOTES;
+ * 0 <= exact_keys; 0 <= m <= N; Ck in [1, 1024]. */
+isg_status isg_select_sample(void *stream, const float *scores, const int32_t *k_offsets,
+                             const int32_t *votes, int B, int H, int Cq, int Ck, int N,
+                             int exact_keys, int m, int mode, uint64_t seed, uint64_t call_id,
+                             int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx,
+                             float *sample_bias, int32_t *n_sample);
+
+/* ------------------------------------------------------------------------ */
+/* isg_attention -- one attention over the exact and sampled keys.
+ * Pages: acceptodds.com page, abstract (the sample is computed together with
+ * the top blocks in a single attention kernel, sampled scores reweighted to
+ * account for the whole skipped region); thelatestinai.com page, Figure 3(d)
+ * (a group's queries share the same keys, so attention runs over dense blocks).
+ * For query row r of group i the columns are every row of every exact group
+ * (offset 0) followed by the n_sample samples (row sample_idx[t], offset
+ * sample_bias[t]):
+ *   l = scale <q_r, k> + offset,  O_r = sum e^l v / sum e^l,  LSE_r = ln sum e^l.
+ * q_p, k_p, v_p device [B,H,N,d] in permuted order (from isg_cluster), dtype dt;
+ * q_offsets [B,H,Cq+1], k_offsets [B,H,Ck+1] device int32; the list arguments
+ * as written by isg_select_sample with the same m; d in {64, 128}; Cq, Ck in
+ * [1, 1024]. o_p device dtype dt [B,H,N,d] (written, permuted order);
+ * lse_p device fp32 [B,H,N] or NULL (natural log).
+ * workspace device, >= isg_attention_workspace_size(B,H,N,Cq,Ck) bytes. */
+size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck);
+isg_status isg_attention(void *stream, const void *q_p, const void *k_p, const void *v_p,
+                         isg_dtype dt, int B, int H, int N, int d, int Cq, int Ck,
+                         const int32_t *q_offsets, const int32_t *k_offsets,
+                         const int32_t *exact_groups, const int32_t *n_exact,
+                         const int32_t *sample_idx, const float *sample_bias,
+                         const int32_t *n_sample, int m, float scale, void *o_p, float *lse_p,
+                         void *workspace, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------ */
+/* isg_unpermute -- rows back to token order: o[perm_q[r]] = o_p[r] (and lse).
+ * Implied by attention over a permuted matrix (Paper Reading AI Learner page,
+ * abstract).  o_p device dtype dt [B,H,N,d]; lse_p device fp32 [B,H,N] or NULL;
+ * perm_q device int32 [B,H,N] (a permutation per head); o device dtype dt with
+ * element (b,h,t,k) at o[b*os[0] + h*os[1] + t*os[2] + k] (os = o_strides in
+ * elements, so [B,N,H,d] works); lse device fp32 [B,H,N] or NULL (iff lse_p). */
+isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, const int32_t *perm_q,
+                         isg_dtype dt, int B, int H, int N, int d, void *o,
+                         const int64_t o_strides[3], float *lse);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ISG_H */
