@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time the attention at every budget of the workload")
+    ap.add_argument("--attention-only", type=int, default=0, metavar="K",
+                    help="profiling aid: after one full step, run only K attention calls and exit")
+    ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
+                    help="profiling aid: copy a GIB-sized buffer 3 times (a plain copy of known size) and exit")
     return ap.parse_args()
 
 
@@ -123,6 +127,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration > 0:
+        n = int(args.copy_calibration * (1 << 30))
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_call": n, "calls": 3,
+                          "read_KiB_per_call": n / 1024, "write_KiB_per_call": n / 1024}), flush=True)
+        return
     w = dict(WORKLOADS[args.workload])
     w["name"] = args.workload
     B, H, N, d = w.get("B", 1), w["H"], w["N"], w["d"]
@@ -166,9 +180,16 @@ def main():
                 ev[s].append((marks[si], marks[si + 1]))
         return cq, ck, sel, o
 
-    for _ in range(args.warmup):
+    for _ in range(max(1, args.warmup) if args.attention_only else args.warmup):
         cq, ck, sel, o = step(False)
     torch.cuda.synchronize()
+    if args.attention_only:
+        for _ in range(args.attention_only):
+            isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"], sel,
+                              scale, workspace=ws_a)
+        torch.cuda.synchronize()
+        print(json.dumps({"attention_only_calls": args.attention_only}), flush=True)
+        return
     flops, pairs = attention_flops(d, cq["offsets"], ck["offsets"], sel["exact_groups"], sel["n_exact"],
                                    sel["n_sample"])
     print(f"# warmup done; attention {flops / 1e12:.2f} TFLOP per call", file=sys.stderr, flush=True)

@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
                                                       const int32_t *n_exact, const int32_t *sample_idx,
                                                       const float *sample_bias, const int32_t *n_sample,
                                                       int Cq, int Ck, int m, int64_t cap, int32_t *col_row,
-                                                      float *col_bias, int32_t *col_len)
+                                                      float *col_bias, int32_t *col_len, int32_t *col_x)
 {
     __shared__ int pref[kMaxGroups + 1];
     __shared__ int start[kMaxGroups];
@@ -78,7 +78,10 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
         cr[c] = row;
         cb[c] = bias;
     }
-    if (threadIdx.x == 0) col_len[gi] = L;
+    if (threadIdx.x == 0) {
+        col_len[gi] = L;
+        col_x[gi] = X;
+    }
 }
 
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t *q_offsets, int BH, int Cq, int tq,
@@ -110,12 +113,78 @@ __device__ __forceinline__ int vt_pos(int k)
     return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
+// K/V rows of one 64-column tile held in registers between the global load and
+// the LDS store (a struct passed by value so it stays in VGPRs).
+template <int KIT> struct KVRegs {
+    u32x4 k[KIT];
+    u32x4 v[4];
+};
+
+template <int D, int KIT, int VTASK>
+__device__ __forceinline__ KVRegs<KIT> kv_gload(const uint16_t *kh, const uint16_t *vh, const int *rows, int tid,
+                                                 int vquad, int vchunk)
+{
+    constexpr int CPR = D / 8;
+    KVRegs<KIT> r;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+        const int e = it * 256 + tid;
+        const int key = e / CPR, ch = e % CPR;
+        r.k[it] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)rows[key] * D + ch * 8);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) r.v[kk] = u32x4{0, 0, 0, 0};
+    if (tid < VTASK) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            r.v[kk] = *reinterpret_cast<const u32x4 *>(vh + (int64_t)rows[vquad * 4 + kk] * D + vchunk * 8);
+    }
+    return r;
+}
+
+// K rows go to LDS as they are (rows padded to KSTR bytes); V goes transposed, one
+// row per d, keys at swizzled positions, four keys (8 bytes) per store.
+template <int D, int KIT, int VTASK>
+__device__ __forceinline__ void kv_sstore(const KVRegs<KIT> &r, uint8_t *kb, int tid, int vquad, int vchunk)
+{
+    constexpr int CPR = D / 8;
+    constexpr int KSTR = D * 2 + 16;
+    constexpr int VSTR = kTK * 2 + 16;
+    uint8_t *vb = kb + kTK * KSTR;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+        const int e = it * 256 + tid;
+        const int key = e / CPR, ch = e % CPR;
+        *reinterpret_cast<u32x4 *>(kb + key * KSTR + ch * 16) = r.k[it];
+    }
+    if (tid < VTASK) {
+        const uint32_t w0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
+        const uint32_t w1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
+        const uint32_t w2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
+        const uint32_t w3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
+        const int pos = vt_pos(vquad * 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int w = e >> 1;
+            uint32_t lo, hi;
+            if (e & 1) {
+                lo = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
+                hi = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
+            } else {
+                lo = (w0[w] & 0xFFFFu) | (w1[w] << 16);
+                hi = (w2[w] & 0xFFFFu) | (w3[w] << 16);
+            }
+            *reinterpret_cast<u32x2 *>(vb + (vchunk * 8 + e) * VSTR + pos * 2) = u32x2{lo, hi};
+        }
+    }
+}
+
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
     const uint16_t *__restrict__ q_p, const uint16_t *__restrict__ k_p, const uint16_t *__restrict__ v_p,
     int N, int Cq, const int4 *__restrict__ table, int nblocks, const int32_t *__restrict__ col_row,
-    const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, int64_t cap, float scale_log2,
-    uint16_t *__restrict__ o_p, float *__restrict__ lse_p)
+    const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
+    int64_t cap, float scale_log2, uint16_t *__restrict__ o_p, float *__restrict__ lse_p)
 {
     constexpr int NDS = D / 16;          // 16-wide d steps of S^T = K Q^T
     constexpr int NDB = D / 32;          // 32-row d blocks of O^T
@@ -137,6 +206,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int i = te.x, r0 = te.y, r1 = te.z, bh = te.w;
     const int64_t gi = (int64_t)bh * Cq + i;
     const int L = col_len[gi];
+    const int X = col_x[gi];
     const int T = (L + kTK - 1) / kTK;
     const int32_t *crow = col_row + gi * cap;
     const float *cbias = col_bias + gi * cap;
@@ -166,58 +236,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
 
-    uint4 kreg[KIT];
-    uint4 vreg[4];
     const int vquad = tid & 15, vchunk = tid >> 4;
-    auto gload = [&](int slot) {
-#pragma unroll
-        for (int it = 0; it < KIT; ++it) {
-            const int e = it * 256 + tid;
-            const int key = e / CPR, ch = e % CPR;
-            const int row = idx_row[slot][key];
-            kreg[it] = *reinterpret_cast<const uint4 *>(kh + (int64_t)row * D + ch * 8);
-        }
-        if (tid < VTASK) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int row = idx_row[slot][vquad * 4 + kk];
-                vreg[kk] = *reinterpret_cast<const uint4 *>(vh + (int64_t)row * D + vchunk * 8);
-            }
-        }
-    };
-    auto sstore = [&](int buf) {
-        uint8_t *kb = smem + buf * BUF;
-        uint8_t *vb = kb + KBYTES;
-#pragma unroll
-        for (int it = 0; it < KIT; ++it) {
-            const int e = it * 256 + tid;
-            const int key = e / CPR, ch = e % CPR;
-            *reinterpret_cast<uint4 *>(kb + key * KSTR + ch * 16) = kreg[it];
-        }
-        if (tid < VTASK) {
-            const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-            const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-            const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-            const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-            const int pos = vt_pos(vquad * 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int w = e >> 1;
-                uint32_t lo, hi;
-                if (e & 1) {
-                    lo = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
-                    hi = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
-                } else {
-                    lo = (w0[w] & 0xFFFFu) | (w1[w] << 16);
-                    hi = (w2[w] & 0xFFFFu) | (w3[w] << 16);
-                }
-                *reinterpret_cast<uint2 *>(vb + (vchunk * 8 + e) * VSTR + pos * 2) = make_uint2(lo, hi);
-            }
-        }
-    };
-
-    gload(0);
-    sstore(0);
+    KVRegs<KIT> kv = kv_gload<D, KIT, VTASK>(kh, vh, idx_row[0], tid, vquad, vchunk);
+    kv_sstore<D, KIT, VTASK>(kv, smem, tid, vquad, vchunk);
     __syncthreads();
 
     f32x16 oacc[NDB];
@@ -230,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int t = 0; t < T; ++t) {
         const int cur = t & 1;
         const bool more = t + 1 < T;
-        if (more) gload((t + 1) % 3);
+        if (more) kv = kv_gload<D, KIT, VTASK>(kh, vh, idx_row[(t + 1) % 3], tid, vquad, vchunk);
         int32_t nrow = 0;
         float nbias = 0.0f;
         const bool fetch2 = wave == 0 && t + 2 < T;
@@ -254,46 +275,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb2], 0, 0, 0);
                 }
             }
-            // logits in log2 units; lane holds keys kb2*32 + 8g + 4hl + e, e = 0..3
+            // Logits in log2 units; lane holds keys kb2*32 + 8g + 4hl + e (e = 0..3) of
+            // its query.  A tile made only of exact columns has no offsets.
             const int slot = t % 3;
-            float x[2][16];
-            float mx = -INFINITY;
+            const bool exact_tile = (t + 1) * kTK <= X;
+            float mx;
+            if (exact_tile) {
+                float mr = sacc[0][0];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+                for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const float4 bv = *reinterpret_cast<const float4 *>(&idx_bias[slot][kb2 * 32 + g * 8 + hl * 4]);
-                    const float bb[4] = {bv.x, bv.y, bv.z, bv.w};
+                    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sacc[kb2][r]);
+                mx = mr * scale_log2;
+            } else {
+                mx = -INFINITY;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float v = fmaf(sacc[kb2][4 * g + e], scale_log2, bb[e]);
-                        x[kb2][4 * g + e] = v;
-                        mx = fmaxf(mx, v);
+                for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(&idx_bias[slot][kb2 * 32 + g * 8 + hl * 4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float v = fmaf(sacc[kb2][4 * g + e], scale_log2, bv[e]);
+                            sacc[kb2][4 * g + e] = v;
+                            mx = fmaxf(mx, v);
+                        }
                     }
-                }
+            }
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            float psum = 0.0f;
+            // Lazy rescale: O and l stay relative to m_run until some lane's maximum
+            // exceeds it by more than 8 (weights up to 2^8 are safe in bf16 and fp32).
+            if (__any(mx > m_run + 8.0f)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+                for (int db = 0; db < NDB; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(x[kb2][r] - m_new);
-                    x[kb2][r] = p;
-                    psum += p;
-                }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m_run = m_new;
+            }
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 bf16x8 pb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) pb[e] = (__bf16)x[s >> 1][8 * (s & 1) + e];
+                for (int e = 0; e < 8; ++e) {
+                    const float v = sacc[s >> 1][8 * (s & 1) + e];
+                    const float p = exact_tile ? __builtin_amdgcn_exp2f(fmaf(v, scale_log2, -m_run))
+                                               : __builtin_amdgcn_exp2f(v - m_run);
+                    pb[e] = (__bf16)p;
+                }
+                // row sum of the rounded weights, the same ones P.V uses
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const bf16x2 pp = {pb[e], pb[e + 1]};
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+                }
 #pragma unroll
                 for (int db = 0; db < NDB; ++db) {
                     const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vb + (db * 32 + l32) * VSTR + (s * 16 + hl * 8) * 2);
@@ -301,7 +339,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             }
         }
-        if (more) sstore(cur ^ 1);
+        if (more) kv_sstore<D, KIT, VTASK>(kv, smem + (cur ^ 1) * BUF, tid, vquad, vchunk);
         if (fetch2) {
             idx_row[(t + 2) % 3][lane] = nrow;
             idx_bias[(t + 2) % 3][lane] = nbias;
@@ -323,7 +361,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                                     ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 1] * inv) << 16);
                 const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 2] * inv) |
                                     ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 3] * inv) << 16);
-                *reinterpret_cast<uint2 *>(orow + d0) = make_uint2(lo, hi);
+                *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
             }
         if (lse_p && hl == 0) lse_p[(int64_t)bh * N + qrow_raw] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
     }
@@ -405,7 +443,7 @@ struct Layout {
     int64_t cap;       // columns per group in the column map
     int tph;           // tile slots per head
     int ntotal;        // launched blocks (multiple of 8)
-    size_t off_row, off_bias, off_len, off_table, total;
+    size_t off_row, off_bias, off_len, off_x, off_table, total;
 };
 
 Layout layout(int B, int H, int N, int Cq, int m, int tq)
@@ -420,6 +458,7 @@ Layout layout(int B, int H, int N, int Cq, int m, int tq)
     L.off_row = o; o += isg_align256((size_t)G * L.cap * sizeof(int32_t));
     L.off_bias = o; o += isg_align256((size_t)G * L.cap * sizeof(float));
     L.off_len = o; o += isg_align256((size_t)G * sizeof(int32_t));
+    L.off_x = o; o += isg_align256((size_t)G * sizeof(int32_t));
     L.off_table = o; o += isg_align256((size_t)L.ntotal * sizeof(int4));
     L.total = o;
     return L;
@@ -469,20 +508,21 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     int32_t *col_row = (int32_t *)(ws + Lq.off_row);
     float *col_bias = (float *)(ws + Lq.off_bias);
     int32_t *col_len = (int32_t *)(ws + Lq.off_len);
+    int32_t *col_x = (int32_t *)(ws + Lq.off_x);
     int4 *table = (int4 *)(ws + Lq.off_table);
     columns_kernel<<<(unsigned)G, 256, 0, st>>>(k_offsets, exact_groups, n_exact, sample_idx, sample_bias,
-                                               n_sample, Cq, Ck, m, Lq.cap, col_row, col_bias, col_len);
+                                               n_sample, Cq, Ck, m, Lq.cap, col_row, col_bias, col_len, col_x);
     tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if (dt == ISG_BF16) {
         if (d == 128)
             attn_bf16_kernel<128><<<Lq.ntotal, 256, 0, st>>>(
                 (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p);
+                col_row, col_bias, col_len, col_x, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p);
         else
             attn_bf16_kernel<64><<<Lq.ntotal, 256, 0, st>>>(
                 (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p);
+                col_row, col_bias, col_len, col_x, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p);
     } else {
         if (d == 128)
             attn_f32_kernel<128><<<Lq.ntotal, 256, 0, st>>>((const float *)q_p, (const float *)k_p,

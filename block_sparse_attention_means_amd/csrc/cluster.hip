@@ -8,6 +8,8 @@
 // Per round: assign (labels) -> per-chunk histograms -> per-head scan ->
 // stable scatter (perm, offsets) -> segmented fp64 mean in sorted order
 // (centroids).  No float atomics: every output is deterministic.
+#include <type_traits>
+
 #include "isg_internal.h"
 
 namespace {
@@ -247,13 +249,398 @@ __global__ __launch_bounds__(256) void gather_kernel(const T *x, Strides xs, con
     }
 }
 
+// ---------------------------------------------------------------- MFMA assign (bf16 x)
+// Distances |x - c|^2 = |c|^2 - 2<x, c> + |x|^2 on v_mfma_f32_32x32x16_bf16.  x is
+// exact in bf16; each fp32 centroid is split into bf16 planes hi + lo (16
+// significant bits, residual <= 2^-16 |c|); padded rows have norm 1e30.  Per token the two best candidates
+// (and the third-best value) are kept; whenever a rival lies within
+// tau = 1e-4 (|x|^2 + max_j |c_j|^2) -- several times the worst-case error of the
+// split and of fp32 accumulation -- the decision is re-taken in fp64 with the
+// same unfused arithmetic as the exact definition (two candidates, or every
+// centroid when a third is also close), ties to the lower index.
+constexpr int kCT = 32;  // centroids per MFMA tile
+
+template <int D>
+__global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent, int C, int Cpad, uint16_t *planes,
+                                                              float *norms, float *cmax)
+{
+    __shared__ float red[256];
+    const int bh = blockIdx.x;
+    float lmax = 0.0f;
+    for (int j = threadIdx.x; j < Cpad; j += 256) {
+        uint16_t *hi = planes + ((int64_t)bh * 2 * Cpad + j) * D;
+        uint16_t *lo = planes + ((int64_t)bh * 2 * Cpad + Cpad + j) * D;
+        if (j < C) {
+            const float *c = cent + ((int64_t)bh * C + j) * D;
+            double nn = 0.0;
+            for (int k = 0; k < D; ++k) {
+                const float v = c[k];
+                const uint16_t hb = f32_to_bf16_bits(v);
+                const float r = v - bf16_bits_to_f32(hb);  // exact
+                hi[k] = hb;
+                lo[k] = f32_to_bf16_bits(r);
+                nn += (double)v * (double)v;
+            }
+            norms[(int64_t)bh * Cpad + j] = (float)nn;
+            lmax = fmaxf(lmax, (float)nn);
+        } else {
+            for (int k = 0; k < D; ++k) { hi[k] = 0; lo[k] = 0; }
+            norms[(int64_t)bh * Cpad + j] = 1e30f;  // never wins; finite so keys stay ordered
+        }
+    }
+    red[threadIdx.x] = lmax;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) cmax[bh] = red[0];
+}
+
+// Candidates are kept as float keys: a positive approximate distance with its
+// low mantissa bits replaced by the centroid index.  Positive floats order like
+// their bit patterns, so min/med3 on keys order by distance (up to the dropped
+// bits, a resolution of 2^bits ulps) and carry the index along.  The four
+// smallest keys are kept sorted: one min and three med3 per candidate.
+struct Top4 {
+    float k1, k2, k3, k4;
+};
+
+__device__ __forceinline__ void top_insert(Top4 &t, float key)
+{
+    const float n4 = __builtin_amdgcn_fmed3f(t.k3, t.k4, key);
+    const float n3 = __builtin_amdgcn_fmed3f(t.k2, t.k3, key);
+    const float n2 = __builtin_amdgcn_fmed3f(t.k1, t.k2, key);
+    t.k1 = fminf(t.k1, key);
+    t.k2 = n2;
+    t.k3 = n3;
+    t.k4 = n4;
+}
+
+__device__ __forceinline__ float make_key(float d, uint32_t hi_mask, int j)
+{
+    return __uint_as_float((__float_as_uint(d) & hi_mask) | (uint32_t)j);
+}
+
+// fp64 partial sum of (x_k - c_k)^2 over the DPL dims of one lane (x bf16, c fp32;
+// both 8/16-byte aligned at these offsets).
+template <int DPL>
+__device__ __forceinline__ double seg_sqdist(const uint16_t *xr, const float *cr)
+{
+    float xv[DPL], cv[DPL];
+    if constexpr (DPL == 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(xr);
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cr);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cr + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xv[2 * q] = __uint_as_float(w[q] << 16);
+            xv[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+            cv[q] = c0[q];
+            cv[4 + q] = c1[q];
+        }
+    } else if constexpr (DPL == 4) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(xr);
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cr);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            xv[2 * q] = __uint_as_float(w[q] << 16);
+            xv[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cv[q] = c0[q];
+    } else {
+#pragma unroll
+        for (int q = 0; q < DPL; ++q) { xv[q] = bf16_bits_to_f32(xr[q]); cv[q] = cr[q]; }
+    }
+    double part = 0.0;
+#pragma unroll
+    for (int q = 0; q < DPL; ++q) {
+        const double a = (double)xv[q] - (double)cv[q];
+        part = fma(a, a, part);
+    }
+    return part;
+}
+
+__device__ __forceinline__ double sum16(double v)
+{
+    v += __shfl_xor(v, 8);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 1);
+    return v;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__restrict__ x, Strides xs, int H, int N,
+                                                          int C, int Cpad, const uint16_t *__restrict__ planes,
+                                                          const float *__restrict__ norms,
+                                                          const float *__restrict__ cmax,
+                                                          const float *__restrict__ cent, int32_t *__restrict__ labels)
+{
+    constexpr int NDS = D / 16;
+    constexpr int RSTR = D * 2 + 16;          // bytes per centroid row in LDS
+    constexpr int PBYTES = kCT * RSTR;        // one plane of a tile
+    constexpr int TBYTES = 2 * PBYTES;
+    constexpr int CPR = D / 8;                // 16-byte chunks per row
+    constexpr int NCH = 2 * kCT * CPR;        // chunks per tile (both planes)
+    constexpr int CIT = (NCH + 255) / 256;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TBYTES];
+    __shared__ float nsm[2][kCT];
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+    const uint16_t *xb = x + b * xs.b + h * xs.h;
+
+    int tok[2];
+    bf16x8 xf[2][NDS];
+    float xn[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int t = blockIdx.x * 256 + wave * 64 + tb * 32 + l32;
+        tok[tb] = t;
+        const uint16_t *row = xb + (int64_t)min(t, N - 1) * xs.t + hl * 8;
+        float ss = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+            xf[tb][s] = *reinterpret_cast<const bf16x8 *>(row + s * 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = (float)xf[tb][s][e];
+                ss = fmaf(v, v, ss);
+            }
+        }
+        xn[tb] = ss + __shfl_xor(ss, 32);
+    }
+
+    const uint16_t *pb = planes + (int64_t)bh * 2 * Cpad * D;
+    const float *nb = norms + (int64_t)bh * Cpad;
+    const int ntiles = Cpad / kCT;
+    // keys hold |x|^2 + 1 + |c|^2 - 2<x,c> >= 1 (so they are positive normal floats)
+    int ibits = 1;
+    while ((1 << ibits) < Cpad) ++ibits;
+    const uint32_t imask = (1u << ibits) - 1u, hi_mask = ~imask;
+    float xn1[2] = {xn[0] + 1.0f, xn[1] + 1.0f};
+    Top4 top[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) top[tb] = Top4{INFINITY, INFINITY, INFINITY, INFINITY};
+
+    u32x4 pre[CIT];
+    float npre = 0.0f;
+    auto gload = [&](int tile) {
+#pragma unroll
+        for (int it = 0; it < CIT; ++it) {
+            const int e = it * 256 + tid;
+            if (e < NCH) {
+                const int plane = e / (kCT * CPR), rem = e % (kCT * CPR), row = rem / CPR, ch = rem % CPR;
+                pre[it] = *reinterpret_cast<const u32x4 *>(pb + ((int64_t)plane * Cpad + tile * kCT + row) * D + ch * 8);
+            }
+        }
+        if (tid < kCT) npre = nb[tile * kCT + tid];
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int it = 0; it < CIT; ++it) {
+            const int e = it * 256 + tid;
+            if (e < NCH) {
+                const int plane = e / (kCT * CPR), rem = e % (kCT * CPR), row = rem / CPR, ch = rem % CPR;
+                *reinterpret_cast<u32x4 *>(smem + buf * TBYTES + plane * PBYTES + row * RSTR + ch * 16) = pre[it];
+            }
+        }
+        if (tid < kCT) nsm[buf][tid] = npre;
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const int cur = tile & 1;
+        const bool more = tile + 1 < ntiles;
+        if (more) gload(tile + 1);
+        f32x16 acc[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
+        const uint8_t *hb = smem + cur * TBYTES;
+        const uint8_t *lb = hb + PBYTES;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+            const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(hb + l32 * RSTR + s * 32 + hl * 16);
+            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(lb + l32 * RSTR + s * 32 + hl * 16);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[tb][s], acc[tb], 0, 0, 0);
+                acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int cl = (r >> 2) * 8 + hl * 4 + (r & 3);
+            const float nc = nsm[cur][cl];
+            const int j = tile * kCT + cl;
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                top_insert(top[tb], make_key(fmaf(-2.0f, acc[tb][r], nc) + xn1[tb], hi_mask, j));
+            }
+        }
+        if (more) sstore(cur ^ 1);
+        __syncthreads();
+    }
+
+    // Decisions.  Close calls go to a work list: 16 lanes per (token, candidate)
+    // entry evaluate |x - c|^2 in fp64 and the token takes the smallest (ties to
+    // the lower index).  A token with four candidates within tau is rescanned in
+    // fp64 over all C, again 16 lanes per candidate.
+    constexpr int kRQ = 3 * 256;
+    constexpr int DPL = D / 16;  // dims per lane
+    __shared__ int rq_n, full_n;
+    __shared__ int rq_slot[kRQ];
+    __shared__ int rq_cand[kRQ];
+    __shared__ double rq_dist[kRQ];
+    __shared__ int full_slot[256];
+    __shared__ int full_best[256];
+    __shared__ double grp_d[16];
+    __shared__ int grp_j[16];
+    if (tid == 0) { rq_n = 0; full_n = 0; }
+    __syncthreads();
+    const float cm = cmax[bh];
+    const float *cb = cent + (int64_t)bh * C * D;
+    int qpos[2] = {0, 0}, qcnt[2] = {0, 0}, fpos[2] = {-1, -1};
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        Top4 &T = top[tb];
+        const float o1 = __shfl_xor(T.k1, 32), o2 = __shfl_xor(T.k2, 32), o3 = __shfl_xor(T.k3, 32),
+                    o4 = __shfl_xor(T.k4, 32);
+        top_insert(T, o1);
+        top_insert(T, o2);
+        top_insert(T, o3);
+        top_insert(T, o4);
+        if (hl != 0 || tok[tb] >= N) continue;
+        // window: tau plus the key resolution (2^ibits ulps of the largest value compared)
+        const float tau = 1e-4f * (xn[tb] + cm);
+        const float d1 = __uint_as_float(__float_as_uint(T.k1) & hi_mask);
+        const float lim0 = d1 + tau;
+        const float res = __uint_as_float((__float_as_uint(lim0) & 0x7F800000u)) * ldexpf(1.0f, ibits - 23);
+        const float lim = lim0 + 2.0f * res;
+        const int slot = wave * 64 + tb * 32 + l32;
+        const float d2 = __uint_as_float(__float_as_uint(T.k2) & hi_mask);
+        const float d3 = __uint_as_float(__float_as_uint(T.k3) & hi_mask);
+        const float d4 = __uint_as_float(__float_as_uint(T.k4) & hi_mask);
+        if (d4 < lim) {
+            const int f = atomicAdd(&full_n, 1);
+            full_slot[f] = slot;
+            fpos[tb] = f;
+        } else {
+            const int n = 1 + (d2 < lim) + (d3 < lim);
+            if (n > 1) {
+                const int pos = atomicAdd(&rq_n, n);
+                rq_slot[pos] = slot; rq_cand[pos] = (int)(__float_as_uint(T.k1) & imask);
+                rq_slot[pos + 1] = slot; rq_cand[pos + 1] = (int)(__float_as_uint(T.k2) & imask);
+                if (n > 2) { rq_slot[pos + 2] = slot; rq_cand[pos + 2] = (int)(__float_as_uint(T.k3) & imask); }
+                qpos[tb] = pos;
+                qcnt[tb] = n;
+            }
+        }
+    }
+    __syncthreads();
+    const int sub = tid & 15, grp = tid >> 4;
+    {
+        const int nq = rq_n;
+        for (int e = grp; e < nq; e += 16) {
+            const int t = blockIdx.x * 256 + rq_slot[e];
+            const double dd = sum16(seg_sqdist<DPL>(xb + (int64_t)t * xs.t + sub * DPL,
+                                                    cb + (int64_t)rq_cand[e] * D + sub * DPL));
+            if (sub == 0) rq_dist[e] = dd;
+        }
+    }
+    const int nf = full_n;
+    for (int f = 0; f < nf; ++f) {
+        const int t = blockIdx.x * 256 + full_slot[f];
+        const uint16_t *xr = xb + (int64_t)t * xs.t + sub * DPL;
+        double bd = INFINITY;
+        int bj = 0;
+        for (int j = grp; j < C; j += 16) {
+            const double dd = sum16(seg_sqdist<DPL>(xr, cb + (int64_t)j * D + sub * DPL));
+            if (dd < bd) { bd = dd; bj = j; }
+        }
+        if (sub == 0) { grp_d[grp] = bd; grp_j[grp] = bj; }
+        __syncthreads();
+        if (tid == 0) {
+            double b = grp_d[0];
+            int jb = grp_j[0];
+            for (int g = 1; g < 16; ++g)
+                if (grp_d[g] < b || (grp_d[g] == b && grp_j[g] < jb)) { b = grp_d[g]; jb = grp_j[g]; }
+            full_best[f] = jb;
+        }
+        __syncthreads();
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int t = tok[tb];
+        if (hl != 0 || t >= N) continue;
+        int best = (int)(__float_as_uint(top[tb].k1) & imask);
+        if (fpos[tb] >= 0) {
+            best = full_best[fpos[tb]];
+        } else if (qcnt[tb] > 1) {
+            double bd = rq_dist[qpos[tb]];
+            best = rq_cand[qpos[tb]];
+            for (int q = 1; q < qcnt[tb]; ++q) {
+                const double dd = rq_dist[qpos[tb] + q];
+                const int j = rq_cand[qpos[tb] + q];
+                if (dd < bd || (dd == bd && j < best)) { bd = dd; best = j; }
+            }
+        }
+        labels[(int64_t)bh * N + t] = best;
+    }
+}
+
+struct ClusterWs {
+    size_t off_hist, off_planes, off_norms, off_cmax, total;
+    int Cpad;
+};
+
+ClusterWs cluster_ws(int B, int H, int N, int d, int C)
+{
+    ClusterWs w;
+    const size_t BH = (size_t)B * H;
+    const size_t nchunks = ((size_t)N + kSortChunk - 1) / kSortChunk;
+    w.Cpad = (C + kCT - 1) / kCT * kCT;
+    size_t o = 0;
+    w.off_hist = o; o += isg_align256(BH * nchunks * C * sizeof(int32_t));
+    w.off_planes = o; o += isg_align256(BH * 2 * w.Cpad * d * sizeof(uint16_t));
+    w.off_norms = o; o += isg_align256(BH * w.Cpad * sizeof(float));
+    w.off_cmax = o; o += isg_align256(BH * sizeof(float));
+    w.total = o;
+    return w;
+}
+
+template <typename T, int D>
+void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, int C, const float *cent,
+                   int32_t *labels, uint8_t *ws, const ClusterWs &w)
+{
+    const int BH = B * H;
+    if constexpr (std::is_same<T, uint16_t>::value) {
+        uint16_t *planes = (uint16_t *)(ws + w.off_planes);
+        float *norms = (float *)(ws + w.off_norms);
+        float *cmax = (float *)(ws + w.off_cmax);
+        centroid_planes_kernel<D><<<BH, 256, 0, st>>>(cent, C, w.Cpad, planes, norms, cmax);
+        assign_mfma_kernel<D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, w.Cpad, planes, norms,
+                                                                         cmax, cent, labels);
+    } else {
+        assign_kernel<T, D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, cent, labels);
+    }
+}
+
 template <typename T, int D>
 isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int N, int C, int iters,
                        int init_mode, const T *comp, float *cent, int32_t *labels, int32_t *perm,
-                       int32_t *offsets, T *x_perm, T *comp_perm, int32_t *hist)
+                       int32_t *offsets, T *x_perm, T *comp_perm, uint8_t *ws)
 {
     const int BH = B * H;
     const int nchunks = (N + kSortChunk - 1) / kSortChunk;
+    const ClusterWs w = cluster_ws(B, H, N, D, C);
+    int32_t *hist = (int32_t *)(ws + w.off_hist);
     int bits = 1;
     while ((1 << bits) < C) ++bits;
     if (init_mode == 0) {
@@ -262,7 +649,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         init_centroids_kernel<T><<<grid, 256, 0, st>>>(x, xs, H, N, C, D, cent, total);
     }
     for (int it = 0; it < iters; ++it) {
-        assign_kernel<T, D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, cent, labels);
+        launch_assign<T, D>(st, x, xs, B, H, N, C, cent, labels, ws, w);
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
         scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, offsets);
         scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, N, C, nchunks, bits, perm);
@@ -279,18 +666,18 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
 template <typename T>
 isg_status dispatch_d(int d, hipStream_t st, const T *x, Strides xs, int B, int H, int N, int C,
                       int iters, int init_mode, const T *comp, float *cent, int32_t *labels,
-                      int32_t *perm, int32_t *offsets, T *x_perm, T *comp_perm, int32_t *hist)
+                      int32_t *perm, int32_t *offsets, T *x_perm, T *comp_perm, uint8_t *ws)
 {
     switch (d) {
     case 16:
         return run_cluster<T, 16>(st, x, xs, B, H, N, C, iters, init_mode, comp, cent, labels, perm,
-                                  offsets, x_perm, comp_perm, hist);
+                                  offsets, x_perm, comp_perm, ws);
     case 64:
         return run_cluster<T, 64>(st, x, xs, B, H, N, C, iters, init_mode, comp, cent, labels, perm,
-                                  offsets, x_perm, comp_perm, hist);
+                                  offsets, x_perm, comp_perm, ws);
     case 128:
         return run_cluster<T, 128>(st, x, xs, B, H, N, C, iters, init_mode, comp, cent, labels, perm,
-                                   offsets, x_perm, comp_perm, hist);
+                                   offsets, x_perm, comp_perm, ws);
     default:
         return isg_fail(ISG_E_UNSUPPORTED, "isg_cluster: d=%d not built (16, 64, 128)", d);
     }
@@ -300,10 +687,8 @@ isg_status dispatch_d(int d, hipStream_t st, const T *x, Strides xs, int B, int 
 
 extern "C" size_t isg_cluster_workspace_size(int B, int H, int N, int d, int C)
 {
-    (void)d;
-    if (B < 1 || H < 1 || N < 1 || C < 1) return 0;
-    const size_t nchunks = ((size_t)N + kSortChunk - 1) / kSortChunk;
-    return isg_align256((size_t)B * H * nchunks * C * sizeof(int32_t));
+    if (B < 1 || H < 1 || N < 1 || C < 1 || d < 1) return 0;
+    return cluster_ws(B, H, N, d, C).total;
 }
 
 extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
@@ -337,12 +722,12 @@ extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, con
                 workspace ? ws_bytes : (size_t)0, need);
     hipStream_t st = (hipStream_t)stream;
     Strides xs{x_strides[0], x_strides[1], x_strides[2]};
-    int32_t *hist = (int32_t *)workspace;
+    uint8_t *ws = (uint8_t *)workspace;
     if (dt == ISG_F32)
         return dispatch_d<float>(d, st, (const float *)x, xs, B, H, N, C, iters, init_mode,
                                  (const float *)companion, centroids, labels, perm, offsets, (float *)x_perm,
-                                 (float *)companion_perm, hist);
+                                 (float *)companion_perm, ws);
     return dispatch_d<uint16_t>(d, st, (const uint16_t *)x, xs, B, H, N, C, iters, init_mode,
                                 (const uint16_t *)companion, centroids, labels, perm, offsets,
-                                (uint16_t *)x_perm, (uint16_t *)companion_perm, hist);
+                                (uint16_t *)x_perm, (uint16_t *)companion_perm, ws);
 }

@@ -20,8 +20,13 @@ static inline size_t isg_align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ---------------------------------------------------------------- device side
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Native vector types for 16/8-byte moves: HIP's uint4/uint2 are union-based
+// structs whose copies can stay in private (scratch) memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // bf16 <-> fp32 (bit-level, round to nearest even; inputs are finite).
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)

@@ -3,7 +3,12 @@
 Bars: block lists, sample indices, permutations and offsets bit-exact given the
 same upstream inputs; k-means labels equal except near-ties (fp64 distance gap
 < 1e-5); centroids within fp32 rounding; pi and offsets within 1e-6; attention
-output max-abs <= 2e-2 (bf16) / <= 1e-4 (fp32), LSE <= 1e-3 (bf16) / 1e-4 (fp32).
+output max-abs <= 2e-2 (bf16) / <= 1e-4 (fp32), LSE <= 2.5e-3 (bf16) / 1e-4 (fp32).
+
+The bf16 LSE bar follows from the arithmetic: the attention kernel sums the
+bf16-rounded weights that its P.V product uses (so O is an exact convex
+combination of V rows), and rounding each non-negative term to bf16 changes the
+sum by a relative 2^-9 at most, i.e. |d LSE| <= 1.95e-3 plus fp32 round-off.
 """
 import math
 
@@ -16,6 +21,8 @@ from block_sparse_attention_means_amd.synth import make_qkv, make_workload
 from block_sparse_attention_means_amd.workloads import WORKLOADS, budget_keys
 
 pytestmark = pytest.mark.gpu
+
+LSE_TOL_BF16 = 2.5e-3
 
 DEV = "cuda:0"
 
@@ -183,7 +190,7 @@ def test_attention_given_lists(orc, H, N, d, dtype, Cq, Ck, E, m):
     lerr = np.abs(npy(lse_p) - lo).max()
     say(f"  max|O-O_oracle| = {err:.3e}, max|LSE-LSE_oracle| = {lerr:.3e}")
     if dtype == "bf16":
-        assert err <= 2e-2 and lerr <= 1e-3
+        assert err <= 2e-2 and lerr <= LSE_TOL_BF16
     else:
         assert err <= 1e-4 and lerr <= 1e-4
 
@@ -192,7 +199,7 @@ def test_attention_high_entropy_zipf(orc):
     """Near-uniform attention (Q scaled by 0.2) with Zipf cluster sizes."""
     *_, o_p, lse_p, oo, lo = _attn_case(orc, 2, 4096, 128, "bf16", 16, 64, 300, 300, q_scale=0.2, zipf=1.2)
     assert np.abs(f32(o_p) - oo).max() <= 2e-2
-    assert np.abs(npy(lse_p) - lo).max() <= 1e-3
+    assert np.abs(npy(lse_p) - lo).max() <= LSE_TOL_BF16
 
 
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
@@ -206,7 +213,7 @@ def test_all_selected_equals_dense(orc, dtype, d):
     err = np.abs(f32(o) - od).max()
     say(f"  all-selected vs dense: {err:.3e}")
     assert err <= (1e-5 if dtype == "f32" else 2e-2)
-    assert np.abs(npy(lse) - ld).max() <= (1e-5 if dtype == "f32" else 1e-3)
+    assert np.abs(npy(lse) - ld).max() <= (1e-5 if dtype == "f32" else LSE_TOL_BF16)
 
 
 def test_every_skipped_token_weight_one(orc):
@@ -351,7 +358,7 @@ def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3):
             err = np.abs(og[rows] - oo[0, 0, rows]).max()
             lerr = np.abs(lg[rows] - lo[0, 0, rows]).max()
             say(f"  head {h} group {i} ({sizes[i]} rows): max|O-O_oracle| {err:.3e} LSE {lerr:.3e}")
-            assert err <= 2e-2 and lerr <= 1e-3
+            assert err <= 2e-2 and lerr <= LSE_TOL_BF16
 
 
 def test_full_size_480p(orc):
