@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
                                                       const int32_t *n_exact, const int32_t *sample_idx,
                                                       const float *sample_bias, const int32_t *n_sample,
                                                       int Cq, int Ck, int m, int64_t cap, int32_t *col_row,
-                                                      float *col_bias, int32_t *col_len, int32_t *col_x)
+                                                      float *col_bias, int32_t *col_len, int32_t *col_x,
+                                                      float *col_bmax)
 {
     __shared__ int pref[kMaxGroups + 1];
     __shared__ int start[kMaxGroups];
@@ -60,6 +61,7 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
     float *cb = col_bias + gi * cap;
     const int32_t *si = sample_idx + gi * (int64_t)m;
     const float *sb = sample_bias + gi * (int64_t)m;
+    float bmax = 0.0f;  // largest offset (log2 units) of the group, exact columns count as 0
     for (int c = threadIdx.x; c < Lpad; c += 256) {
         int row = 0;
         float bias = -INFINITY;
@@ -74,18 +76,57 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
         } else if (c < L) {
             row = si[c - X];
             bias = sb[c - X] * kLog2e;
+            bmax = fmaxf(bmax, bias);
         }
         cr[c] = row;
         cb[c] = bias;
     }
+    tmp[threadIdx.x] = __float_as_int(bmax);  // non-negative floats order like ints
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) tmp[threadIdx.x] = max(tmp[threadIdx.x], tmp[threadIdx.x + off]);
+        __syncthreads();
+    }
     if (threadIdx.x == 0) {
         col_len[gi] = L;
         col_x[gi] = X;
+        col_bmax[gi] = __int_as_float(tmp[0]);
     }
 }
 
+// Largest key norm |k| of each head (fp32 of the bf16 rows); kmax must start at 0.
+template <int D>
+__global__ __launch_bounds__(256) void kmax_kernel(const uint16_t *k_p, int N, int *kmax)
+{
+    __shared__ int red[256];
+    const int bh = blockIdx.y;
+    float best = 0.0f;
+    for (int r = blockIdx.x * 256 + threadIdx.x; r < N; r += gridDim.x * 256) {
+        const uint16_t *row = k_p + ((int64_t)bh * N + r) * D;
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(row + c * 8);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float a = __uint_as_float(w[q] << 16), b = __uint_as_float(w[q] & 0xFFFF0000u);
+                ss = fmaf(a, a, ss);
+                ss = fmaf(b, b, ss);
+            }
+        }
+        best = fmaxf(best, ss);
+    }
+    red[threadIdx.x] = __float_as_int(best);
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (threadIdx.x < off) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + off]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) atomicMax(&kmax[bh], red[0]);  // squared norm, as float bits
+}
+
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t *q_offsets, int BH, int Cq, int tq,
-                                                         int tph, int ntotal, int4 *table)
+                                                         int tph, int ntotal, int4 *table, int *redo, int *kmax2)
 {
     __shared__ int cnt[kMaxGroups];
     __shared__ int tmp[256];
@@ -103,6 +144,11 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t *q_offset
     for (int s = total + threadIdx.x; s < tph; s += 256) tb[s] = make_int4(-1, 0, 0, bh);
     if (bh == BH - 1)
         for (int s = BH * tph + threadIdx.x; s < ntotal; s += 256) table[s] = make_int4(-1, 0, 0, bh);
+    // clear the per-tile redo flags (indexed by logical tile) and this head's key-norm maximum
+    for (int s = bh * tph + threadIdx.x; s < (bh + 1) * tph; s += 256) redo[s] = 0;
+    if (bh == BH - 1)
+        for (int s = BH * tph + threadIdx.x; s < ntotal; s += 256) redo[s] = 0;
+    if (threadIdx.x == 0) kmax2[bh] = 0;
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
@@ -113,96 +159,108 @@ __device__ __forceinline__ int vt_pos(int k)
     return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-// K/V rows of one 64-column tile held in registers between the global load and
-// the LDS store (a struct passed by value so it stays in VGPRs).
-template <int KIT> struct KVRegs {
-    u32x4 k[KIT];
+// K tile in LDS: 64 unpadded rows, the 16-byte chunks of row r XOR-swizzled by
+// r mod (chunks per row) so that 8 lanes reading one chunk of 8 rows hit 8
+// distinct bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int row, int chunk)
+{
+    constexpr int CPR = D / 8;
+    return row * CPR + (chunk ^ (row & (CPR - 1)));
+}
+
+// K rows go straight from memory into LDS (global_load_lds_dwordx4: lane l of a
+// wave writes 16 bytes at M0 + 16 l); each lane fetches the chunk that belongs at
+// its swizzled position.
+template <int D>
+__device__ __forceinline__ void k_direct(uint8_t *kbuf, const uint16_t *kh, const int *rows, int wave, int lane)
+{
+    constexpr int CPR = D / 8;
+    constexpr int ROUNDS = kTK * CPR / 256;
+#pragma unroll
+    for (int it = 0; it < ROUNDS; ++it) {
+        const int blk = it * 4 + wave;  // 64-chunk (1 KB) block of the tile
+        const int P = blk * 64 + lane;
+        const int row = P / CPR, c = (P % CPR) ^ (row & (CPR - 1));
+        const uint16_t *src = kh + (uint32_t)rows[row] * (uint32_t)D + (uint32_t)(c * 8);
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                         (void __attribute__((address_space(3))) *)(kbuf + blk * 1024), 16, 0, 0);
+    }
+}
+
+// V rows are staged through registers (a thread holds 16 bytes of 4 consecutive
+// keys) and written transposed: one LDS row per d, keys at vt_pos positions.
+struct VRegs {
     u32x4 v[4];
 };
 
-template <int D, int KIT, int VTASK>
-__device__ __forceinline__ KVRegs<KIT> kv_gload(const uint16_t *kh, const uint16_t *vh, const int *rows, int tid,
-                                                 int vquad, int vchunk)
+template <int D>
+__device__ __forceinline__ void v_gload(VRegs &r, const uint16_t *vh, const int *rows, int tid)
 {
-    constexpr int CPR = D / 8;
-    KVRegs<KIT> r;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-        const int e = it * 256 + tid;
-        const int key = e / CPR, ch = e % CPR;
-        r.k[it] = *reinterpret_cast<const u32x4 *>(kh + (int64_t)rows[key] * D + ch * 8);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) r.v[kk] = u32x4{0, 0, 0, 0};
+    constexpr int VTASK = 16 * (D / 8);
     if (tid < VTASK) {
+        const int quad = tid & 15, chunk = tid >> 4;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-            r.v[kk] = *reinterpret_cast<const u32x4 *>(vh + (int64_t)rows[vquad * 4 + kk] * D + vchunk * 8);
-    }
-    return r;
-}
-
-// K rows go to LDS as they are (rows padded to KSTR bytes); V goes transposed, one
-// row per d, keys at swizzled positions, four keys (8 bytes) per store.
-template <int D, int KIT, int VTASK>
-__device__ __forceinline__ void kv_sstore(const KVRegs<KIT> &r, uint8_t *kb, int tid, int vquad, int vchunk)
-{
-    constexpr int CPR = D / 8;
-    constexpr int KSTR = D * 2 + 16;
-    constexpr int VSTR = kTK * 2 + 16;
-    uint8_t *vb = kb + kTK * KSTR;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-        const int e = it * 256 + tid;
-        const int key = e / CPR, ch = e % CPR;
-        *reinterpret_cast<u32x4 *>(kb + key * KSTR + ch * 16) = r.k[it];
-    }
-    if (tid < VTASK) {
-        const uint32_t w0[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-        const uint32_t w1[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
-        const uint32_t w2[4] = {r.v[2].x, r.v[2].y, r.v[2].z, r.v[2].w};
-        const uint32_t w3[4] = {r.v[3].x, r.v[3].y, r.v[3].z, r.v[3].w};
-        const int pos = vt_pos(vquad * 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            uint32_t lo, hi;
-            if (e & 1) {
-                lo = (w0[w] >> 16) | (w1[w] & 0xFFFF0000u);
-                hi = (w2[w] >> 16) | (w3[w] & 0xFFFF0000u);
-            } else {
-                lo = (w0[w] & 0xFFFFu) | (w1[w] << 16);
-                hi = (w2[w] & 0xFFFFu) | (w3[w] << 16);
-            }
-            *reinterpret_cast<u32x2 *>(vb + (vchunk * 8 + e) * VSTR + pos * 2) = u32x2{lo, hi};
-        }
+            r.v[kk] = *reinterpret_cast<const u32x4 *>(vh + (uint32_t)rows[quad * 4 + kk] * (uint32_t)D +
+                                                       (uint32_t)(chunk * 8));
     }
 }
 
 template <int D>
+__device__ __forceinline__ void v_sstore(const VRegs &r, uint8_t *vb, int tid)
+{
+    constexpr int VTASK = 16 * (D / 8);
+    constexpr int VSTR = kTK * 2 + 16;
+    if (tid < VTASK) {
+        const int quad = tid & 15, chunk = tid >> 4;
+        const int pos = vt_pos(quad * 4);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            // bf16 pairs (d, d+1) of the four keys -> rows d and d+1, four keys each
+            const uint32_t a = r.v[0][w], b = r.v[1][w], c = r.v[2][w], d = r.v[3][w];
+            const uint32_t lo_e = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo, b.lo)
+            const uint32_t hi_e = __builtin_amdgcn_perm(d, c, 0x05040100u);
+            const uint32_t lo_o = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi, b.hi)
+            const uint32_t hi_o = __builtin_amdgcn_perm(d, c, 0x07060302u);
+            *reinterpret_cast<u32x2 *>(vb + (chunk * 8 + 2 * w) * VSTR + pos * 2) = u32x2{lo_e, hi_e};
+            *reinterpret_cast<u32x2 *>(vb + (chunk * 8 + 2 * w + 1) * VSTR + pos * 2) = u32x2{lo_o, hi_o};
+        }
+    }
+}
+
+// One work-group = 4 waves x 32 query rows of one query group; two work-groups
+// per CU.  S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, so each
+// lane owns one query: its weights stay in registers and feed P.V directly.
+//
+// FIXED = true (the fast kernel): every row uses the fixed reference
+//   m_ref = scale log2(e) |q| max|k| + max(offsets, 0) >= every logit of the row
+// (Cauchy-Schwarz), so weights exp2(l - m_ref) never exceed 1 and O, l need no
+// rescaling.  If a row's weight sum ends below 2^-80 (its logits all far below
+// the bound), weights may have underflowed: the tile is flagged in `redo`.
+// FIXED = false (the fallback): running maximum with rescaling; it processes
+// only the flagged tiles.
+template <int D, bool FIXED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
     const uint16_t *__restrict__ q_p, const uint16_t *__restrict__ k_p, const uint16_t *__restrict__ v_p,
     int N, int Cq, const int4 *__restrict__ table, int nblocks, const int32_t *__restrict__ col_row,
     const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
-    int64_t cap, float scale_log2, uint16_t *__restrict__ o_p, float *__restrict__ lse_p)
+    const float *__restrict__ col_bmax, const int *__restrict__ kmax2, int64_t cap, float scale_log2,
+    uint16_t *__restrict__ o_p, float *__restrict__ lse_p, int *__restrict__ redo)
 {
     constexpr int NDS = D / 16;          // 16-wide d steps of S^T = K Q^T
     constexpr int NDB = D / 32;          // 32-row d blocks of O^T
-    constexpr int KSTR = D * 2 + 16;     // bytes per K row in LDS
+    constexpr int KBYTES = kTK * D * 2;
     constexpr int VSTR = kTK * 2 + 16;   // bytes per transposed V row (one d) in LDS
-    constexpr int KBYTES = kTK * KSTR;
-    constexpr int VBYTES = D * VSTR;
-    constexpr int BUF = KBYTES + VBYTES;
-    constexpr int CPR = D / 8;           // 16-byte chunks per row
-    constexpr int KIT = kTK * CPR / 256; // K chunks per thread per tile
-    constexpr int VTASK = 16 * CPR;      // (key quad, chunk) tasks per tile
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+    constexpr int BUF = KBYTES + D * VSTR;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
     __shared__ int idx_row[3][kTK];
     __shared__ __attribute__((aligned(16))) float idx_bias[3][kTK];
 
     const int lb = xcd_logical_block(blockIdx.x, nblocks);
     const int4 te = table[lb];
     if (te.x < 0) return;
+    if (!FIXED && redo[lb] == 0) return;
     const int i = te.x, r0 = te.y, r1 = te.z, bh = te.w;
     const int64_t gi = (int64_t)bh * Cq + i;
     const int L = col_len[gi];
@@ -219,10 +277,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int qrow = min(qrow_raw, r1 - 1);
     const bool wave_active = r0 + wave * 32 < r1;
     bf16x8 qf[NDS];
+    float qss = 0.0f;
     {
         const uint16_t *qsrc = q_p + ((int64_t)bh * N + qrow) * D + hl * 8;
 #pragma unroll
-        for (int s = 0; s < NDS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+        for (int s = 0; s < NDS; ++s) {
+            qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+            if (FIXED) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[s][e], (float)qf[s][e], qss);
+            }
+        }
+    }
+    float m_run = -INFINITY;
+    if (FIXED) {
+        qss += __shfl_xor(qss, 32);
+        const float kmx = sqrtf(__int_as_float(kmax2[bh]));
+        m_run = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, col_bmax[gi]) + 1e-6f;
     }
 
     // column list of tiles 0 and 1 into the index ring
@@ -235,10 +306,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
     __syncthreads();
-
-    const int vquad = tid & 15, vchunk = tid >> 4;
-    KVRegs<KIT> kv = kv_gload<D, KIT, VTASK>(kh, vh, idx_row[0], tid, vquad, vchunk);
-    kv_sstore<D, KIT, VTASK>(kv, smem, tid, vquad, vchunk);
+    VRegs vr;
+    k_direct<D>(smem, kh, idx_row[0], wave, lane);
+    v_gload<D>(vr, vh, idx_row[0], tid);
+    v_sstore<D>(vr, smem + KBYTES, tid);
+    __builtin_amdgcn_s_waitcnt(0);  // direct K loads have landed in LDS
     __syncthreads();
 
     f32x16 oacc[NDB];
@@ -246,12 +318,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
+    float l_run = 0.0f;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
     for (int t = 0; t < T; ++t) {
         const int cur = t & 1;
         const bool more = t + 1 < T;
-        if (more) kv = kv_gload<D, KIT, VTASK>(kh, vh, idx_row[(t + 1) % 3], tid, vquad, vchunk);
+        if (more) {
+            k_direct<D>(smem + (cur ^ 1) * BUF, kh, idx_row[(t + 1) % 3], wave, lane);
+            v_gload<D>(vr, vh, idx_row[(t + 1) % 3], tid);
+        }
         int32_t nrow = 0;
         float nbias = 0.0f;
         const bool fetch2 = wave == 0 && t + 2 < T;
@@ -264,68 +340,62 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const uint8_t *vb = kb + KBYTES;
             f32x16 sacc[2];
 #pragma unroll
-            for (int kb2 = 0; kb2 < 2; ++kb2)
+            for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[kb2][r] = 0.0f;
+                for (int r = 0; r < 16; ++r) sacc[k2][r] = 0.0f;
 #pragma unroll
             for (int s = 0; s < NDS; ++s) {
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(kb + (kb2 * 32 + l32) * KSTR + s * 32 + hl * 16);
-                    sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb2], 0, 0, 0);
-                }
+                const int c = s * 2 + hl;
+                const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kb + kswz<D>(l32, c) * 16);
+                const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kb + kswz<D>(32 + l32, c) * 16);
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], sacc[1], 0, 0, 0);
             }
-            // Logits in log2 units; lane holds keys kb2*32 + 8g + 4hl + e (e = 0..3) of
-            // its query.  A tile made only of exact columns has no offsets.
+            // Logits in log2 units; lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of
+            // its query.  Exact tiles keep raw scores (cf = scale log2 e); tiles with
+            // sampled or padded columns get scale and offset folded in (cf = 1).
             const int slot = t % 3;
             const bool exact_tile = (t + 1) * kTK <= X;
-            float mx;
-            if (exact_tile) {
-                float mr = sacc[0][0];
+            const float cf = exact_tile ? scale_log2 : 1.0f;
+            if (!exact_tile) {
 #pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sacc[kb2][r]);
-                mx = mr * scale_log2;
-            } else {
-                mx = -INFINITY;
-#pragma unroll
-                for (int kb2 = 0; kb2 < 2; ++kb2)
+                for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(&idx_bias[slot][kb2 * 32 + g * 8 + hl * 4]);
+                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(&idx_bias[slot][k2 * 32 + g * 8 + hl * 4]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const float v = fmaf(sacc[kb2][4 * g + e], scale_log2, bv[e]);
-                            sacc[kb2][4 * g + e] = v;
-                            mx = fmaxf(mx, v);
-                        }
+                        for (int e = 0; e < 4; ++e)
+                            sacc[k2][4 * g + e] = fmaf(sacc[k2][4 * g + e], scale_log2, bv[e]);
                     }
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // Lazy rescale: O and l stay relative to m_run until some lane's maximum
-            // exceeds it by more than 8 (weights up to 2^8 are safe in bf16 and fp32).
-            if (__any(mx > m_run + 8.0f)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
+            if (!FIXED) {
+                float mr = sacc[0][0];
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                m_run = m_new;
+                    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sacc[k2][r]);
+                float mx = mr * cf;
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                // lazy rescale: O and l stay relative to m_run until some lane's
+                // maximum exceeds it by more than 8 (weights up to 2^8 are safe)
+                if (__any(mx > m_run + 8.0f)) {
+                    const float m_new = fmaxf(m_run, mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                    m_run = m_new;
+                }
             }
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            const float mneg = -m_run;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 bf16x8 pb;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float v = sacc[s >> 1][8 * (s & 1) + e];
-                    const float p = exact_tile ? __builtin_amdgcn_exp2f(fmaf(v, scale_log2, -m_run))
-                                               : __builtin_amdgcn_exp2f(v - m_run);
-                    pb[e] = (__bf16)p;
-                }
+                for (int e = 0; e < 8; ++e)
+                    pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cf, mneg));
                 // row sum of the rounded weights, the same ones P.V uses
 #pragma unroll
                 for (int e = 0; e < 8; e += 2) {
@@ -339,16 +409,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 }
             }
         }
-        if (more) kv_sstore<D, KIT, VTASK>(kv, smem + (cur ^ 1) * BUF, tid, vquad, vchunk);
+        if (more) v_sstore<D>(vr, smem + (cur ^ 1) * BUF + KBYTES, tid);
         if (fetch2) {
             idx_row[(t + 2) % 3][lane] = nrow;
             idx_bias[(t + 2) % 3][lane] = nbias;
         }
+        __builtin_amdgcn_s_waitcnt(0);  // direct K loads of the next tile have landed
         __syncthreads();
     }
 
     if (!wave_active) return;
     const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (FIXED && __any(qrow_raw < r1 && !(l_tot >= 8.271806e-25f))) {  // 2^-80
+        if (lane == 0) redo[lb] = 1;
+        return;
+    }
     const float inv = 1.0f / l_tot;
     if (qrow_raw < r1) {
         uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
@@ -443,7 +518,7 @@ struct Layout {
     int64_t cap;       // columns per group in the column map
     int tph;           // tile slots per head
     int ntotal;        // launched blocks (multiple of 8)
-    size_t off_row, off_bias, off_len, off_x, off_table, total;
+    size_t off_row, off_bias, off_len, off_x, off_bmax, off_kmax, off_redo, off_table, total;
 };
 
 Layout layout(int B, int H, int N, int Cq, int m, int tq)
@@ -459,6 +534,9 @@ Layout layout(int B, int H, int N, int Cq, int m, int tq)
     L.off_bias = o; o += isg_align256((size_t)G * L.cap * sizeof(float));
     L.off_len = o; o += isg_align256((size_t)G * sizeof(int32_t));
     L.off_x = o; o += isg_align256((size_t)G * sizeof(int32_t));
+    L.off_bmax = o; o += isg_align256((size_t)G * sizeof(float));
+    L.off_kmax = o; o += isg_align256((size_t)B * H * sizeof(int));
+    L.off_redo = o; o += isg_align256((size_t)L.ntotal * sizeof(int));
     L.off_table = o; o += isg_align256((size_t)L.ntotal * sizeof(int4));
     L.total = o;
     return L;
@@ -509,20 +587,35 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     float *col_bias = (float *)(ws + Lq.off_bias);
     int32_t *col_len = (int32_t *)(ws + Lq.off_len);
     int32_t *col_x = (int32_t *)(ws + Lq.off_x);
+    float *col_bmax = (float *)(ws + Lq.off_bmax);
+    int *kmax2 = (int *)(ws + Lq.off_kmax);
+    int *redo = (int *)(ws + Lq.off_redo);
     int4 *table = (int4 *)(ws + Lq.off_table);
     columns_kernel<<<(unsigned)G, 256, 0, st>>>(k_offsets, exact_groups, n_exact, sample_idx, sample_bias,
-                                               n_sample, Cq, Ck, m, Lq.cap, col_row, col_bias, col_len, col_x);
-    tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table);
+                                               n_sample, Cq, Ck, m, Lq.cap, col_row, col_bias, col_len, col_x, col_bmax);
+    tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table, redo, kmax2);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if (dt == ISG_BF16) {
-        if (d == 128)
-            attn_bf16_kernel<128><<<Lq.ntotal, 256, 0, st>>>(
+        // fast kernel (fixed per-row reference), then the rescaling kernel on the
+        // tiles the fast one flagged (rows whose logits all sit far below the bound)
+        const dim3 kgrid((unsigned)((N + 255) / 256), (unsigned)(B * H));
+        if (d == 128) {
+            kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
+            attn_bf16_kernel<128, true><<<Lq.ntotal, 256, 0, st>>>(
                 (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, col_x, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p);
-        else
-            attn_bf16_kernel<64><<<Lq.ntotal, 256, 0, st>>>(
+                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+            attn_bf16_kernel<128, false><<<Lq.ntotal, 256, 0, st>>>(
                 (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, col_x, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p);
+                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+        } else {
+            kmax_kernel<64><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
+            attn_bf16_kernel<64, true><<<Lq.ntotal, 256, 0, st>>>(
+                (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
+                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+            attn_bf16_kernel<64, false><<<Lq.ntotal, 256, 0, st>>>(
+                (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
+                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+        }
     } else {
         if (d == 128)
             attn_f32_kernel<128><<<Lq.ntotal, 256, 0, st>>>((const float *)q_p, (const float *)k_p,

@@ -195,6 +195,38 @@ def test_attention_given_lists(orc, H, N, d, dtype, Cq, Ck, E, m):
         assert err <= 1e-4 and lerr <= 1e-4
 
 
+def test_attention_extreme_logit_range_falls_back(orc):
+    """Queries and keys anti-aligned with large norms: the Cauchy-Schwarz reference
+    of the fast kernel sits ~2000 log2 units above every logit, all its weights
+    underflow, and the tile must be recomputed by the rescaling kernel."""
+    H, N, d, Cq, Ck = 1, 2048, 128, 8, 32
+    g = torch.Generator().manual_seed(5)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = (200.0 * u + 0.05 * torch.randn(1, H, N, d, generator=g)).to(torch.bfloat16)
+    k = (-200.0 * u + 0.05 * torch.randn(1, H, N, d, generator=g)).to(torch.bfloat16)
+    v = torch.randn(1, H, N, d, generator=g).to(torch.bfloat16)
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    scale = isg.default_scale(d)
+    cq = isg.isg_cluster(qg, Cq, 5)
+    ck = isg.isg_cluster(kg, Ck, 5, companion=vg)
+    S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+    sel = isg.isg_select_sample(S, ck["offsets"], N, 300, 300, seed=1)
+    o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
+                                   ck["offsets"], sel, scale)
+    torch.cuda.synchronize()
+    selo = {kk: npy(vv) for kk, vv in sel.items() if kk != "m"}
+    oo, lo = orc.attention(f32(cq["x_perm"]), f32(ck["x_perm"]), f32(ck["companion_perm"]), npy(cq["offsets"]),
+                           npy(ck["offsets"]), selo, 300, scale)
+    assert np.isfinite(f32(o_p)).all()
+    err = np.abs(f32(o_p) - oo).max()
+    say(f"  extreme range: max|O-O_oracle| {err:.3e}, LSE range {lo.min():.1f}..{lo.max():.1f}")
+    assert err <= 2e-2
+    assert lo.max() < -1000  # the case really is extreme
+    # |LSE| ~ 3500 here: fp32 logits carry ~1e-7 relative error on top of the bf16 bar
+    assert np.abs(npy(lse_p) - lo).max() <= LSE_TOL_BF16 + 1e-6 * np.abs(lo).max()
+
+
 def test_attention_high_entropy_zipf(orc):
     """Near-uniform attention (Q scaled by 0.2) with Zipf cluster sizes."""
     *_, o_p, lse_p, oo, lo = _attn_case(orc, 2, 4096, 128, "bf16", 16, 64, 300, 300, q_scale=0.2, zipf=1.2)
