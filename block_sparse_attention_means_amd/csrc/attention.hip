@@ -229,6 +229,121 @@ __device__ __forceinline__ void v_sstore(const VRegs &r, uint8_t *vb, int tid)
     }
 }
 
+// One tile step of the attention loop: multiply the 64 columns of tile t held in
+// (kcur, vcur) while tile t+1 is being fetched into (knext, vnext).  The four
+// buffers are distinct LDS objects, so the compiler can see that reading the
+// current tile does not depend on the direct loads filling the next one.
+template <int D, bool FIXED>
+__device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kcur, const uint8_t *vcur,
+                                          uint8_t *knext, uint8_t *vnext, const uint16_t *kh, const uint16_t *vh,
+                                          const int32_t *crow, const float *cbias, int (*idx_row)[kTK],
+                                          float (*idx_bias)[kTK], const bf16x8 *qf, f32x16 *oacc, float &l_run,
+                                          float &m_run, VRegs &vr, float scale_log2, bool wave_active, int tid,
+                                          int wave, int lane, int hl, int l32)
+{
+    constexpr int NDS = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int VSTR = kTK * 2 + 16;
+    const bool more = t + 1 < T;
+    if (more) k_direct<D>(knext, kh, idx_row[(t + 1) % 3], wave, lane);
+    int32_t nrow = 0;
+    float nbias = 0.0f;
+    const bool fetch2 = wave == 0 && t + 2 < T;
+    if (fetch2) {
+        nrow = crow[(int64_t)(t + 2) * kTK + lane];
+        nbias = cbias[(int64_t)(t + 2) * kTK + lane];
+    }
+    f32x16 sacc[2];
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[k2][r] = 0.0f;
+    if (wave_active) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+            const int c = s * 2 + hl;
+            const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kcur + kswz<D>(l32, c) * 16);
+            const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kcur + kswz<D>(32 + l32, c) * 16);
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], sacc[1], 0, 0, 0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+    }
+    // the next tile's V rows: fetched here so their registers live only through P.V
+    if (more) v_gload<D>(vr, vh, idx_row[(t + 1) % 3], tid);
+    if (wave_active) {
+        // Logits in log2 units; lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of
+        // its query.  Exact tiles keep raw scores (cf = scale log2 e); tiles with
+        // sampled or padded columns get scale and offset folded in (cf = 1).
+        const int slot = t % 3;
+        const bool exact_tile = (t + 1) * kTK <= X;
+        const float cf = exact_tile ? scale_log2 : 1.0f;
+        if (!exact_tile) {
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(&idx_bias[slot][k2 * 32 + g * 8 + hl * 4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sacc[k2][4 * g + e] = fmaf(sacc[k2][4 * g + e], scale_log2, bv[e]);
+                }
+        }
+        if (!FIXED) {
+            float mr = sacc[0][0];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sacc[k2][r]);
+            float mx = mr * cf;
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // lazy rescale: O and l stay relative to m_run until some lane's maximum
+            // exceeds it by more than 8 (weights up to 2^8 are safe)
+            if (__any(mx > m_run + 8.0f)) {
+                const float m_new = fmaxf(m_run, mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m_run = m_new;
+            }
+        }
+        const float mneg = -m_run;
+        // raised wave priority while this wave issues MFMAs lets the SIMD's other
+        // wave fill the VALU slots (and vice versa)
+        __builtin_amdgcn_s_setprio(1);
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cf, mneg));
+            // row sum of the rounded weights, the same ones P.V uses
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const bf16x2 pp = {pb[e], pb[e + 1]};
+                l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vcur + (db * 32 + l32) * VSTR + (s * 16 + hl * 8) * 2);
+                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+            }
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (more) v_sstore<D>(vr, vnext, tid);
+    if (fetch2) {
+        idx_row[(t + 2) % 3][lane] = nrow;
+        idx_bias[(t + 2) % 3][lane] = nbias;
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // direct K loads of the next tile have landed
+    __syncthreads();
+}
+
 // One work-group = 4 waves x 32 query rows of one query group; two work-groups
 // per CU.  S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, so each
 // lane owns one query: its weights stay in registers and feed P.V directly.
@@ -251,9 +366,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NDS = D / 16;          // 16-wide d steps of S^T = K Q^T
     constexpr int NDB = D / 32;          // 32-row d blocks of O^T
     constexpr int KBYTES = kTK * D * 2;
-    constexpr int VSTR = kTK * 2 + 16;   // bytes per transposed V row (one d) in LDS
-    constexpr int BUF = KBYTES + D * VSTR;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * BUF];
+    constexpr int VBYTES = D * (kTK * 2 + 16);  // transposed V, rows padded to 144 bytes
+    __shared__ __attribute__((aligned(1024))) uint8_t kb0[KBYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t kb1[KBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t vb0[VBYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t vb1[VBYTES];
     __shared__ int idx_row[3][kTK];
     __shared__ __attribute__((aligned(16))) float idx_bias[3][kTK];
 
@@ -307,9 +424,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();
     VRegs vr;
-    k_direct<D>(smem, kh, idx_row[0], wave, lane);
+    k_direct<D>(kb0, kh, idx_row[0], wave, lane);
     v_gload<D>(vr, vh, idx_row[0], tid);
-    v_sstore<D>(vr, smem + KBYTES, tid);
+    v_sstore<D>(vr, vb0, tid);
     __builtin_amdgcn_s_waitcnt(0);  // direct K loads have landed in LDS
     __syncthreads();
 
@@ -319,103 +436,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
     float l_run = 0.0f;
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-    for (int t = 0; t < T; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < T;
-        if (more) {
-            k_direct<D>(smem + (cur ^ 1) * BUF, kh, idx_row[(t + 1) % 3], wave, lane);
-            v_gload<D>(vr, vh, idx_row[(t + 1) % 3], tid);
-        }
-        int32_t nrow = 0;
-        float nbias = 0.0f;
-        const bool fetch2 = wave == 0 && t + 2 < T;
-        if (fetch2) {
-            nrow = crow[(int64_t)(t + 2) * kTK + lane];
-            nbias = cbias[(int64_t)(t + 2) * kTK + lane];
-        }
-        if (wave_active) {
-            const uint8_t *kb = smem + cur * BUF;
-            const uint8_t *vb = kb + KBYTES;
-            f32x16 sacc[2];
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[k2][r] = 0.0f;
-#pragma unroll
-            for (int s = 0; s < NDS; ++s) {
-                const int c = s * 2 + hl;
-                const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kb + kswz<D>(l32, c) * 16);
-                const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kb + kswz<D>(32 + l32, c) * 16);
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], sacc[1], 0, 0, 0);
-            }
-            // Logits in log2 units; lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of
-            // its query.  Exact tiles keep raw scores (cf = scale log2 e); tiles with
-            // sampled or padded columns get scale and offset folded in (cf = 1).
-            const int slot = t % 3;
-            const bool exact_tile = (t + 1) * kTK <= X;
-            const float cf = exact_tile ? scale_log2 : 1.0f;
-            if (!exact_tile) {
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 bv = *reinterpret_cast<const f32x4 *>(&idx_bias[slot][k2 * 32 + g * 8 + hl * 4]);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sacc[k2][4 * g + e] = fmaf(sacc[k2][4 * g + e], scale_log2, bv[e]);
-                    }
-            }
-            if (!FIXED) {
-                float mr = sacc[0][0];
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sacc[k2][r]);
-                float mx = mr * cf;
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                // lazy rescale: O and l stay relative to m_run until some lane's
-                // maximum exceeds it by more than 8 (weights up to 2^8 are safe)
-                if (__any(mx > m_run + 8.0f)) {
-                    const float m_new = fmaxf(m_run, mx);
-                    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                    l_run *= alpha;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                    m_run = m_new;
-                }
-            }
-            const float mneg = -m_run;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8 pb;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cf, mneg));
-                // row sum of the rounded weights, the same ones P.V uses
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const bf16x2 pp = {pb[e], pb[e + 1]};
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-                }
-#pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vb + (db * 32 + l32) * VSTR + (s * 16 + hl * 8) * 2);
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
-                }
-            }
-        }
-        if (more) v_sstore<D>(vr, smem + (cur ^ 1) * BUF + KBYTES, tid);
-        if (fetch2) {
-            idx_row[(t + 2) % 3][lane] = nrow;
-            idx_bias[(t + 2) % 3][lane] = nbias;
-        }
-        __builtin_amdgcn_s_waitcnt(0);  // direct K loads of the next tile have landed
-        __syncthreads();
+    for (int t = 0; t < T; t += 2) {
+        tile_step<D, FIXED>(t, T, X, kb0, vb0, kb1, vb1, kh, vh, crow, cbias, idx_row, idx_bias, qf, oacc, l_run,
+                            m_run, vr, scale_log2, wave_active, tid, wave, lane, hl, l32);
+        if (t + 1 < T)
+            tile_step<D, FIXED>(t + 1, T, X, kb1, vb1, kb0, vb0, kh, vh, crow, cbias, idx_row, idx_bias, qf, oacc,
+                                l_run, m_run, vr, scale_log2, wave_active, tid, wave, lane, hl, l32);
     }
 
     if (!wave_active) return;
