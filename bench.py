@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--exact", type=float, default=0.08)
     ap.add_argument("--sample", type=float, default=0.08)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--mode", default=None, choices=["importance", "uniform", "votes"],
+                    help="sampling mode (default: votes for a workload with product quantisation, else importance)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time the attention at every budget of the workload")
     ap.add_argument("--attention-only", type=int, default=0, metavar="K",
@@ -66,7 +68,7 @@ def attention_flops(d, q_offsets, k_offsets, exact_groups, n_exact, n_sample):
     return float(4 * d * (nq * cols).sum()), float((nq * cols).sum())
 
 
-def cpu_baseline(w, q, k, v, E, m, seed):
+def cpu_baseline(w, q, k, v, E, m, seed, mode="importance"):
     """The oracle as it stands on one head of the workload: every stage on the whole
     head except attention, which runs on a sample of query groups and is scaled to all
     groups of the head by its share of the head's attention flops."""
@@ -81,7 +83,16 @@ def cpu_baseline(w, q, k, v, E, m, seed):
     cq = oracle.cluster(qh, Cq, w["iters"])
     ck = oracle.cluster(kh, Ck, w["iters"], companion=vh)
     S, _ = oracle.probs(cq["centroids"], ck["centroids"], ck["offsets"], scale)
-    sel = oracle.select_sample(S, ck["offsets"], N, E, m, seed=seed)
+    votes = None
+    if mode == "votes":
+        P, Cc = w["pq"]
+        qc, qcb = oracle.pq_codebooks(qh, P, Cc, w["iters"])
+        kc, kcb = oracle.pq_codebooks(kh, P, Cc, w["iters"])
+        kbar = oracle.pq_kbar(kc, kcb, ck["perm"], ck["offsets"])
+        tables = oracle.pq_tables(qcb, kbar, scale)
+        votes = oracle.pq_votes(qc, tables, cq["perm"], cq["offsets"], ck["offsets"], E)
+    sel = oracle.select_sample(S, ck["offsets"], N, E, m, seed=seed, mode={"importance": 0, "uniform": 1,
+                                                                          "votes": 2}[mode], votes=votes)
     t_pre = time.perf_counter() - t0
     nq = np.diff(cq["offsets"][0, 0])
     nk = np.diff(ck["offsets"][0, 0])
@@ -104,7 +115,8 @@ def cpu_baseline(w, q, k, v, E, m, seed):
     t_head = t_pre + t_att / frac + t_un
     flops_head = 4.0 * d * work.sum()
     return {"value": flops_head / t_head / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": (f"1 of {w['H']} heads of {w.get('name')}: clustering, scores, selection and "
+            "sample": (f"1 of {w['H']} heads of {w.get('name')}: clustering, scores, "
+                       f"{'PQ votes, ' if mode == 'votes' else ''}selection and "
                        f"un-permute on the whole head ({t_pre + t_un:.1f} s); attention on the "
                        f"{len(pick)} heaviest query groups ({frac * 100:.1f} % of the head's attention flops, "
                        f"{t_att:.1f} s) scaled to the head; fp64 C with OpenMP"),
@@ -141,6 +153,10 @@ def main():
     w["name"] = args.workload
     B, H, N, d = w.get("B", 1), w["H"], w["N"], w["d"]
     E, m = budget_keys(args.exact, N), budget_keys(args.sample, N)
+    mode = args.mode or ("votes" if w.get("pq") else "importance")
+    if mode == "votes" and not w.get("pq"):
+        print(f"bench.py: workload {args.workload} has no product-quantisation setting", file=sys.stderr)
+        sys.exit(2)
     t0 = time.perf_counter()
     q, k, v, _ = make_workload(w, seed=args.seed)
     print(f"# inputs generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
@@ -150,7 +166,8 @@ def main():
     stream = torch.cuda.current_stream()
     ws_c = torch.empty(isg.cluster_workspace_size(B, H, N, d, max(w["Cq"], w["Ck"])), device=dev, dtype=torch.uint8)
     ws_a = torch.empty(isg.attention_workspace_size(B, H, N, w["Cq"], w["Ck"]), device=dev, dtype=torch.uint8)
-    stages = ["cluster_q", "cluster_k", "probs", "select_sample", "attention", "unpermute"]
+    stages = ["cluster_q", "cluster_k", "probs"] + (["pq_codes", "pq_votes"] if mode == "votes" else []) + [
+        "select_sample", "attention", "unpermute"]
     ev = {s: [] for s in stages}
 
     def step(record):
@@ -164,18 +181,35 @@ def main():
         if record:
             marks[2].record(stream)
         S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+        mi = 3
         if record:
-            marks[3].record(stream)
-        sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, seed=args.seed)
+            marks[mi].record(stream)
+        votes = None
+        if mode == "votes":
+            P, Cc = w["pq"]
+            qc, qcb = isg.pq_codebooks(qg, P, Cc, w["iters"])
+            kc, kcb = isg.pq_codebooks(kg, P, Cc, w["iters"])
+            mi += 1
+            if record:
+                marks[mi].record(stream)
+            votes = isg.isg_pq_votes(qc, qcb, kc, kcb, cq["perm"], cq["offsets"], ck["perm"], ck["offsets"], E,
+                                     scale)["votes"]
+            mi += 1
+            if record:
+                marks[mi].record(stream)
+        sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, mode=mode, seed=args.seed, votes=votes)
+        mi += 1
         if record:
-            marks[4].record(stream)
+            marks[mi].record(stream)
         o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
                                        ck["offsets"], sel, scale, workspace=ws_a)
+        mi += 1
         if record:
-            marks[5].record(stream)
+            marks[mi].record(stream)
         o, lse = isg.isg_unpermute(o_p, lse_p, cq["perm"])
+        mi += 1
         if record:
-            marks[6].record(stream)
+            marks[mi].record(stream)
             for si, s in enumerate(stages):
                 ev[s].append((marks[si], marks[si + 1]))
         return cq, ck, sel, o
@@ -219,7 +253,8 @@ def main():
         "data": "synthetic (seeded Gaussian-mixture Q/K with 3-D locality bias, V ~ N(0,1); no model weights)",
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "Cq": w["Cq"], "Ck": w["Ck"],
                    "kmeans_iters": w["iters"], "exact_share": args.exact, "sample_share": args.sample,
-                   "exact_keys": E, "m": m, "seed": args.seed},
+                   "exact_keys": E, "m": m, "seed": args.seed, "mode": mode,
+                   "pq": list(w["pq"]) if mode == "votes" else None},
         "attention_ms": round(att_ms, 3),
         "attention_tflops": round(att_tflops, 2),
         "attention_tflop_per_call": round(flops / 1e12, 4),
@@ -233,7 +268,8 @@ def main():
         for (es, ss) in w["sweep"]:
             E2, m2 = budget_keys(es, N), budget_keys(ss, N)
             S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
-            sel2 = isg.isg_select_sample(S, ck["offsets"], N, E2, m2, seed=args.seed)
+            sel2 = isg.isg_select_sample(S, ck["offsets"], N, E2, m2, seed=args.seed,
+                                         mode="uniform" if mode == "uniform" else "importance")
             f2, _ = attention_flops(d, cq["offsets"], ck["offsets"], sel2["exact_groups"], sel2["n_exact"],
                                     sel2["n_sample"])
             for _ in range(2):
@@ -253,7 +289,7 @@ def main():
         result["attention_sweep"] = sweep
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, E, m, args.seed)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, E, m, args.seed, mode)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -18,8 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libisg.so")
 
-SOURCES = ["util.hip", "cluster.hip", "select.hip", "attention.hip", "unpermute.hip"]
-EXTRA = {"select.hip": ["-ffp-contract=off"]}
+SOURCES = ["util.hip", "cluster.hip", "select.hip", "attention.hip", "unpermute.hip", "pq.hip"]
+EXTRA = {"select.hip": ["-ffp-contract=off"], "pq.hip": ["-ffp-contract=off"]}
 
 
 def hipcc() -> str:

@@ -18,7 +18,7 @@ ISG_F32, ISG_BF16 = 0, 1
 MODES = {"importance": 0, "uniform": 1, "votes": 2}
 EXPORTS = ["isg_last_error", "isg_version", "isg_proposal_table", "isg_cluster_workspace_size",
            "isg_cluster", "isg_probs", "isg_select_sample", "isg_attention_workspace_size",
-           "isg_attention", "isg_unpermute"]
+           "isg_attention", "isg_unpermute", "isg_pq_votes"]
 
 _lib = None
 
@@ -57,7 +57,10 @@ def _declare(L):
     L.isg_attention.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                                 _i, _f, _p, _p, _p, _sz]
     L.isg_unpermute.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p]
-    for name in ["isg_cluster", "isg_probs", "isg_select_sample", "isg_attention", "isg_unpermute"]:
+    L.isg_pq_votes.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
+                               _p, _p, _p]
+    for name in ["isg_cluster", "isg_probs", "isg_select_sample", "isg_attention", "isg_unpermute",
+                 "isg_pq_votes"]:
         getattr(L, name).restype = _i
 
 
@@ -212,23 +215,84 @@ def isg_unpermute(o_p, lse_p, perm_q, *, out=None, lse_out=None, stream=None):
     return o, lse
 
 
+def pq_codebooks(x, P, Cc, iters, *, stream=None):
+    """Product-quantisation codes [P,B,H,N] and codebooks [P,B,H,Cc,d/P] of x [B,H,N,d]:
+    one isg_cluster call per subspace, on a strided view, writing in place."""
+    _dev(x, "x")
+    B, H, N, d = x.shape
+    if x.stride(3) != 1 or d % P:
+        raise IsgError("x must have a contiguous last dimension divisible into P subspaces")
+    ds = d // P
+    dev = x.device
+    codes = torch.empty((P, B, H, N), device=dev, dtype=torch.int32)
+    cbs = torch.empty((P, B, H, Cc, ds), device=dev, dtype=torch.float32)
+    perm = torch.empty((B, H, N), device=dev, dtype=torch.int32)
+    offsets = torch.empty((B, H, Cc + 1), device=dev, dtype=torch.int32)
+    ws = torch.empty(max(cluster_workspace_size(B, H, N, ds, Cc), 1), device=dev, dtype=torch.uint8)
+    for s in range(P):
+        xs = x[..., s * ds:(s + 1) * ds]
+        st = lib().isg_cluster(_stream(stream), _ptr(xs), _dtype(x), _i64x3(xs.stride()[:3]), B, H, N, ds, Cc,
+                               iters, 0, None, _ptr(cbs[s]), _ptr(codes[s]), _ptr(perm), _ptr(offsets), None, None,
+                               _ptr(ws), ws.numel())
+        _check(st, "isg_cluster (subspace)")
+    return codes, cbs
+
+
+def isg_pq_votes(q_codes, q_codebooks, k_codes, k_codebooks, perm_q, q_offsets, perm_k, k_offsets, exact_keys,
+                 scale, *, stream=None):
+    """Per-query PQ votes [B,H,Cq,Ck] (plus the Kbar and table intermediates)."""
+    for n, t in (("q_codes", q_codes), ("q_codebooks", q_codebooks), ("k_codes", k_codes),
+                 ("k_codebooks", k_codebooks), ("perm_q", perm_q), ("q_offsets", q_offsets),
+                 ("perm_k", perm_k), ("k_offsets", k_offsets)):
+        _dev(t, n)
+    P, B, H, N = q_codes.shape
+    Cc, ds = q_codebooks.shape[-2:]
+    if k_codes.shape != q_codes.shape or k_codebooks.shape != q_codebooks.shape:
+        raise IsgError("query and key codes/codebooks must have the same shapes")
+    d = P * ds
+    Cq, Ck = q_offsets.shape[-1] - 1, k_offsets.shape[-1] - 1
+    dev = q_codes.device
+    kbar = torch.empty((B, H, Ck, d), device=dev, dtype=torch.float32)
+    tables = torch.empty((B, H, P, Cc, Ck), device=dev, dtype=torch.float32)
+    votes = torch.empty((B, H, Cq, Ck), device=dev, dtype=torch.int32)
+    st = lib().isg_pq_votes(_stream(stream), _ptr(q_codes.contiguous()), _ptr(q_codebooks.contiguous()),
+                            _ptr(k_codes.contiguous()), _ptr(k_codebooks.contiguous()), _ptr(perm_q.contiguous()),
+                            _ptr(q_offsets.contiguous()), _ptr(perm_k.contiguous()), _ptr(k_offsets.contiguous()),
+                            B, H, N, d, P, Cc, Cq, Ck, int(exact_keys), float(scale), _ptr(kbar), _ptr(tables),
+                            _ptr(votes))
+    _check(st, "isg_pq_votes")
+    return dict(kbar=kbar, tables=tables, votes=votes)
+
+
 def default_scale(d: int) -> float:
     """1/sqrt(d) rounded to fp32 (the softmax scale of standard attention)."""
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
 
 
 def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0, call_id=0, scale=None,
-             stream=None):
-    """All steps on one batch: cluster Q, cluster K (+V), probs, select/sample,
-    attention, unpermute.  Returns every intermediate (all on the GPU)."""
+             pq=None, stream=None):
+    """All steps on one batch: cluster Q, cluster K (+V), probs, [PQ votes],
+    select/sample, attention, unpermute.  ``pq=(P, Cc)`` is required by
+    mode "votes".  Returns every intermediate (all on the GPU)."""
     d = q.shape[-1]
     scale = default_scale(d) if scale is None else scale
     cq = isg_cluster(q, Cq, iters, stream=stream)
     ck = isg_cluster(k, Ck, iters, companion=v, stream=stream)
     scores, pi = isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, stream=stream)
+    pqr = None
+    if (MODES[mode] if isinstance(mode, str) else int(mode)) == MODES["votes"]:
+        if pq is None:
+            raise IsgError('mode "votes" needs pq=(P, Cc)')
+        P, Cc = pq
+        qc, qcb = pq_codebooks(q, P, Cc, iters, stream=stream)
+        kc, kcb = pq_codebooks(k, P, Cc, iters, stream=stream)
+        pqr = isg_pq_votes(qc, qcb, kc, kcb, cq["perm"], cq["offsets"], ck["perm"], ck["offsets"], exact_keys,
+                           scale, stream=stream)
+        pqr.update(q_codes=qc, q_codebooks=qcb, k_codes=kc, k_codebooks=kcb)
     sel = isg_select_sample(scores, ck["offsets"], q.shape[2], exact_keys, m, mode=mode, seed=seed,
-                            call_id=call_id, stream=stream)
+                            call_id=call_id, votes=None if pqr is None else pqr["votes"], stream=stream)
     o_p, lse_p = isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
                                sel, scale, stream=stream)
     o, lse = isg_unpermute(o_p, lse_p, cq["perm"], stream=stream)
-    return dict(cq=cq, ck=ck, scores=scores, pi=pi, sel=sel, o_p=o_p, lse_p=lse_p, o=o, lse=lse, scale=scale)
+    return dict(cq=cq, ck=ck, scores=scores, pi=pi, pq=pqr, sel=sel, o_p=o_p, lse_p=lse_p, o=o, lse=lse,
+                scale=scale)

@@ -194,6 +194,39 @@ isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, cons
                          isg_dtype dt, int B, int H, int N, int d, void *o,
                          const int64_t o_strides[3], float *lse);
 
+/* ------------------------------------------------------------------------ */
+/* isg_pq_votes -- product-quantised per-query votes for the exact set.
+ * Pages: InstaGen, acceptodds.com page, abstract (queries and keys are product-
+ * quantised so that block scores are cheap enough for every query; each query
+ * votes for its top blocks; a query group's exact set is the blocks with the
+ * most votes).  The pages give no formula; the reading taken:
+ *   Kbar_{j,s} = mean over the rows of key group j of their subspace-s codeword
+ *                (fp64 sum in permuted row order, one division, fp32 result;
+ *                0 for an empty group);
+ *   M_s[a][j]  = (fp32 fused multiply-add chain over the ds dims of
+ *                cwq_{s,a} * Kbar_{j,s}) * scale;
+ *   score(q,j) = fp32 sum over s ascending of M_s[code_s(q)][j];
+ *   every query applies the exact-set rule of isg_select_sample to its own
+ *   ranking (score desc, j asc) and votes for each group it takes;
+ *   votes[i][j] = number of queries of group i that voted for j.
+ * The votes feed isg_select_sample in ISG_SAMPLE_VOTES mode.
+ *
+ * q_codes, k_codes   device int32 [P,B,H,N], token order: the labels of
+ *                    isg_cluster run on subspace s (dims [s*ds, (s+1)*ds), ds = d/P);
+ * q_codebooks, k_codebooks  device fp32 [P,B,H,Cc,ds]: that run's centroids;
+ * perm_q, q_offsets, perm_k, k_offsets  device int32, from isg_cluster on the
+ *                    full vectors ([B,H,N] and [B,H,C+1]);
+ * kbar    device fp32 [B,H,Ck,d] (written);
+ * tables  device fp32 [B,H,P,Cc,Ck] (written);
+ * votes   device int32 [B,H,Cq,Ck] (written).
+ * d <= 256, 1 <= P <= 16, P | d; Cc in [1, 4096]; Cq, Ck in [1, 1024];
+ * exact_keys >= 0; codes must lie in [0, Cc) (not checked). */
+isg_status isg_pq_votes(void *stream, const int32_t *q_codes, const float *q_codebooks,
+                        const int32_t *k_codes, const float *k_codebooks, const int32_t *perm_q,
+                        const int32_t *q_offsets, const int32_t *perm_k, const int32_t *k_offsets,
+                        int B, int H, int N, int d, int P, int Cc, int Cq, int Ck, int exact_keys,
+                        float scale, float *kbar, float *tables, int32_t *votes);
+
 #ifdef __cplusplus
 }
 #endif

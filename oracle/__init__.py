@@ -51,6 +51,9 @@ def _declare(L):
                                 _i, _f, _p, _p, _p]
     L.orc_dense.argtypes = [_p, _p, _p, _i, _i, _i, _i, _f, _p, _i, _p, _p]
     L.orc_unpermute.argtypes = [_p, _p, _p, _i, _i, _i, _i, _p, _p]
+    L.orc_pq_kbar.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p]
+    L.orc_pq_tables.argtypes = [_p, _p, _i, _i, _i, _i, _i, _i, _f, _p]
+    L.orc_pq_votes.argtypes = [_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p]
 
 
 def _c(a, dtype):
@@ -221,3 +224,56 @@ def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, mode=0, seed=0, call_id=0, s
     o, lse = unpermute(o_p, lse_p, cq["perm"])
     return dict(cq=cq, ck=ck, scores=S, pi=pi, sel=sel, o_p=o_p, lse_p=lse_p, o=o, lse=lse,
                 scale=scale)
+
+
+# ---------------------------------------------------------------- product-quantised voting
+def pq_codebooks(x, P, Cc, iters):
+    """Codes [P,B,H,N] and codebooks [P,B,H,Cc,d/P] from k-means of each subspace."""
+    x = _c(x, np.float32)
+    B, H, N, d = x.shape
+    ds = d // P
+    codes = np.zeros((P, B, H, N), np.int32)
+    cbs = np.zeros((P, B, H, Cc, ds), np.float32)
+    for s in range(P):
+        r = cluster(np.ascontiguousarray(x[..., s * ds:(s + 1) * ds]), Cc, iters, want_perm=False)
+        codes[s] = r["labels"]
+        cbs[s] = r["centroids"]
+    return codes, cbs
+
+
+def pq_kbar(k_codes, k_cb, perm_k, k_offsets):
+    k_codes = _c(k_codes, np.int32)
+    k_cb = _c(k_cb, np.float32)
+    pk = _c(perm_k, np.int32)
+    ko = _c(k_offsets, np.int32)
+    P, B, H, N = k_codes.shape
+    Cc, ds = k_cb.shape[-2:]
+    Ck = ko.shape[-1] - 1
+    kbar = np.zeros((B, H, Ck, P * ds), np.float32)
+    lib().orc_pq_kbar(_ptr(k_codes), _ptr(k_cb), _ptr(pk), _ptr(ko), B, H, N, P, Cc, ds, Ck, _ptr(kbar))
+    return kbar
+
+
+def pq_tables(q_cb, kbar, scale):
+    q_cb = _c(q_cb, np.float32)
+    kbar = _c(kbar, np.float32)
+    P, B, H, Cc, ds = q_cb.shape
+    Ck = kbar.shape[2]
+    t = np.zeros((B, H, P, Cc, Ck), np.float32)
+    lib().orc_pq_tables(_ptr(q_cb), _ptr(kbar), B, H, P, Cc, ds, Ck, float(scale), _ptr(t))
+    return t
+
+
+def pq_votes(q_codes, tables, perm_q, q_offsets, k_offsets, exact_keys):
+    q_codes = _c(q_codes, np.int32)
+    tables = _c(tables, np.float32)
+    pq_ = _c(perm_q, np.int32)
+    qo = _c(q_offsets, np.int32)
+    ko = _c(k_offsets, np.int32)
+    P, B, H, N = q_codes.shape
+    Cc = tables.shape[3]
+    Cq, Ck = qo.shape[-1] - 1, ko.shape[-1] - 1
+    v = np.zeros((B, H, Cq, Ck), np.int32)
+    lib().orc_pq_votes(_ptr(q_codes), _ptr(tables), _ptr(pq_), _ptr(qo), _ptr(ko), B, H, N, P, Cc, Cq, Ck,
+                       int(exact_keys), _ptr(v))
+    return v

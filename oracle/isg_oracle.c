@@ -466,3 +466,116 @@ void orc_unpermute(const double *o_p, const double *lse_p, const int32_t *perm_q
             if (lse && lse_p) lse[dst] = lse_p[bh * N + r];
         }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Product-quantised per-query voting, [A] (queries and keys are product-
+ * quantised so block scores are cheap per query; each query votes for its top
+ * blocks; the cluster attends to the blocks with the most votes).  The pages
+ * give no formula; the reading taken (parity unpinned by the pages):
+ *   codes: k-means of each d/P-dim subspace into Cc codewords (as orc_cluster);
+ *   Kbar_{j,s} = mean over the keys of group j of their subspace-s codeword;
+ *   M_s[a][j]  = scale * <cw^q_{s,a}, Kbar_{j,s}>   (fp32 fma chain over the dims);
+ *   score(q,j) = sum_s M_s[code_s(q)][j]           (fp32, s ascending);
+ *   each query ranks the non-empty key groups by (score desc, j asc), takes the
+ *   first always and the following ones while the key count stays <= exact_keys
+ *   (the exact-set rule), and votes for every group it takes;
+ *   votes[i][j] = number of queries of group i that voted for j.
+ * Layouts: codes [P,B,H,N] (token order), codebooks [P,B,H,Cc,ds], ds = d/P. */
+void orc_pq_kbar(const int32_t *k_codes, const float *k_cb, const int32_t *perm_k, const int32_t *k_offsets,
+                 int B, int H, int N, int P, int Cc, int ds, int Ck, float *kbar)
+{
+    int d = P * ds;
+    double *acc = (double *)malloc(sizeof(double) * (size_t)d);
+    for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+        int64_t bh = (int64_t)b * H + h;
+        const int32_t *ko = k_offsets + bh * (Ck + 1);
+        for (int j = 0; j < Ck; ++j) {
+            for (int e = 0; e < d; ++e) acc[e] = 0.0;
+            int n = ko[j + 1] - ko[j];
+            for (int r = ko[j]; r < ko[j + 1]; ++r) {
+                int t = perm_k[bh * N + r];
+                for (int s = 0; s < P; ++s) {
+                    int code = k_codes[(((int64_t)s * B + b) * H + h) * N + t];
+                    const float *cw = k_cb + ((((int64_t)s * B + b) * H + h) * Cc + code) * ds;
+                    for (int e = 0; e < ds; ++e) acc[s * ds + e] += (double)cw[e];
+                }
+            }
+            float *out = kbar + (bh * Ck + j) * d;
+            for (int e = 0; e < d; ++e) out[e] = n > 0 ? (float)(acc[e] / n) : 0.0f;
+        }
+    }
+    free(acc);
+}
+
+void orc_pq_tables(const float *q_cb, const float *kbar, int B, int H, int P, int Cc, int ds, int Ck,
+                   float scale, float *tables)
+{
+    int d = P * ds;
+    for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+        int64_t bh = (int64_t)b * H + h;
+        for (int s = 0; s < P; ++s)
+            for (int a = 0; a < Cc; ++a) {
+                const float *cw = q_cb + ((((int64_t)s * B + b) * H + h) * Cc + a) * ds;
+                for (int j = 0; j < Ck; ++j) {
+                    const float *kb = kbar + (bh * Ck + j) * d + s * ds;
+                    float acc = 0.0f;
+                    for (int e = 0; e < ds; ++e) acc = fmaf(cw[e], kb[e], acc);
+                    tables[(((bh * P + s) * Cc) + a) * Ck + j] = acc * scale;
+                }
+            }
+    }
+}
+
+static const float *g_vote_score;
+static int cmp_vote(const void *a, const void *b)
+{
+    int ja = *(const int *)a, jb = *(const int *)b;
+    if (g_vote_score[ja] != g_vote_score[jb]) return g_vote_score[ja] > g_vote_score[jb] ? -1 : 1;
+    return ja < jb ? -1 : (ja > jb ? 1 : 0);
+}
+
+void orc_pq_votes(const int32_t *q_codes, const float *tables, const int32_t *perm_q, const int32_t *q_offsets,
+                  const int32_t *k_offsets, int B, int H, int N, int P, int Cc, int Cq, int Ck, int exact_keys,
+                  int32_t *votes)
+{
+    float *score = (float *)malloc(sizeof(float) * Ck);
+    int *order = (int *)malloc(sizeof(int) * Ck);
+    for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+        int64_t bh = (int64_t)b * H + h;
+        const int32_t *qo = q_offsets + bh * (Cq + 1);
+        const int32_t *ko = k_offsets + bh * (Ck + 1);
+        for (int i = 0; i < Cq; ++i) {
+            int32_t *vi = votes + (bh * Cq + i) * Ck;
+            for (int j = 0; j < Ck; ++j) vi[j] = 0;
+            for (int r = qo[i]; r < qo[i + 1]; ++r) {
+                int t = perm_q[bh * N + r];
+                for (int j = 0; j < Ck; ++j) {
+                    float acc = 0.0f;
+                    for (int s = 0; s < P; ++s) {
+                        int code = q_codes[(((int64_t)s * B + b) * H + h) * N + t];
+                        acc += tables[(((bh * P + s) * Cc) + code) * Ck + j];
+                    }
+                    score[j] = acc;
+                }
+                int n_ne = 0;
+                for (int j = 0; j < Ck; ++j)
+                    if (ko[j + 1] > ko[j]) order[n_ne++] = j;
+                g_vote_score = score;
+                qsort(order, (size_t)n_ne, sizeof(int), cmp_vote);
+                int64_t cum = 0;
+                for (int p = 0; p < n_ne; ++p) {
+                    int j = order[p];
+                    int nj = ko[j + 1] - ko[j];
+                    if (p > 0 && cum + nj > exact_keys) break;
+                    cum += nj;
+                    vi[j] += 1;
+                }
+            }
+        }
+    }
+    free(score);
+    free(order);
+}

@@ -145,6 +145,23 @@ def test_unpermute_rejects(kw, status):
     assert _unperm(**kw) == status
 
 
+def _pq(**kw):
+    a = dict(qc=FAKE, qcb=FAKE, kc=FAKE, kcb=FAKE, pq=FAKE, qo=FAKE, pk=FAKE, ko=FAKE, B=1, H=1, N=256, d=128,
+             P=8, Cc=256, Cq=4, Ck=8, E=32, scale=0.088, kbar=FAKE, tab=FAKE, votes=FAKE)
+    a.update(kw)
+    return isg.lib().isg_pq_votes(None, a["qc"], a["qcb"], a["kc"], a["kcb"], a["pq"], a["qo"], a["pk"], a["ko"],
+                                  a["B"], a["H"], a["N"], a["d"], a["P"], a["Cc"], a["Cq"], a["Ck"], a["E"],
+                                  a["scale"], a["kbar"], a["tab"], a["votes"])
+
+
+@pytest.mark.parametrize("kw", [dict(qc=None), dict(votes=None), dict(tab=None), dict(N=0), dict(d=512),
+                                dict(P=3), dict(P=32, d=256), dict(Cc=0), dict(Cc=5000), dict(Cq=0),
+                                dict(Ck=1025), dict(E=-1), dict(scale=float("inf"))])
+def test_pq_votes_rejects(kw):
+    assert _pq(**kw) == 1
+    assert len(isg.lib().isg_last_error()) > 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 16, 16)

@@ -336,14 +336,15 @@ def test_unbiased_over_1000_seeds_gpu(orc):
 
 
 # ------------------------------------------------------------------ full sizes, sampled checks
-def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3):
+def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode="importance"):
     w = WORKLOADS[name]
     N, d = w["N"], w["d"]
     say(f"full size {name}: generating inputs")
     q, k, v, _ = make_workload(w)
     E, m = budget_keys(E_share, N), budget_keys(S_share, N)
-    say(f"full size {name}: pipeline E={E} m={m}")
-    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), w["Cq"], w["Ck"], w["iters"], E, m, seed=0)
+    say(f"full size {name}: pipeline E={E} m={m} mode={mode}")
+    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), w["Cq"], w["Ck"], w["iters"], E, m, seed=0, mode=mode,
+                     pq=w.get("pq"))
     torch.cuda.synchronize()
     Cq = w["Cq"]
     qo_all = npy(r["cq"]["offsets"])
@@ -351,7 +352,24 @@ def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3):
     # every head: scores, lists and sample indices bit-exact from the GPU's centroids
     S, _ = orc.probs(npy(r["cq"]["centroids"]), npy(r["ck"]["centroids"]), ko_all, r["scale"])
     assert np.array_equal(S, npy(r["scores"]))
-    sel = orc.select_sample(S, ko_all, N, E, m, seed=0)
+    votes = None
+    if mode == "votes":
+        pq = r["pq"]
+        votes = npy(pq["votes"])
+        rng = np.random.default_rng(1)
+        for h in heads:
+            hs = slice(h, h + 1)
+            kbar = orc.pq_kbar(npy(pq["k_codes"][:, :, hs]), npy(pq["k_codebooks"][:, :, hs]),
+                               npy(r["ck"]["perm"][:, hs]), ko_all[:, hs])
+            assert np.array_equal(kbar, npy(pq["kbar"][:, hs]))
+            tables = orc.pq_tables(npy(pq["q_codebooks"][:, :, hs]), kbar, r["scale"])
+            assert np.array_equal(tables, npy(pq["tables"][:, hs]))
+            i0 = int(rng.integers(0, Cq - 3))
+            vo = orc.pq_votes(npy(pq["q_codes"][:, :, hs]), tables, npy(r["cq"]["perm"][:, hs]),
+                              qo_all[:, hs, i0:i0 + 4], ko_all[:, hs], E)
+            say(f"  head {h}: PQ votes of groups {i0}..{i0 + 2} vs the oracle")
+            assert np.array_equal(vo[0, 0], votes[0, h, i0:i0 + 3])
+    sel = orc.select_sample(S, ko_all, N, E, m, seed=0, mode=isg.MODES[mode], votes=votes)
     for key in ("exact_groups", "n_exact", "n_sample", "sample_idx"):
         assert np.array_equal(sel[key], npy(r["sel"][key])), key
     # sampled heads: assignment of a token sample (near-tie rule) and attention on a few groups
@@ -399,3 +417,94 @@ def test_full_size_480p(orc):
 
 def test_full_size_14b_720p(orc):
     _full_size_check(orc, "wan14b_720p", 0.08, 0.08, heads=[0, 20, 39], groups_per_head=3)
+
+
+# ------------------------------------------------------------------ product-quantised votes
+def _pq_stage(orc, qc, qcb, kc, kcb, cq, ck, E, scale):
+    """Oracle Kbar, tables and votes from the GPU's codes (stage by stage), and the GPU's."""
+    g = isg.isg_pq_votes(qc, qcb, kc, kcb, cq["perm"], cq["offsets"], ck["perm"], ck["offsets"], E, scale)
+    torch.cuda.synchronize()
+    kbar = orc.pq_kbar(npy(kc), npy(kcb), npy(ck["perm"]), npy(ck["offsets"]))
+    tables = orc.pq_tables(npy(qcb), kbar, scale)
+    votes = orc.pq_votes(npy(qc), tables, npy(cq["perm"]), npy(cq["offsets"]), npy(ck["offsets"]), E)
+    return g, kbar, tables, votes
+
+
+@pytest.mark.parametrize("H,N,d,P,Cc,Cq,Ck,E", [
+    (2, 2000, 128, 8, 64, 10, 50, 200),     # one key group per lane
+    (2, 3000, 128, 8, 128, 12, 100, 300),   # two per lane
+    (1, 3000, 128, 8, 64, 8, 200, 0),       # exact_keys 0: only the top group
+    (1, 4096, 128, 8, 256, 16, 500, 400),   # the 500-group shape
+    (1, 5000, 64, 4, 32, 8, 1000, 500),     # sixteen per lane
+    (1, 2048, 128, 8, 64, 8, 64, 4096),     # every group fits
+])
+def test_pq_votes_stagewise(orc, H, N, d, P, Cc, Cq, Ck, E):
+    """Kbar, tables and votes bit-exact against the oracle given the same codes."""
+    say(f"pq votes H={H} N={N} d={d} P={P} Cc={Cc} Cq={Cq} Ck={Ck} E={E}")
+    (q, k, v), cq, ck = _clustered(H, N, d, "bf16", Cq, Ck, seed=P + Ck)
+    qc, qcb = isg.pq_codebooks(q.to(DEV), P, Cc, 3)
+    kc, kcb = isg.pq_codebooks(k.to(DEV), P, Cc, 3)
+    scale = isg.default_scale(d)
+    g, kbar, tables, votes = _pq_stage(orc, qc, qcb, kc, kcb, cq, ck, E, scale)
+    assert np.array_equal(npy(g["kbar"]), kbar)
+    assert np.array_equal(npy(g["tables"]), tables)
+    assert np.array_equal(npy(g["votes"]), votes)
+    assert (votes.sum(-1) >= np.diff(npy(cq["offsets"]), axis=-1)).all()
+
+
+def test_pq_votes_all_scores_tied(orc):
+    """Every key has the same codes, so every group mean (and score) is equal: the
+    ranking is by group id alone, and the exact-set rule stops part-way."""
+    H, N, d, P, Cc, Cq, Ck = 1, 3000, 128, 8, 32, 8, 100
+    (q, k, v), cq, ck = _clustered(H, N, d, "bf16", Cq, Ck, seed=5)
+    qc, qcb = isg.pq_codebooks(q.to(DEV), P, Cc, 2)
+    kc = torch.zeros_like(qc)
+    kcb = qcb.clone()
+    scale = isg.default_scale(d)
+    for E in (0, 7, 250, 1234):
+        g, _, _, votes = _pq_stage(orc, qc, qcb, kc, kcb, cq, ck, E, scale)
+        assert np.array_equal(npy(g["votes"]), votes), E
+
+
+def test_pq_codebooks_strided_and_vs_oracle(orc):
+    """Subspace codes through strided views equal isg_cluster on contiguous copies;
+    agreement with the oracle's own k-means of each subspace is reported."""
+    H, N, d, P, Cc = 2, 3000, 128, 8, 64
+    q, k, v = _inputs(H, N, d, "bf16", seed=21)
+    qg = q.to(DEV)
+    codes, cbs = isg.pq_codebooks(qg, P, Cc, 3)
+    ds = d // P
+    for s in (0, 5):
+        r = isg.isg_cluster(qg[..., s * ds:(s + 1) * ds].contiguous(), Cc, 3)
+        assert torch.equal(r["labels"], codes[s]) and torch.equal(r["centroids"], cbs[s])
+    oc, ocb = orc.pq_codebooks(f32(q), P, Cc, 3)
+    agree = (oc == npy(codes)).mean()
+    say(f"  PQ code agreement with the oracle's own k-means: {agree:.5f}")
+    assert agree > 0.97
+
+
+def test_pipeline_votes_mode_vs_oracle(orc):
+    """Votes mode end to end: the oracle re-runs PQ votes, selection (mode 2) and
+    attention from the GPU's clustering and codes."""
+    H, N, d, Cq, Ck, E, m, P, Cc = 2, 4096, 128, 16, 64, 400, 400, 8, 64
+    q, k, v = _inputs(H, N, d, "bf16", seed=8, q_scale=0.5, zipf=1.2)
+    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), Cq, Ck, 3, E, m, mode="votes", pq=(P, Cc), seed=4)
+    torch.cuda.synchronize()
+    pq = r["pq"]
+    kbar = orc.pq_kbar(npy(pq["k_codes"]), npy(pq["k_codebooks"]), npy(r["ck"]["perm"]), npy(r["ck"]["offsets"]))
+    tables = orc.pq_tables(npy(pq["q_codebooks"]), kbar, r["scale"])
+    votes = orc.pq_votes(npy(pq["q_codes"]), tables, npy(r["cq"]["perm"]), npy(r["cq"]["offsets"]),
+                         npy(r["ck"]["offsets"]), E)
+    assert np.array_equal(votes, npy(pq["votes"]))
+    sel = orc.select_sample(npy(r["scores"]), npy(r["ck"]["offsets"]), N, E, m, mode=2, votes=votes, seed=4)
+    for key in ("exact_groups", "n_exact", "n_sample", "sample_idx"):
+        assert np.array_equal(sel[key], npy(r["sel"][key])), key
+    o_p, lse_p = orc.attention(f32(r["cq"]["x_perm"]), f32(r["ck"]["x_perm"]), f32(r["ck"]["companion_perm"]),
+                               npy(r["cq"]["offsets"]), npy(r["ck"]["offsets"]), sel, m, r["scale"])
+    o, lse = orc.unpermute(o_p, lse_p, npy(r["cq"]["perm"]))
+    assert np.abs(f32(r["o"]) - o).max() <= 2e-2
+    assert np.abs(npy(r["lse"]) - lse).max() <= LSE_TOL_BF16
+
+
+def test_full_size_14b_720p_pq_votes(orc):
+    _full_size_check(orc, "wan14b_720p_stress_pq", 0.08, 0.08, heads=[0, 39], groups_per_head=3, mode="votes")

@@ -488,3 +488,107 @@ def test_error_falls_with_sample_size(orc):
             e.append(np.linalg.norm(o[0, 0] - o_ref) / np.linalg.norm(o_ref))
         errs.append(np.mean(e))
     assert errs[0] > errs[1] > errs[2]
+
+
+# ---------------------------------------------------------------- product-quantised voting
+def _pq_case(orc, exact_pq=False, same_query=False, seed=0):
+    """Tiny head: Cq query groups, Ck key groups, P subspaces of ds dims."""
+    rng = np.random.default_rng(seed)
+    H, N, P, ds, Cc, Cq, Ck = 1, 240, 4, 4, 16, 4, 12
+    d = P * ds
+    if exact_pq:
+        # every sub-vector is one of Cc distinct codewords, so 16-means recovers them
+        words = rng.standard_normal((P, Cc, ds)) * 3
+        qi = rng.integers(0, Cc, (N, P))
+        ki = rng.integers(0, Cc, (N, P))
+        q = np.concatenate([words[s][qi[:, s]] for s in range(P)], 1)
+        k = np.concatenate([words[s][ki[:, s]] for s in range(P)], 1)
+    else:
+        q = rng.standard_normal((N, d))
+        k = rng.standard_normal((N, d))
+    q = q.astype(np.float32)[None, None]
+    k = k.astype(np.float32)[None, None]
+    cq = orc.cluster(q, Cq, 5)
+    if same_query:
+        # every query of a group equals its group's centroid (then re-quantised exactly)
+        q = cq["centroids"][0, 0][cq["labels"][0, 0]][None, None].astype(np.float32)
+    ck = orc.cluster(k, Ck, 5)
+    return q, k, cq, ck, P, Cc
+
+
+def test_pq_exact_quantisation_reproduces_centroid_ranking(orc):
+    """When every query of a group equals the group's centroid and the quantisation
+    is exact, each query's per-group scores are the centroid scores, so every query of
+    group i votes for exactly the exact set that the centroid ranking selects."""
+    rng = np.random.default_rng(3)
+    H, N, P, ds, Cq, Ck = 1, 240, 4, 4, 4, 12
+    d = P * ds
+    k = (rng.standard_normal((N, d)) * 2).astype(np.float32)[None, None]
+    ck = orc.cluster(k, Ck, 5)
+    # queries: Cq distinct vectors, each repeated; quantisation of both is exact when the
+    # number of distinct sub-vectors is <= Cc
+    qv = (rng.standard_normal((Cq, d)) * 2).astype(np.float32)
+    lab = np.repeat(np.arange(Cq), N // Cq)
+    q = qv[lab][None, None]
+    cq = orc.cluster(q, Cq, 5)
+    Cc = 256
+    # keys: at most N distinct sub-vectors per subspace (<= Cc) -> exact codebooks
+    qc, qcb = orc.pq_codebooks(q, P, Cc, 5)
+    kc, kcb = orc.pq_codebooks(k, P, Cc, 5)
+    for s in range(P):
+        assert np.array_equal(qcb[s, 0, 0][qc[s, 0, 0]], q[0, 0][:, s * ds:(s + 1) * ds])
+        assert np.array_equal(kcb[s, 0, 0][kc[s, 0, 0]], k[0, 0][:, s * ds:(s + 1) * ds])
+    scale = 0.25
+    kbar = orc.pq_kbar(kc, kcb, ck["perm"], ck["offsets"])
+    cent = ck["centroids"][0, 0]
+    assert np.allclose(kbar[0, 0], cent, atol=1e-5)
+    tables = orc.pq_tables(qcb, kbar, scale)
+    E = 60
+    votes = orc.pq_votes(qc, tables, cq["perm"], cq["offsets"], ck["offsets"], E)
+    S, _ = orc.probs(cq["centroids"], ck["centroids"], ck["offsets"], scale)
+    sel = orc.select_sample(S, ck["offsets"], N, E, 0)
+    n_q = np.diff(cq["offsets"][0, 0])
+    for i in range(Cq):
+        ex = set(sel["exact_groups"][0, 0, i, :sel["n_exact"][0, 0, i]].tolist())
+        got = {j for j in range(Ck) if votes[0, 0, i, j] > 0}
+        assert got == ex
+        assert all(votes[0, 0, i, j] == n_q[i] for j in got)
+    # votes mode then reproduces the exact set
+    selv = orc.select_sample(S, ck["offsets"], N, E, 0, mode=2, votes=votes)
+    assert np.array_equal(selv["exact_groups"], sel["exact_groups"])
+
+
+def test_pq_votes_brute_force(orc):
+    """Votes against a direct numpy evaluation of the same reading on a tiny head."""
+    q, k, cq, ck, P, Cc = _pq_case(orc, seed=4)
+    qc, qcb = orc.pq_codebooks(q, P, Cc, 5)
+    kc, kcb = orc.pq_codebooks(k, P, Cc, 5)
+    scale = 0.5
+    kbar = orc.pq_kbar(kc, kcb, ck["perm"], ck["offsets"])
+    tables = orc.pq_tables(qcb, kbar, scale)
+    E = 50
+    votes = orc.pq_votes(qc, tables, cq["perm"], cq["offsets"], ck["offsets"], E)
+    ds = q.shape[-1] // P
+    ko = ck["offsets"][0, 0]
+    n_k = np.diff(ko)
+    # direct: per-key reconstruction, group means, per-query scores from reconstructed q
+    krec = np.concatenate([kcb[s, 0, 0][kc[s, 0, 0]] for s in range(P)], 1).astype(np.float64)
+    qrec = np.concatenate([qcb[s, 0, 0][qc[s, 0, 0]] for s in range(P)], 1).astype(np.float64)
+    kperm = krec[ck["perm"][0, 0]]
+    gmean = np.stack([kperm[ko[j]:ko[j + 1]].mean(0) if n_k[j] else np.zeros(q.shape[-1]) for j in range(len(n_k))])
+    want = np.zeros_like(votes[0, 0])
+    qo = cq["offsets"][0, 0]
+    for i in range(len(qo) - 1):
+        for r in range(qo[i], qo[i + 1]):
+            t = cq["perm"][0, 0, r]
+            sc = scale * gmean @ qrec[t]
+            order = sorted([j for j in range(len(n_k)) if n_k[j]], key=lambda j: (-sc[j], j))
+            cum = 0
+            for p_, j in enumerate(order):
+                if p_ > 0 and cum + n_k[j] > E:
+                    break
+                cum += n_k[j]
+                want[i, j] += 1
+    # float rounding of the table path can reorder near-equal scores: demand near-total agreement
+    assert (votes[0, 0] == want).mean() > 0.97
+    assert np.all(votes[0, 0].sum(1) >= np.diff(qo))
