@@ -152,13 +152,6 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t *q_offset
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-// Position of key k (0..63) inside a transposed V row: bits 2 and 3 swapped, so
-// that the 8 keys one lane feeds to the P.V product are contiguous.
-__device__ __forceinline__ int vt_pos(int k)
-{
-    return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
-
 // K tile in LDS: 64 unpadded rows, the 16-byte chunks of row r XOR-swizzled by
 // r mod (chunks per row) so that 8 lanes reading one chunk of 8 rows hit 8
 // distinct bank groups.
@@ -188,45 +181,48 @@ __device__ __forceinline__ void k_direct(uint8_t *kbuf, const uint16_t *kh, cons
     }
 }
 
-// V rows are staged through registers (a thread holds 16 bytes of 4 consecutive
-// keys) and written transposed: one LDS row per d, keys at vt_pos positions.
-struct VRegs {
-    u32x4 v[4];
-};
-
+// V tile in LDS: row-major (key rows of D elements), loaded straight from memory
+// like K; the 16-byte chunks of row r are XOR-swizzled by 2 (r mod 4).  The P.V
+// product reads it with the LDS transpose read (ds_read_b64_tr_b16): inside each
+// group of 16 lanes, lane j supplies the address of 4 elements of key row
+// k0 + j/4 at column d0 + 4 (j mod 4), and lane i receives column d0 + i of the
+// four rows k0 .. k0+3.  Four consecutive rows at one chunk pair then cover 8
+// distinct 16-byte bank slots.
 template <int D>
-__device__ __forceinline__ void v_gload(VRegs &r, const uint16_t *vh, const int *rows, int tid)
+__device__ __forceinline__ int vswz(int row, int chunk)
 {
-    constexpr int VTASK = 16 * (D / 8);
-    if (tid < VTASK) {
-        const int quad = tid & 15, chunk = tid >> 4;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            r.v[kk] = *reinterpret_cast<const u32x4 *>(vh + (uint32_t)rows[quad * 4 + kk] * (uint32_t)D +
-                                                       (uint32_t)(chunk * 8));
-    }
+    constexpr int CPR = D / 8;
+    return row * CPR + (chunk ^ (2 * (row & 3)));
 }
 
 template <int D>
-__device__ __forceinline__ void v_sstore(const VRegs &r, uint8_t *vb, int tid)
+__device__ __forceinline__ void v_direct(uint8_t *vbuf, const uint16_t *vh, const int *rows, int wave, int lane)
 {
-    constexpr int VTASK = 16 * (D / 8);
-    constexpr int VSTR = kTK * 2 + 16;
-    if (tid < VTASK) {
-        const int quad = tid & 15, chunk = tid >> 4;
-        const int pos = vt_pos(quad * 4);
+    constexpr int CPR = D / 8;
+    constexpr int ROUNDS = kTK * CPR / 256;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            // bf16 pairs (d, d+1) of the four keys -> rows d and d+1, four keys each
-            const uint32_t a = r.v[0][w], b = r.v[1][w], c = r.v[2][w], d = r.v[3][w];
-            const uint32_t lo_e = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (a.lo, b.lo)
-            const uint32_t hi_e = __builtin_amdgcn_perm(d, c, 0x05040100u);
-            const uint32_t lo_o = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (a.hi, b.hi)
-            const uint32_t hi_o = __builtin_amdgcn_perm(d, c, 0x07060302u);
-            *reinterpret_cast<u32x2 *>(vb + (chunk * 8 + 2 * w) * VSTR + pos * 2) = u32x2{lo_e, hi_e};
-            *reinterpret_cast<u32x2 *>(vb + (chunk * 8 + 2 * w + 1) * VSTR + pos * 2) = u32x2{lo_o, hi_o};
-        }
+    for (int it = 0; it < ROUNDS; ++it) {
+        const int blk = it * 4 + wave;
+        const int P = blk * 64 + lane;
+        const int row = P / CPR, c = (P % CPR) ^ (2 * (row & 3));
+        const uint16_t *src = vh + (uint32_t)rows[row] * (uint32_t)D + (uint32_t)(c * 8);
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                         (void __attribute__((address_space(3))) *)(vbuf + blk * 1024), 16, 0, 0);
     }
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+// Byte offset, inside a V tile, of the 8 bytes this lane supplies to the transpose
+// read of d-block db (32 columns) for key rows 4 hl + (j/4) (+16 s, +8 later).
+template <int D>
+__device__ __forceinline__ int v_tr_offset(int db, int lane)
+{
+    const int j = lane & 15, x = (lane >> 4) & 1, hl = lane >> 5;
+    const int row = 4 * hl + (j >> 2);
+    const int dcol = db * 32 + 16 * x + 4 * (j & 3);
+    return vswz<D>(row, dcol >> 3) * 16 + ((dcol >> 2) & 1) * 8;
 }
 
 // One tile step of the attention loop: multiply the 64 columns of tile t held in
@@ -238,14 +234,17 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
                                           uint8_t *knext, uint8_t *vnext, const uint16_t *kh, const uint16_t *vh,
                                           const int32_t *crow, const float *cbias, int (*idx_row)[kTK],
                                           float (*idx_bias)[kTK], const bf16x8 *qf, f32x16 *oacc, float &l_run,
-                                          float &m_run, VRegs &vr, float scale_log2, bool wave_active, int tid,
+                                          float &m_run, const int *vtr, float scale_log2, bool wave_active,
                                           int wave, int lane, int hl, int l32)
 {
     constexpr int NDS = D / 16;
     constexpr int NDB = D / 32;
-    constexpr int VSTR = kTK * 2 + 16;
+    constexpr int RSTR = D * 2;  // bytes per V row
     const bool more = t + 1 < T;
-    if (more) k_direct<D>(knext, kh, idx_row[(t + 1) % 3], wave, lane);
+    if (more) {
+        k_direct<D>(knext, kh, idx_row[(t + 1) % 3], wave, lane);
+        v_direct<D>(vnext, vh, idx_row[(t + 1) % 3], wave, lane);
+    }
     int32_t nrow = 0;
     float nbias = 0.0f;
     const bool fetch2 = wave == 0 && t + 2 < T;
@@ -270,8 +269,6 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
         }
         __builtin_amdgcn_s_setprio(0);
     }
-    // the next tile's V rows: fetched here so their registers live only through P.V
-    if (more) v_gload<D>(vr, vh, idx_row[(t + 1) % 3], tid);
     if (wave_active) {
         // Logits in log2 units; lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of
         // its query.  Exact tiles keep raw scores (cf = scale log2 e); tiles with
@@ -329,18 +326,21 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
             }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(vcur + (db * 32 + l32) * VSTR + (s * 16 + hl * 8) * 2);
+                // keys 16 s + 4 hl + 0..3 and 16 s + 8 + 4 hl + 0..3 of column db*32 + l32
+                const uint8_t *vp = vcur + vtr[db] + s * 16 * RSTR;
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)vp);
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp + 8 * RSTR));
+                const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
             }
         }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (more) v_sstore<D>(vr, vnext, tid);
     if (fetch2) {
         idx_row[(t + 2) % 3][lane] = nrow;
         idx_bias[(t + 2) % 3][lane] = nbias;
     }
-    __builtin_amdgcn_s_waitcnt(0);  // direct K loads of the next tile have landed
+    __builtin_amdgcn_s_waitcnt(0);  // direct K and V loads of the next tile have landed
     __syncthreads();
 }
 
@@ -366,11 +366,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NDS = D / 16;          // 16-wide d steps of S^T = K Q^T
     constexpr int NDB = D / 32;          // 32-row d blocks of O^T
     constexpr int KBYTES = kTK * D * 2;
-    constexpr int VBYTES = D * (kTK * 2 + 16);  // transposed V, rows padded to 144 bytes
+    constexpr int VBYTES = kTK * D * 2;
     __shared__ __attribute__((aligned(1024))) uint8_t kb0[KBYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t kb1[KBYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t vb0[VBYTES];
-    __shared__ __attribute__((aligned(16))) uint8_t vb1[VBYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb0[VBYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb1[VBYTES];
     __shared__ int idx_row[3][kTK];
     __shared__ __attribute__((aligned(16))) float idx_bias[3][kTK];
 
@@ -423,11 +423,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
     __syncthreads();
-    VRegs vr;
     k_direct<D>(kb0, kh, idx_row[0], wave, lane);
-    v_gload<D>(vr, vh, idx_row[0], tid);
-    v_sstore<D>(vr, vb0, tid);
-    __builtin_amdgcn_s_waitcnt(0);  // direct K loads have landed in LDS
+    v_direct<D>(vb0, vh, idx_row[0], wave, lane);
+    int vtr[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vtr[db] = v_tr_offset<D>(db, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // direct K and V loads have landed in LDS
     __syncthreads();
 
     f32x16 oacc[NDB];
@@ -439,10 +440,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     for (int t = 0; t < T; t += 2) {
         tile_step<D, FIXED>(t, T, X, kb0, vb0, kb1, vb1, kh, vh, crow, cbias, idx_row, idx_bias, qf, oacc, l_run,
-                            m_run, vr, scale_log2, wave_active, tid, wave, lane, hl, l32);
+                            m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
         if (t + 1 < T)
             tile_step<D, FIXED>(t + 1, T, X, kb1, vb1, kb0, vb0, kh, vh, crow, cbias, idx_row, idx_bias, qf, oacc,
-                                l_run, m_run, vr, scale_log2, wave_active, tid, wave, lane, hl, l32);
+                                l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
     }
 
     if (!wave_active) return;
