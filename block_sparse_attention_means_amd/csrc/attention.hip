@@ -15,10 +15,10 @@
 //                       query tile; the launch walks tiles in an XCD-aware order
 //                       so the tiles of one group share an L2.
 //   3. attn_bf16_kernel 4 waves x 32 query rows; K/V tiles of 64 columns are
-//                       gathered row by row into LDS (double buffered, one tile
-//                       prefetched in registers); S^T = K Q^T and O^T += V^T P^T
-//                       on v_mfma_f32_32x32x16_bf16 so each lane owns one query
-//                       and the online softmax stays in registers.
+//                       gathered row by row straight into LDS (double buffered);
+//                       S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16
+//                       so each lane owns one query and the softmax weights stay
+//                       in registers; V is read through the LDS transpose read.
 //      attn_f32_kernel  fp32 inputs: plain VALU version of the same loop.
 #include <cmath>
 
@@ -31,6 +31,12 @@ constexpr int kTQ = 128;         // query rows per bf16 work-group
 constexpr int kTQ32 = 64;        // query rows per fp32 work-group
 constexpr int kMaxGroups = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
+// 32-row query blocks per wave in the fast bf16 kernel.  Two blocks per wave
+// halve the LDS fragment traffic per product but leave one wave per SIMD, whose
+// single instruction stream serialises LDS latency, exponentials and products;
+// measured slower on gfx950 than two single-block waves per SIMD.
+constexpr int kQB = 1;
+
 
 // ------------------------------------------------------------------ prep
 __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, const int32_t *exact_groups,
@@ -162,32 +168,12 @@ __device__ __forceinline__ int kswz(int row, int chunk)
     return row * CPR + (chunk ^ (row & (CPR - 1)));
 }
 
-// K rows go straight from memory into LDS (global_load_lds_dwordx4: lane l of a
-// wave writes 16 bytes at M0 + 16 l); each lane fetches the chunk that belongs at
-// its swizzled position.
-template <int D>
-__device__ __forceinline__ void k_direct(uint8_t *kbuf, const uint16_t *kh, const int *rows, int wave, int lane)
-{
-    constexpr int CPR = D / 8;
-    constexpr int ROUNDS = kTK * CPR / 256;
-#pragma unroll
-    for (int it = 0; it < ROUNDS; ++it) {
-        const int blk = it * 4 + wave;  // 64-chunk (1 KB) block of the tile
-        const int P = blk * 64 + lane;
-        const int row = P / CPR, c = (P % CPR) ^ (row & (CPR - 1));
-        const uint16_t *src = kh + (uint32_t)rows[row] * (uint32_t)D + (uint32_t)(c * 8);
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
-                                         (void __attribute__((address_space(3))) *)(kbuf + blk * 1024), 16, 0, 0);
-    }
-}
-
-// V tile in LDS: row-major (key rows of D elements), loaded straight from memory
-// like K; the 16-byte chunks of row r are XOR-swizzled by 2 (r mod 4).  The P.V
-// product reads it with the LDS transpose read (ds_read_b64_tr_b16): inside each
-// group of 16 lanes, lane j supplies the address of 4 elements of key row
-// k0 + j/4 at column d0 + 4 (j mod 4), and lane i receives column d0 + i of the
-// four rows k0 .. k0+3.  Four consecutive rows at one chunk pair then cover 8
-// distinct 16-byte bank slots.
+// V tile in LDS: row-major (key rows of D elements); the 16-byte chunks of row r
+// are XOR-swizzled by 2 (r mod 4).  The P.V product reads it with the LDS
+// transpose read (ds_read_b64_tr_b16): inside each group of 16 lanes, lane j
+// supplies the address of 4 elements of key row k0 + j/4 at column d0 + 4 (j mod 4),
+// and lane i receives column d0 + i of the four rows k0 .. k0+3.  Four consecutive
+// rows at one chunk pair then cover 8 distinct 16-byte bank slots.
 template <int D>
 __device__ __forceinline__ int vswz(int row, int chunk)
 {
@@ -195,19 +181,24 @@ __device__ __forceinline__ int vswz(int row, int chunk)
     return row * CPR + (chunk ^ (2 * (row & 3)));
 }
 
-template <int D>
-__device__ __forceinline__ void v_direct(uint8_t *vbuf, const uint16_t *vh, const int *rows, int wave, int lane)
+// Tile rows go straight from memory into LDS (global_load_lds_dwordx4: lane l of a
+// wave writes 16 bytes at M0 + 16 l); each lane fetches the chunk that belongs at
+// its swizzled position.  `base` is the head's first row and rows[] holds row
+// indices.
+template <int D, int NW, bool ISV>
+__device__ __forceinline__ void tile_direct(uint8_t *buf, const uint8_t *base, const int *rows, int wave, int lane)
 {
     constexpr int CPR = D / 8;
-    constexpr int ROUNDS = kTK * CPR / 256;
+    constexpr int ROUNDS = kTK * CPR / (64 * NW);
 #pragma unroll
     for (int it = 0; it < ROUNDS; ++it) {
-        const int blk = it * 4 + wave;
+        const int blk = it * NW + wave;  // 64-chunk (1 KB) block of the tile
         const int P = blk * 64 + lane;
-        const int row = P / CPR, c = (P % CPR) ^ (2 * (row & 3));
-        const uint16_t *src = vh + (uint32_t)rows[row] * (uint32_t)D + (uint32_t)(c * 8);
+        const int row = P / CPR;
+        const int c = ISV ? (P % CPR) ^ (2 * (row & 3)) : (P % CPR) ^ (row & (CPR - 1));
+        const uint16_t *src = reinterpret_cast<const uint16_t *>(base) + (uint32_t)rows[row] * (uint32_t)D + (uint32_t)(c * 8);
         __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
-                                         (void __attribute__((address_space(3))) *)(vbuf + blk * 1024), 16, 0, 0);
+                                         (void __attribute__((address_space(3))) *)(buf + blk * 1024), 16, 0, 0);
     }
 }
 
@@ -225,25 +216,28 @@ __device__ __forceinline__ int v_tr_offset(int db, int lane)
     return vswz<D>(row, dcol >> 3) * 16 + ((dcol >> 2) & 1) * 8;
 }
 
-// One tile step of the attention loop: multiply the 64 columns of tile t held in
-// (kcur, vcur) while tile t+1 is being fetched into (knext, vnext).  The four
-// buffers are distinct LDS objects, so the compiler can see that reading the
-// current tile does not depend on the direct loads filling the next one.
-template <int D, bool FIXED>
+// One tile step of the attention loop for a wave holding QB blocks of 32 query
+// rows: multiply the 64 columns of tile t held in (kcur, vcur) while tile t+1 is
+// being fetched into (knext, vnext).  The four buffers are distinct LDS objects,
+// so the compiler can see that reading the current tile does not depend on the
+// direct loads filling the next one.  Each K or V fragment read from LDS feeds
+// QB matrix products.
+template <int D, bool FIXED, int QB>
 __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kcur, const uint8_t *vcur,
-                                          uint8_t *knext, uint8_t *vnext, const uint16_t *kh, const uint16_t *vh,
-                                          const int32_t *crow, const float *cbias, int (*idx_row)[kTK],
-                                          float (*idx_bias)[kTK], const bf16x8 *qf, f32x16 *oacc, float &l_run,
-                                          float &m_run, const int *vtr, float scale_log2, bool wave_active,
-                                          int wave, int lane, int hl, int l32)
+                                          uint8_t *knext, uint8_t *vnext, const uint8_t *kbase,
+                                          const uint8_t *vbase, const int32_t *crow, const float *cbias,
+                                          int (*idx_row)[kTK], float (*idx_bias)[kTK], const bf16x8 (*qf)[D / 16],
+                                          f32x16 (*oacc)[D / 32], float *l_run, float *m_run, const int *vtr,
+                                          float scale_log2, bool wave_active, int wave, int lane, int hl, int l32)
 {
+    constexpr int NW = 4 / QB;
     constexpr int NDS = D / 16;
     constexpr int NDB = D / 32;
     constexpr int RSTR = D * 2;  // bytes per V row
     const bool more = t + 1 < T;
     if (more) {
-        k_direct<D>(knext, kh, idx_row[(t + 1) % 3], wave, lane);
-        v_direct<D>(vnext, vh, idx_row[(t + 1) % 3], wave, lane);
+        tile_direct<D, NW, false>(knext, kbase, idx_row[(t + 1) % 3], wave, lane);
+        tile_direct<D, NW, true>(vnext, vbase, idx_row[(t + 1) % 3], wave, lane);
     }
     int32_t nrow = 0;
     float nbias = 0.0f;
@@ -252,24 +246,27 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
         nrow = crow[(int64_t)(t + 2) * kTK + lane];
         nbias = cbias[(int64_t)(t + 2) * kTK + lane];
     }
-    f32x16 sacc[2];
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[k2][r] = 0.0f;
     if (wave_active) {
+        f32x16 sacc[QB][2];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sacc[qb][k2][r] = 0.0f;
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
             const int c = s * 2 + hl;
             const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(kcur + kswz<D>(l32, c) * 16);
             const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(kcur + kswz<D>(32 + l32, c) * 16);
-            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[s], sacc[0], 0, 0, 0);
-            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[s], sacc[1], 0, 0, 0);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                sacc[qb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[qb][s], sacc[qb][0], 0, 0, 0);
+                sacc[qb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[qb][s], sacc[qb][1], 0, 0, 0);
+            }
         }
         __builtin_amdgcn_s_setprio(0);
-    }
-    if (wave_active) {
         // Logits in log2 units; lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of
         // its query.  Exact tiles keep raw scores (cf = scale log2 e); tiles with
         // sampled or padded columns get scale and offset folded in (cf = 1).
@@ -283,46 +280,57 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
                 for (int g = 0; g < 4; ++g) {
                     const f32x4 bv = *reinterpret_cast<const f32x4 *>(&idx_bias[slot][k2 * 32 + g * 8 + hl * 4]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sacc[k2][4 * g + e] = fmaf(sacc[k2][4 * g + e], scale_log2, bv[e]);
+                    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sacc[qb][k2][4 * g + e] = fmaf(sacc[qb][k2][4 * g + e], scale_log2, bv[e]);
                 }
         }
         if (!FIXED) {
-            float mr = sacc[0][0];
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
+            for (int qb = 0; qb < QB; ++qb) {
+                float mr = sacc[qb][0][0];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sacc[k2][r]);
-            float mx = mr * cf;
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            // lazy rescale: O and l stay relative to m_run until some lane's maximum
-            // exceeds it by more than 8 (weights up to 2^8 are safe)
-            if (__any(mx > m_run + 8.0f)) {
-                const float m_new = fmaxf(m_run, mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-                l_run *= alpha;
+                for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db)
+                    for (int r = 0; r < 16; ++r) mr = fmaxf(mr, sacc[qb][k2][r]);
+                float mx = mr * cf;
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                // lazy rescale: O and l stay relative to m_run until some lane's
+                // maximum exceeds it by more than 8 (weights up to 2^8 are safe)
+                if (__any(mx > m_run[qb] + 8.0f)) {
+                    const float m_new = fmaxf(m_run[qb], mx);
+                    const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+                    l_run[qb] *= alpha;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-                m_run = m_new;
+                    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
+                    m_run[qb] = m_new;
+                }
             }
         }
-        const float mneg = -m_run;
-        // raised wave priority while this wave issues MFMAs lets the SIMD's other
-        // wave fill the VALU slots (and vice versa)
-        __builtin_amdgcn_s_setprio(1);
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        // raised wave priority while this wave issues MFMAs lets another wave on
+        // the SIMD fill the VALU slots; s_setprio also bounds the scheduling
+        // region, so it brackets the whole loop (the exponentials of chunk s+1
+        // interleave with the products of chunk s)
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            bf16x8 pb;
+            bf16x8 pb[QB];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], cf, mneg));
-            // row sum of the rounded weights, the same ones P.V uses
+            for (int qb = 0; qb < QB; ++qb) {
+                const float mneg = -m_run[qb];
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const bf16x2 pp = {pb[e], pb[e + 1]};
-                l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+                for (int e = 0; e < 8; ++e)
+                    pb[qb][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[qb][s >> 1][8 * (s & 1) + e], cf, mneg));
+                // row sum of the rounded weights, the same ones P.V uses
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const bf16x2 pp = {pb[qb][e], pb[qb][e + 1]};
+                    l_run[qb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run[qb], false);
+                }
             }
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
@@ -331,11 +339,13 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)vp);
                 const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp + 8 * RSTR));
                 const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[db], 0, 0, 0);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[qb], oacc[qb][db], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     }
-    __builtin_amdgcn_s_setprio(0);
     if (fetch2) {
         idx_row[(t + 2) % 3][lane] = nrow;
         idx_bias[(t + 2) % 3][lane] = nbias;
@@ -344,9 +354,12 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
     __syncthreads();
 }
 
-// One work-group = 4 waves x 32 query rows of one query group; two work-groups
-// per CU.  S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, so each
-// lane owns one query: its weights stay in registers and feed P.V directly.
+// One work-group = 128 query rows of one query group: 4/QB waves, each holding
+// QB blocks of 32 rows.  S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_32x32x16_bf16, so each lane owns one query per block: its weights
+// stay in registers and feed P.V directly.  QB = 2 halves the LDS fragment
+// traffic per product (one wave per SIMD, up to 512 registers); QB = 1 runs two
+// waves per SIMD.
 //
 // FIXED = true (the fast kernel): every row uses the fixed reference
 //   m_ref = scale log2(e) |q| max|k| + max(offsets, 0) >= every logit of the row
@@ -355,8 +368,8 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
 // the bound), weights may have underflowed: the tile is flagged in `redo`.
 // FIXED = false (the fallback): running maximum with rescaling; it processes
 // only the flagged tiles.
-template <int D, bool FIXED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
+template <int D, bool FIXED, int QB>
+__global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB, 3 - QB))) void attn_bf16_kernel(
     const uint16_t *__restrict__ q_p, const uint16_t *__restrict__ k_p, const uint16_t *__restrict__ v_p,
     int N, int Cq, const int4 *__restrict__ table, int nblocks, const int32_t *__restrict__ col_row,
     const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
@@ -367,6 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int NDB = D / 32;          // 32-row d blocks of O^T
     constexpr int KBYTES = kTK * D * 2;
     constexpr int VBYTES = kTK * D * 2;
+    constexpr int WROWS = 32 * QB;       // query rows per wave
     __shared__ __attribute__((aligned(1024))) uint8_t kb0[KBYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t kb1[KBYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t vb0[VBYTES];
@@ -386,31 +400,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int32_t *crow = col_row + gi * cap;
     const float *cbias = col_bias + gi * cap;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-    const uint16_t *kh = k_p + (int64_t)bh * N * D;
-    const uint16_t *vh = v_p + (int64_t)bh * N * D;
+    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(k_p + (int64_t)bh * N * D);
+    const uint8_t *vbase = reinterpret_cast<const uint8_t *>(v_p + (int64_t)bh * N * D);
 
-    // Q^T fragment (B operand of S^T = K Q^T): lane owns query row l32 of its wave.
-    const int qrow_raw = r0 + wave * 32 + l32;
-    const int qrow = min(qrow_raw, r1 - 1);
-    const bool wave_active = r0 + wave * 32 < r1;
-    bf16x8 qf[NDS];
-    float qss = 0.0f;
-    {
+    // Q^T fragments (B operand of S^T = K Q^T): lane owns query row l32 of each block.
+    const bool wave_active = r0 + wave * WROWS < r1;
+    bf16x8 qf[QB][NDS];
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qrow = min(r0 + wave * WROWS + qb * 32 + l32, r1 - 1);
         const uint16_t *qsrc = q_p + ((int64_t)bh * N + qrow) * D + hl * 8;
+        float qss = 0.0f;
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
-            qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+            qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
             if (FIXED) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[s][e], (float)qf[s][e], qss);
+                for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[qb][s][e], (float)qf[qb][s][e], qss);
             }
         }
-    }
-    float m_run = -INFINITY;
-    if (FIXED) {
-        qss += __shfl_xor(qss, 32);
-        const float kmx = sqrtf(__int_as_float(kmax2[bh]));
-        m_run = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, col_bmax[gi]) + 1e-6f;
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.0f;
+        if (FIXED) {
+            qss += __shfl_xor(qss, 32);
+            const float kmx = sqrtf(__int_as_float(kmax2[bh]));
+            m_run[qb] = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, col_bmax[gi]) + 1e-6f;
+        }
     }
 
     // column list of tiles 0 and 1 into the index ring
@@ -423,50 +439,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
     __syncthreads();
-    k_direct<D>(kb0, kh, idx_row[0], wave, lane);
-    v_direct<D>(vb0, vh, idx_row[0], wave, lane);
+    constexpr int NW = 4 / QB;
+    tile_direct<D, NW, false>(kb0, kbase, idx_row[0], wave, lane);
+    tile_direct<D, NW, true>(vb0, vbase, idx_row[0], wave, lane);
     int vtr[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vtr[db] = v_tr_offset<D>(db, lane);
     __builtin_amdgcn_s_waitcnt(0);  // direct K and V loads have landed in LDS
     __syncthreads();
 
-    f32x16 oacc[NDB];
+    f32x16 oacc[QB][NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    float l_run = 0.0f;
-
-    for (int t = 0; t < T; t += 2) {
-        tile_step<D, FIXED>(t, T, X, kb0, vb0, kb1, vb1, kh, vh, crow, cbias, idx_row, idx_bias, qf, oacc, l_run,
-                            m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
-        if (t + 1 < T)
-            tile_step<D, FIXED>(t + 1, T, X, kb1, vb1, kb0, vb0, kh, vh, crow, cbias, idx_row, idx_bias, qf, oacc,
-                                l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
-    }
-
-    if (!wave_active) return;
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
-    if (FIXED && __any(qrow_raw < r1 && !(l_tot >= 8.271806e-25f))) {  // 2^-80
-        if (lane == 0) redo[lb] = 1;
-        return;
-    }
-    const float inv = 1.0f / l_tot;
-    if (qrow_raw < r1) {
-        uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = db * 32 + g * 8 + hl * 4;
-                const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g] * inv) |
-                                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 1] * inv) << 16);
-                const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 2] * inv) |
-                                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 3] * inv) << 16);
-                *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
-            }
-        if (lse_p && hl == 0) lse_p[(int64_t)bh * N + qrow_raw] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+            for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
+
+    for (int t = 0; t < T; t += 2) {
+        tile_step<D, FIXED, QB>(t, T, X, kb0, vb0, kb1, vb1, kbase, vbase, crow, cbias, idx_row, idx_bias, qf,
+                                oacc, l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
+        if (t + 1 < T)
+            tile_step<D, FIXED, QB>(t + 1, T, X, kb1, vb1, kb0, vb0, kbase, vbase, crow, cbias, idx_row, idx_bias,
+                                    qf, oacc, l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
+    }
+
+    if (!wave_active) return;
+    float l_tot[QB];
+    bool low = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
+        const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
+        low = low || (qrow_raw < r1 && !(l_tot[qb] >= 8.271806e-25f));  // 2^-80
+    }
+    if (FIXED && __any(low)) {
+        if (lane == 0) redo[lb] = 1;
+        return;
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
+        if (qrow_raw < r1) {
+            const float inv = 1.0f / l_tot[qb];
+            uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = db * 32 + g * 8 + hl * 4;
+                    const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g] * inv) |
+                                        ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 1] * inv) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 2] * inv) |
+                                        ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 3] * inv) << 16);
+                    *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
+                }
+            if (lse_p && hl == 0)
+                lse_p[(int64_t)bh * N + qrow_raw] = (m_run[qb] + log2f(l_tot[qb])) * 0.6931471805599453f;
+        }
     }
 }
 
@@ -570,6 +600,24 @@ Layout layout(int B, int H, int N, int Cq, int m, int tq)
     return L;
 }
 
+// Fast kernel (fixed per-row reference), then the rescaling kernel on the tiles
+// the fast one flagged (rows whose logits all sit far below the bound).  Both
+// walk the same 128-row tile table; the rare fallback keeps one query block per
+// wave, where its running-maximum state fits the registers.
+template <int D, int QB>
+void launch_bf16(hipStream_t st, const Layout &Lq, const void *q_p, const void *k_p, const void *v_p, int N, int Cq,
+                 const int4 *table, const int32_t *col_row, const float *col_bias, const int32_t *col_len,
+                 const int32_t *col_x, const float *col_bmax, const int *kmax2, float scale_log2, void *o_p,
+                 float *lse_p, int *redo)
+{
+    attn_bf16_kernel<D, true, QB><<<Lq.ntotal, 256 / QB, 0, st>>>(
+        (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
+        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+    attn_bf16_kernel<D, false, 1><<<Lq.ntotal, 256, 0, st>>>(
+        (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
+        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+}
+
 }  // namespace
 
 extern "C" size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck)
@@ -598,6 +646,8 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     ISG_REQUIRE(Cq >= 1 && Cq <= kMaxGroups && Ck >= 1 && Ck <= kMaxGroups, ISG_E_ARG,
                 "isg_attention: Cq, Ck must be in [1, %d]", kMaxGroups);
     ISG_REQUIRE(m >= 0 && m <= N, ISG_E_ARG, "isg_attention: need 0 <= m <= N");
+    ISG_REQUIRE((int64_t)N * d * 4 <= 0x7fffffff, ISG_E_ARG,
+                "isg_attention: N*d too large for 32-bit row offsets (N=%d, d=%d)", N, d);
     ISG_REQUIRE(std::isfinite(scale), ISG_E_ARG, "isg_attention: scale must be finite");
     ISG_REQUIRE(((uintptr_t)q_p & 15) == 0 && ((uintptr_t)k_p & 15) == 0 && ((uintptr_t)v_p & 15) == 0 &&
                     ((uintptr_t)o_p & 15) == 0,
@@ -624,25 +674,15 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table, redo, kmax2);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if (dt == ISG_BF16) {
-        // fast kernel (fixed per-row reference), then the rescaling kernel on the
-        // tiles the fast one flagged (rows whose logits all sit far below the bound)
         const dim3 kgrid((unsigned)((N + 255) / 256), (unsigned)(B * H));
         if (d == 128) {
             kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
-            attn_bf16_kernel<128, true><<<Lq.ntotal, 256, 0, st>>>(
-                (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
-            attn_bf16_kernel<128, false><<<Lq.ntotal, 256, 0, st>>>(
-                (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+            launch_bf16<128, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
+                                  kmax2, scale_log2, o_p, lse_p, redo);
         } else {
             kmax_kernel<64><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
-            attn_bf16_kernel<64, true><<<Lq.ntotal, 256, 0, st>>>(
-                (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
-            attn_bf16_kernel<64, false><<<Lq.ntotal, 256, 0, st>>>(
-                (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal,
-                col_row, col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+            launch_bf16<64, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
+                                 kmax2, scale_log2, o_p, lse_p, redo);
         }
     } else {
         if (d == 128)
