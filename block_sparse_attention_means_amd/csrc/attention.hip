@@ -20,6 +20,7 @@
 //                       so each lane owns one query and the softmax weights stay
 //                       in registers; V is read through the LDS transpose read.
 //      attn_f32_kernel  fp32 inputs: plain VALU version of the same loop.
+#include <algorithm>
 #include <cmath>
 
 #include "isg_internal.h"
@@ -100,35 +101,40 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
     }
 }
 
-// Largest key norm |k| of each head (fp32 of the bf16 rows); kmax must start at 0.
+// Largest squared key norm of each head (fp32 of the bf16 rows), as float bits
+// (non-negative floats order like their bits); kmax must start at 0.  D/8 lanes
+// share a row, each summing one 16-byte chunk, then a butterfly over the row.
 template <int D>
 __global__ __launch_bounds__(256) void kmax_kernel(const uint16_t *k_p, int N, int *kmax)
 {
-    __shared__ int red[256];
-    const int bh = blockIdx.y;
+    constexpr int TPR = D / 8;     // lanes per row
+    constexpr int RPB = 256 / TPR;  // rows per block step
+    __shared__ float red[4];
+    const int bh = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ck = threadIdx.x % TPR;
     float best = 0.0f;
-    for (int r = blockIdx.x * 256 + threadIdx.x; r < N; r += gridDim.x * 256) {
-        const uint16_t *row = k_p + ((int64_t)bh * N + r) * D;
+    for (int r0 = blockIdx.x * RPB; r0 < N; r0 += gridDim.x * RPB) {
+        const int r = r0 + threadIdx.x / TPR;
         float ss = 0.0f;
-#pragma unroll
-        for (int c = 0; c < D / 8; ++c) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(row + c * 8);
+        if (r < N) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(k_p + ((int64_t)bh * N + r) * D + ck * 8);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const float a = __uint_as_float(w[q] << 16), b = __uint_as_float(w[q] & 0xFFFF0000u);
+                const float a = __uint_as_float(w[q] << 16), c = __uint_as_float(w[q] & 0xFFFF0000u);
                 ss = fmaf(a, a, ss);
-                ss = fmaf(b, b, ss);
+                ss = fmaf(c, c, ss);
             }
         }
+#pragma unroll
+        for (int off = TPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
         best = fmaxf(best, ss);
     }
-    red[threadIdx.x] = __float_as_int(best);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+    if (lane == 0) red[wave] = best;
     __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (threadIdx.x < off) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + off]);
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) atomicMax(&kmax[bh], red[0]);  // squared norm, as float bits
+    if (threadIdx.x == 0)
+        atomicMax(&kmax[bh], __float_as_int(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t *q_offsets, int BH, int Cq, int tq,
@@ -674,7 +680,7 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table, redo, kmax2);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if (dt == ISG_BF16) {
-        const dim3 kgrid((unsigned)((N + 255) / 256), (unsigned)(B * H));
+        const dim3 kgrid((unsigned)std::min((N + 255) / 256, 64), (unsigned)(B * H));
         if (d == 128) {
             kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<128, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,

@@ -17,6 +17,7 @@ namespace {
 constexpr int kSortChunk = 1024;  // tokens per histogram / scatter chunk
 constexpr int kMaxC = 4096;
 constexpr int kAssignTile = 32;   // centroids per LDS tile in the assign kernel
+constexpr int kPieceRows = 256;   // rows per piece of the centroid update
 
 struct Strides {
     int64_t b, h, t;
@@ -136,10 +137,13 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *labels, int N,
     for (int c = threadIdx.x; c < C; c += 256) out[c] = hs[c];
 }
 
-// hist[bh][chunk][c] -> first sorted row of (chunk, c); offsets = prefix of counts.
-__global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, int C, int32_t *offsets)
+// hist[bh][chunk][c] -> first sorted row of (chunk, c); offsets = prefix of counts;
+// poff = prefix of the number of kPieceRows-row pieces of every group.
+__global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, int C, int32_t *offsets,
+                                                   int32_t *poff)
 {
     __shared__ int cnt[kMaxC];
+    __shared__ int pcs[kMaxC];
     __shared__ int tmp[256];
     const int bh = blockIdx.x;
     int32_t *hb = hist + (int64_t)bh * nchunks * C;
@@ -151,15 +155,22 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, i
             run += v;
         }
         cnt[c] = run;
+        pcs[c] = (run + kPieceRows - 1) / kPieceRows;
     }
     __syncthreads();
     const int total = block_exclusive_scan_int(cnt, C, tmp);
+    const int ptotal = block_exclusive_scan_int(pcs, C, tmp);
     int32_t *ob = offsets + (int64_t)bh * (C + 1);
+    int32_t *pb = poff + (int64_t)bh * (C + 1);
     for (int c = threadIdx.x; c < C; c += 256) {
         ob[c] = cnt[c];
+        pb[c] = pcs[c];
         for (int ch = 0; ch < nchunks; ++ch) hb[(int64_t)ch * C + c] += cnt[c];
     }
-    if (threadIdx.x == 0) ob[C] = total;
+    if (threadIdx.x == 0) {
+        ob[C] = total;
+        pb[C] = ptotal;
+    }
 }
 
 // One wave per chunk walks its tokens in order, 64 at a time; a token's rank
@@ -197,37 +208,73 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
     }
 }
 
-// c_j = mean of the rows of group j in sorted order, fp64 partial sums in a fixed
-// order (rows strided over RP slots, then slot order), rounded to fp32.
+// Centroid update in two passes, both in a fixed order: every group is cut into
+// pieces of kPieceRows sorted rows; a work-group sums one piece in fp64 (rows
+// strided over RP slots, then slot order) and the final pass adds the pieces of
+// each group in order and divides: c_j = mean of the rows of group j, rounded
+// to fp32 (an empty group keeps its centroid).
 template <typename T, int D>
-__global__ __launch_bounds__(256) void update_kernel(const T *x, Strides xs, int H, int N, int C,
-                                                     const int32_t *perm, const int32_t *offsets,
-                                                     float *cent)
+__global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides xs, int H, int N, int C,
+                                                           const int32_t *perm, const int32_t *offsets,
+                                                           const int32_t *poff, int maxp, double *partial)
 {
     constexpr int TPR = D / 8;     // threads per row
-    constexpr int RP = 256 / TPR;  // rows in flight
+    constexpr int RP = 256 / TPR;  // row slots
+    constexpr int U = 4;           // rows per slot loaded ahead
     __shared__ double red[RP][D];
-    const int j = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
-    const int r0 = offsets[(int64_t)bh * (C + 1) + j], r1 = offsets[(int64_t)bh * (C + 1) + j + 1];
-    if (r1 == r0) return;  // empty: keep the centroid
+    const int q = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int32_t *pb = poff + (int64_t)bh * (C + 1);
+    if (q >= pb[C]) return;
+    // group of piece q: the last j with poff[j] <= q (binary search)
+    int lo = 0, hi = C;  // poff[lo] <= q < poff[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (pb[mid] <= q) lo = mid; else hi = mid;
+    }
+    const int j = lo;
+    const int32_t *ob = offsets + (int64_t)bh * (C + 1);
+    const int r0 = ob[j] + (q - pb[j]) * kPieceRows, r1 = min(ob[j + 1], r0 + kPieceRows);
     const int rs = threadIdx.x / TPR, ck = threadIdx.x % TPR;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const T *xb = x + b * xs.b + h * xs.h + ck * 8;
-    const int32_t *pb = perm + (int64_t)bh * N;
-    for (int r = r0 + rs; r < r1; r += RP) {
-        float v[8];
-        load8(xb + (int64_t)pb[r] * xs.t, v);
+    const int32_t *pm = perm + (int64_t)bh * N;
+    for (int r = r0 + rs; r < r1; r += U * RP) {
+        float v[U][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += (double)v[e];
+        for (int u = 0; u < U; ++u) {
+            const int rr = r + u * RP;
+            if (rr < r1) load8(xb + (int64_t)pm[rr] * xs.t, v[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (r + u * RP < r1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] += (double)v[u][e];
+            }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[rs][ck * 8 + e] = acc[e];
     __syncthreads();
-    const double n = (double)(r1 - r0);
     for (int k = threadIdx.x; k < D; k += 256) {
-        double s = 0.0;
-        for (int rr = 0; rr < RP; ++rr) s += red[rr][k];
-        cent[((int64_t)bh * C + j) * D + k] = (float)(s / n);
+        double sum = 0.0;
+        for (int rr = 0; rr < RP; ++rr) sum += red[rr][k];
+        partial[((int64_t)bh * maxp + q) * D + k] = sum;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(128) void update_final_kernel(int C, const int32_t *offsets, const int32_t *poff,
+                                                           int maxp, const double *partial, float *cent)
+{
+    const int j = blockIdx.x, bh = blockIdx.y;
+    const int32_t *ob = offsets + (int64_t)bh * (C + 1);
+    const int n = ob[j + 1] - ob[j];
+    if (n == 0) return;  // empty: keep the centroid
+    const int32_t *pb = poff + (int64_t)bh * (C + 1);
+    for (int k = threadIdx.x; k < D; k += 128) {
+        double sum = 0.0;
+        for (int q = pb[j]; q < pb[j + 1]; ++q) sum += partial[((int64_t)bh * maxp + q) * D + k];
+        cent[((int64_t)bh * C + j) * D + k] = (float)(sum / (double)n);
     }
 }
 
@@ -252,74 +299,68 @@ __global__ __launch_bounds__(256) void gather_kernel(const T *x, Strides xs, con
 // ---------------------------------------------------------------- MFMA assign (bf16 x)
 // Distances |x - c|^2 = |c|^2 - 2<x, c> + |x|^2 on v_mfma_f32_32x32x16_bf16.  x is
 // exact in bf16; each fp32 centroid is split into bf16 planes hi + lo (16
-// significant bits, residual <= 2^-16 |c|); padded rows have norm 1e30.  Per token the two best candidates
-// (and the third-best value) are kept; whenever a rival lies within
+// significant bits, residual <= 2^-16 |c|); padded rows have norm 1e30.  Per
+// token the four best candidates are kept; whenever a rival lies within
 // tau = 1e-4 (|x|^2 + max_j |c_j|^2) -- several times the worst-case error of the
 // split and of fp32 accumulation -- the decision is re-taken in fp64 with the
-// same unfused arithmetic as the exact definition (two candidates, or every
-// centroid when a third is also close), ties to the lower index.
+// same unfused arithmetic as the exact definition (two or three candidates, or
+// every centroid when a fourth is also close), ties to the lower index.
 constexpr int kCT = 32;  // centroids per MFMA tile
 
+// One wave per centroid: bf16 planes hi + lo and the squared norm (fp64 over the
+// lanes, then a fixed butterfly); padded rows get zero planes and norm 1e30.
 template <int D>
 __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent, int C, int Cpad, uint16_t *planes,
-                                                              float *norms, float *cmax)
+                                                              float *norms)
 {
-    __shared__ float red[256];
-    const int bh = blockIdx.x;
-    float lmax = 0.0f;
-    for (int j = threadIdx.x; j < Cpad; j += 256) {
-        uint16_t *hi = planes + ((int64_t)bh * 2 * Cpad + j) * D;
-        uint16_t *lo = planes + ((int64_t)bh * 2 * Cpad + Cpad + j) * D;
+    const int bh = blockIdx.y, lane = threadIdx.x & 63;
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (j >= Cpad) return;
+    uint16_t *hi = planes + ((int64_t)bh * 2 * Cpad + j) * D;
+    uint16_t *lo = planes + ((int64_t)bh * 2 * Cpad + Cpad + j) * D;
+    double nn = 0.0;
+    for (int k = lane; k < D; k += 64) {
         if (j < C) {
-            const float *c = cent + ((int64_t)bh * C + j) * D;
-            double nn = 0.0;
-            for (int k = 0; k < D; ++k) {
-                const float v = c[k];
-                const uint16_t hb = f32_to_bf16_bits(v);
-                const float r = v - bf16_bits_to_f32(hb);  // exact
-                hi[k] = hb;
-                lo[k] = f32_to_bf16_bits(r);
-                nn += (double)v * (double)v;
-            }
-            norms[(int64_t)bh * Cpad + j] = (float)nn;
-            lmax = fmaxf(lmax, (float)nn);
+            const float v = cent[((int64_t)bh * C + j) * D + k];
+            const uint16_t hb = f32_to_bf16_bits(v);
+            const float r = v - bf16_bits_to_f32(hb);  // exact
+            hi[k] = hb;
+            lo[k] = f32_to_bf16_bits(r);
+            nn += (double)v * (double)v;
         } else {
-            for (int k = 0; k < D; ++k) { hi[k] = 0; lo[k] = 0; }
-            norms[(int64_t)bh * Cpad + j] = 1e30f;  // never wins; finite so keys stay ordered
+            hi[k] = 0;
+            lo[k] = 0;
         }
     }
-    red[threadIdx.x] = lmax;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) cmax[bh] = red[0];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) nn += __shfl_xor(nn, off);
+    if (lane == 0) norms[(int64_t)bh * Cpad + j] = j < C ? (float)nn : 1e30f;  // padded: never wins
 }
 
-// Candidates are kept as float keys: a positive approximate distance with its
-// low mantissa bits replaced by the centroid index.  Positive floats order like
-// their bit patterns, so min/med3 on keys order by distance (up to the dropped
-// bits, a resolution of 2^bits ulps) and carry the index along.  The four
-// smallest keys are kept sorted: one min and three med3 per candidate.
+// Candidates are kept as integer keys: the bits of a positive approximate
+// distance with the low bits replaced by the centroid index.  Positive floats
+// order like their bit patterns, so unsigned min/med3 on keys order by distance
+// (up to the dropped bits, a resolution of 2^bits ulps) and carry the index
+// along.  The four smallest keys are kept sorted: one min and three med3 per
+// candidate.
 struct Top4 {
-    float k1, k2, k3, k4;
+    uint32_t k1, k2, k3, k4;
 };
 
-__device__ __forceinline__ void top_insert(Top4 &t, float key)
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c)
 {
-    const float n4 = __builtin_amdgcn_fmed3f(t.k3, t.k4, key);
-    const float n3 = __builtin_amdgcn_fmed3f(t.k2, t.k3, key);
-    const float n2 = __builtin_amdgcn_fmed3f(t.k1, t.k2, key);
-    t.k1 = fminf(t.k1, key);
+    return max(min(a, b), min(max(a, b), c));
+}
+
+__device__ __forceinline__ void top_insert(Top4 &t, uint32_t key)
+{
+    const uint32_t n4 = umed3(t.k3, t.k4, key);
+    const uint32_t n3 = umed3(t.k2, t.k3, key);
+    const uint32_t n2 = umed3(t.k1, t.k2, key);
+    t.k1 = min(t.k1, key);
     t.k2 = n2;
     t.k3 = n3;
     t.k4 = n4;
-}
-
-__device__ __forceinline__ float make_key(float d, uint32_t hi_mask, int j)
-{
-    return __uint_as_float((__float_as_uint(d) & hi_mask) | (uint32_t)j);
 }
 
 // fp64 partial sum of (x_k - c_k)^2 over the DPL dims of one lane (x bf16, c fp32;
@@ -371,21 +412,80 @@ __device__ __forceinline__ double sum16(double v)
     return v;
 }
 
+// Centroid tile in LDS: [plane][row][16-byte chunk], the chunks of row r
+// XOR-swizzled by r mod (chunks per row), loaded straight from memory.
 template <int D>
-__global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__restrict__ x, Strides xs, int H, int N,
-                                                          int C, int Cpad, const uint16_t *__restrict__ planes,
-                                                          const float *__restrict__ norms,
-                                                          const float *__restrict__ cmax,
-                                                          const float *__restrict__ cent, int32_t *__restrict__ labels)
+__device__ __forceinline__ int cswz(int plane, int row, int chunk)
+{
+    constexpr int CPR = D / 8;
+    return (plane * kCT + row) * CPR + (chunk ^ (row & (CPR - 1)));
+}
+
+template <int D>
+__device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, int Cpad, int tile, int wave,
+                                              int lane)
+{
+    constexpr int CPR = D / 8;
+    constexpr int NCH = 2 * kCT * CPR;  // chunks per tile (both planes)
+#pragma unroll
+    for (int it = 0; it < (NCH + 255) / 256; ++it) {
+        const int blk = it * 4 + wave;
+        if (blk * 64 < NCH) {
+            const int P = blk * 64 + lane;
+            const int plane = P / (kCT * CPR), rem = P % (kCT * CPR), row = rem / CPR;
+            const int c = (rem % CPR) ^ (row & (CPR - 1));
+            const uint16_t *src = pb + ((int64_t)plane * Cpad + tile * kCT + row) * D + c * 8;
+            __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                             (void __attribute__((address_space(3))) *)(buf + blk * 1024), 16, 0,
+                                             0);
+        }
+    }
+}
+
+// One tile of 32 centroids against the 64 tokens of this wave: distances via
+// MFMA, then every (token, centroid) key into the token's top three.
+template <int D>
+__device__ __forceinline__ void assign_tile(const uint8_t *cur, const float *ncur, int tile, const bf16x8 (*xf)[D / 16],
+                                            const float *xn1, uint32_t hi_mask, Top4 *top, int hl, int l32)
 {
     constexpr int NDS = D / 16;
-    constexpr int RSTR = D * 2 + 16;          // bytes per centroid row in LDS
-    constexpr int PBYTES = kCT * RSTR;        // one plane of a tile
-    constexpr int TBYTES = 2 * PBYTES;
-    constexpr int CPR = D / 8;                // 16-byte chunks per row
-    constexpr int NCH = 2 * kCT * CPR;        // chunks per tile (both planes)
-    constexpr int CIT = (NCH + 255) / 256;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * TBYTES];
+    f32x16 acc[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) {
+        const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(cur + cswz<D>(0, l32, 2 * s + hl) * 16);
+        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(cur + cswz<D>(1, l32, 2 * s + hl) * 16);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[tb][s], acc[tb], 0, 0, 0);
+            acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int cl = (r >> 2) * 8 + hl * 4 + (r & 3);
+        const float nc = ncur[cl];
+        const uint32_t j = (uint32_t)(tile * kCT + cl);
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const uint32_t d = __float_as_uint(fmaf(-2.0f, acc[tb][r], nc) + xn1[tb]);
+            top_insert(top[tb], (d & hi_mask) | j);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void assign_mfma_kernel(
+    const uint16_t *__restrict__ x, Strides xs, int H, int N, int C, int Cpad, const uint16_t *__restrict__ planes,
+    const float *__restrict__ norms, const float *__restrict__ cent, int32_t *__restrict__ labels)
+{
+    constexpr int NDS = D / 16;
+    constexpr int TBYTES = 2 * kCT * D * 2;  // both planes of a tile
+    __shared__ __attribute__((aligned(1024))) uint8_t tb0[TBYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t tb1[TBYTES];
     __shared__ float nsm[2][kCT];
     const int bh = blockIdx.y, b = bh / H, h = bh % H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
@@ -419,71 +519,43 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__rest
     int ibits = 1;
     while ((1 << ibits) < Cpad) ++ibits;
     const uint32_t imask = (1u << ibits) - 1u, hi_mask = ~imask;
-    float xn1[2] = {xn[0] + 1.0f, xn[1] + 1.0f};
+    const float xn1[2] = {xn[0] + 1.0f, xn[1] + 1.0f};
     Top4 top[2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) top[tb] = Top4{INFINITY, INFINITY, INFINITY, INFINITY};
+    for (int tb = 0; tb < 2; ++tb) top[tb] = Top4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
 
-    u32x4 pre[CIT];
-    float npre = 0.0f;
-    auto gload = [&](int tile) {
+    // largest centroid norm of the head (for the decision window)
+    __shared__ float cm_part[4];
+    float lmax = 0.0f;
+    for (int j = tid; j < C; j += 256) lmax = fmaxf(lmax, nb[j]);
 #pragma unroll
-        for (int it = 0; it < CIT; ++it) {
-            const int e = it * 256 + tid;
-            if (e < NCH) {
-                const int plane = e / (kCT * CPR), rem = e % (kCT * CPR), row = rem / CPR, ch = rem % CPR;
-                pre[it] = *reinterpret_cast<const u32x4 *>(pb + ((int64_t)plane * Cpad + tile * kCT + row) * D + ch * 8);
-            }
-        }
-        if (tid < kCT) npre = nb[tile * kCT + tid];
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int it = 0; it < CIT; ++it) {
-            const int e = it * 256 + tid;
-            if (e < NCH) {
-                const int plane = e / (kCT * CPR), rem = e % (kCT * CPR), row = rem / CPR, ch = rem % CPR;
-                *reinterpret_cast<u32x4 *>(smem + buf * TBYTES + plane * PBYTES + row * RSTR + ch * 16) = pre[it];
-            }
-        }
-        if (tid < kCT) nsm[buf][tid] = npre;
-    };
-
-    gload(0);
-    sstore(0);
+    for (int off = 32; off > 0; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off));
+    if (lane == 0) cm_part[wave] = lmax;
+    planes_direct<D>(tb0, pb, Cpad, 0, wave, lane);
+    if (tid < kCT) nsm[0][tid] = nb[tid];
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int tile = 0; tile < ntiles; ++tile) {
-        const int cur = tile & 1;
-        const bool more = tile + 1 < ntiles;
-        if (more) gload(tile + 1);
-        f32x16 acc[2];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
-        const uint8_t *hb = smem + cur * TBYTES;
-        const uint8_t *lb = hb + PBYTES;
-#pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-            const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(hb + l32 * RSTR + s * 32 + hl * 16);
-            const bf16x8 al = *reinterpret_cast<const bf16x8 *>(lb + l32 * RSTR + s * 32 + hl * 16);
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xf[tb][s], acc[tb], 0, 0, 0);
-                acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
-            }
+    const float cm = fmaxf(fmaxf(cm_part[0], cm_part[1]), fmaxf(cm_part[2], cm_part[3]));
+    for (int tile = 0; tile < ntiles; tile += 2) {
+        // tile in tb0 while tile+1 loads into tb1, then the reverse
+        float npre = 0.0f;
+        if (tile + 1 < ntiles) {
+            planes_direct<D>(tb1, pb, Cpad, tile + 1, wave, lane);
+            if (tid < kCT) npre = nb[(tile + 1) * kCT + tid];
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int cl = (r >> 2) * 8 + hl * 4 + (r & 3);
-            const float nc = nsm[cur][cl];
-            const int j = tile * kCT + cl;
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) {
-                top_insert(top[tb], make_key(fmaf(-2.0f, acc[tb][r], nc) + xn1[tb], hi_mask, j));
-            }
+        assign_tile<D>(tb0, nsm[0], tile, xf, xn1, hi_mask, top, hl, l32);
+        if (tid < kCT) nsm[1][tid] = npre;
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tile + 1 >= ntiles) break;
+        npre = 0.0f;
+        if (tile + 2 < ntiles) {
+            planes_direct<D>(tb0, pb, Cpad, tile + 2, wave, lane);
+            if (tid < kCT) npre = nb[(tile + 2) * kCT + tid];
         }
-        if (more) sstore(cur ^ 1);
+        assign_tile<D>(tb1, nsm[1], tile + 1, xf, xn1, hi_mask, top, hl, l32);
+        if (tid < kCT) nsm[0][tid] = npre;
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
 
@@ -503,14 +575,13 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__rest
     __shared__ int grp_j[16];
     if (tid == 0) { rq_n = 0; full_n = 0; }
     __syncthreads();
-    const float cm = cmax[bh];
     const float *cb = cent + (int64_t)bh * C * D;
     int qpos[2] = {0, 0}, qcnt[2] = {0, 0}, fpos[2] = {-1, -1};
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         Top4 &T = top[tb];
-        const float o1 = __shfl_xor(T.k1, 32), o2 = __shfl_xor(T.k2, 32), o3 = __shfl_xor(T.k3, 32),
-                    o4 = __shfl_xor(T.k4, 32);
+        const uint32_t o1 = __shfl_xor(T.k1, 32), o2 = __shfl_xor(T.k2, 32), o3 = __shfl_xor(T.k3, 32),
+                       o4 = __shfl_xor(T.k4, 32);
         top_insert(T, o1);
         top_insert(T, o2);
         top_insert(T, o3);
@@ -518,15 +589,15 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__rest
         if (hl != 0 || tok[tb] >= N) continue;
         // window: tau plus the key resolution (2^ibits ulps of the largest value compared)
         const float tau = 1e-4f * (xn[tb] + cm);
-        const float d1 = __uint_as_float(__float_as_uint(T.k1) & hi_mask);
+        const float d1 = __uint_as_float(T.k1 & hi_mask);
         const float lim0 = d1 + tau;
         const float res = __uint_as_float((__float_as_uint(lim0) & 0x7F800000u)) * ldexpf(1.0f, ibits - 23);
         const float lim = lim0 + 2.0f * res;
         const int slot = wave * 64 + tb * 32 + l32;
-        const float d2 = __uint_as_float(__float_as_uint(T.k2) & hi_mask);
-        const float d3 = __uint_as_float(__float_as_uint(T.k3) & hi_mask);
-        const float d4 = __uint_as_float(__float_as_uint(T.k4) & hi_mask);
-        if (d4 < lim) {
+        const float d2 = __uint_as_float(T.k2 & hi_mask);
+        const float d3 = __uint_as_float(T.k3 & hi_mask);
+        const float d4 = __uint_as_float(T.k4 & hi_mask);
+        if (d4 < lim) {  // four or more close candidates: every centroid in fp64
             const int f = atomicAdd(&full_n, 1);
             full_slot[f] = slot;
             fpos[tb] = f;
@@ -534,9 +605,9 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__rest
             const int n = 1 + (d2 < lim) + (d3 < lim);
             if (n > 1) {
                 const int pos = atomicAdd(&rq_n, n);
-                rq_slot[pos] = slot; rq_cand[pos] = (int)(__float_as_uint(T.k1) & imask);
-                rq_slot[pos + 1] = slot; rq_cand[pos + 1] = (int)(__float_as_uint(T.k2) & imask);
-                if (n > 2) { rq_slot[pos + 2] = slot; rq_cand[pos + 2] = (int)(__float_as_uint(T.k3) & imask); }
+                rq_slot[pos] = slot; rq_cand[pos] = (int)(T.k1 & imask);
+                rq_slot[pos + 1] = slot; rq_cand[pos + 1] = (int)(T.k2 & imask);
+                if (n > 2) { rq_slot[pos + 2] = slot; rq_cand[pos + 2] = (int)(T.k3 & imask); }
                 qpos[tb] = pos;
                 qcnt[tb] = n;
             }
@@ -579,7 +650,7 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__rest
     for (int tb = 0; tb < 2; ++tb) {
         const int t = tok[tb];
         if (hl != 0 || t >= N) continue;
-        int best = (int)(__float_as_uint(top[tb].k1) & imask);
+        int best = (int)(top[tb].k1 & imask);
         if (fpos[tb] >= 0) {
             best = full_best[fpos[tb]];
         } else if (qcnt[tb] > 1) {
@@ -596,8 +667,8 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const uint16_t *__rest
 }
 
 struct ClusterWs {
-    size_t off_hist, off_planes, off_norms, off_cmax, total;
-    int Cpad;
+    size_t off_hist, off_planes, off_norms, off_poff, off_partial, total;
+    int Cpad, maxp;
 };
 
 ClusterWs cluster_ws(int B, int H, int N, int d, int C)
@@ -606,11 +677,13 @@ ClusterWs cluster_ws(int B, int H, int N, int d, int C)
     const size_t BH = (size_t)B * H;
     const size_t nchunks = ((size_t)N + kSortChunk - 1) / kSortChunk;
     w.Cpad = (C + kCT - 1) / kCT * kCT;
+    w.maxp = (N + kPieceRows - 1) / kPieceRows + C;  // >= sum over groups of ceil(n_j / kPieceRows)
     size_t o = 0;
     w.off_hist = o; o += isg_align256(BH * nchunks * C * sizeof(int32_t));
     w.off_planes = o; o += isg_align256(BH * 2 * w.Cpad * d * sizeof(uint16_t));
     w.off_norms = o; o += isg_align256(BH * w.Cpad * sizeof(float));
-    w.off_cmax = o; o += isg_align256(BH * sizeof(float));
+    w.off_poff = o; o += isg_align256(BH * (C + 1) * sizeof(int32_t));
+    w.off_partial = o; o += isg_align256(BH * (size_t)w.maxp * d * sizeof(double));
     w.total = o;
     return w;
 }
@@ -623,10 +696,9 @@ void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, 
     if constexpr (std::is_same<T, uint16_t>::value) {
         uint16_t *planes = (uint16_t *)(ws + w.off_planes);
         float *norms = (float *)(ws + w.off_norms);
-        float *cmax = (float *)(ws + w.off_cmax);
-        centroid_planes_kernel<D><<<BH, 256, 0, st>>>(cent, C, w.Cpad, planes, norms, cmax);
+        centroid_planes_kernel<D><<<dim3(w.Cpad / 4, BH), 256, 0, st>>>(cent, C, w.Cpad, planes, norms);
         assign_mfma_kernel<D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, w.Cpad, planes, norms,
-                                                                         cmax, cent, labels);
+                                                                         cent, labels);
     } else {
         assign_kernel<T, D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, cent, labels);
     }
@@ -641,6 +713,8 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     const int nchunks = (N + kSortChunk - 1) / kSortChunk;
     const ClusterWs w = cluster_ws(B, H, N, D, C);
     int32_t *hist = (int32_t *)(ws + w.off_hist);
+    int32_t *poff = (int32_t *)(ws + w.off_poff);
+    double *partial = (double *)(ws + w.off_partial);
     int bits = 1;
     while ((1 << bits) < C) ++bits;
     if (init_mode == 0) {
@@ -651,9 +725,11 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     for (int it = 0; it < iters; ++it) {
         launch_assign<T, D>(st, x, xs, B, H, N, C, cent, labels, ws, w);
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
-        scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, offsets);
+        scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, offsets, poff);
         scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, N, C, nchunks, bits, perm);
-        update_kernel<T, D><<<dim3(C, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, cent);
+        update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
+                                                                    partial);
+        update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent);
     }
     if (x_perm || comp_perm) {
         const int64_t total = (int64_t)BH * N * (D / 8);
