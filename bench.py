@@ -47,6 +47,51 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_wan14b_720p_e8s8_traffic.md")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_means_amd", "csrc", "attention.hip")
+
+
+def measured_traffic(workload, exact, sample):
+    """HBM bytes per attention launch from the committed counter summary (FETCH_SIZE
+    and WRITE_SIZE, each scaled by the plain-copy calibration), or None when that
+    summary was taken on another workload or on a different attention source."""
+    import hashlib
+    if (workload, exact, sample) != ("wan14b_720p", 0.08, 0.08) or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    src = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != src:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def attention_bytes(d, N, H, B, q_offsets, k_offsets, exact_groups, n_exact, n_sample):
+    """Algorithmic HBM bytes of one attention launch: K and V rows (bf16) of every
+    column of a query group read once per group, Q read and O written once (bf16),
+    LSE written once (fp32)."""
+    import numpy as np
+    ko = k_offsets.cpu().numpy().astype(np.int64)
+    eg = exact_groups.cpu().numpy()
+    ne = n_exact.cpu().numpy()
+    ns = n_sample.cpu().numpy().astype(np.int64)
+    nk = np.diff(ko, axis=-1)
+    Bq, Hq, Cq, Ck = eg.shape
+    cols = ns.copy()
+    for b in range(Bq):
+        for h in range(Hq):
+            valid = np.arange(Ck)[None, :] < ne[b, h][:, None]
+            g = np.where(valid, eg[b, h], 0)
+            cols[b, h] += (nk[b, h][g] * valid).sum(-1)
+    return float(cols.sum() * 2 * d * 2 + 2 * B * H * N * d * 2 + B * H * N * 4)
+
+
 def attention_flops(d, q_offsets, k_offsets, exact_groups, n_exact, n_sample):
     """4 d sum_i n^q_i (|E_i| + n_sample_i), from the lists the step produced."""
     import numpy as np
@@ -234,6 +279,8 @@ def main():
     # the work of the timed steps (every step computes the same lists)
     flops, pairs = attention_flops(d, cq["offsets"], ck["offsets"], sel["exact_groups"], sel["n_exact"],
                                    sel["n_sample"])
+    abytes = attention_bytes(d, N, H, B, cq["offsets"], ck["offsets"], sel["exact_groups"], sel["n_exact"],
+                             sel["n_sample"])
     print(f"# attention {flops / 1e12:.2f} TFLOP per call", file=sys.stderr, flush=True)
     ms_step = wall * 1e3 / args.steps
     stage_ms = {s: float(np.mean([a.elapsed_time(b) for a, b in ev[s]])) for s in stages}
@@ -262,8 +309,11 @@ def main():
         "attention_tflop_per_call": round(flops / 1e12, 4),
         "stage_ms": {s: round(t, 3) for s, t in stage_ms.items()},
         "roofline": {"bound": "mfma" if w["dtype"] == "bf16" else "alu", "achieved": round(att_tflops, 2),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(att_tflops / peak, 4), "traffic": None,
-                     "kernel": "isg_attention (attn_bf16_kernel + column-list and tile-table prep)"},
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(att_tflops / peak, 4),
+                     "traffic": measured_traffic(args.workload, args.exact, args.sample),
+                     "traffic_unit": "bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
+                     "algorithmic_bytes": abytes,
+                     "kernel": "isg_attention: attn_bf16_kernel with its key-norm, column-list and tile-table prep"},
     }
     if args.sweep:
         sweep = {}
