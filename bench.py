@@ -40,6 +40,14 @@ def parse():
                     help="sampling mode (default: votes for a workload with product quantisation, else importance)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time the attention at every budget of the workload")
+    ap.add_argument("--top-p", type=float, default=None, metavar="P",
+                    help="size the exact set by mass (groups by pi until the running pi reaches P) instead of --exact")
+    ap.add_argument("--density-study", action="store_true",
+                    help="also report the relative L2 error against dense attention of exact-only, importance and "
+                         "uniform calls across the budget sweep (standard and high-entropy generators)")
+    ap.add_argument("--study-heads", type=int, default=4, help="heads used by --density-study and --n-sweep")
+    ap.add_argument("--n-sweep", action="store_true",
+                    help="also time the step and the attention at N = 75600 x 1, 2, 4, 8 (more latent frames)")
     ap.add_argument("--attention-only", type=int, default=0, metavar="K",
                     help="profiling aid: after one full step, run only K attention calls and exit")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
@@ -113,7 +121,7 @@ def attention_flops(d, q_offsets, k_offsets, exact_groups, n_exact, n_sample):
     return float(4 * d * (nq * cols).sum()), float((nq * cols).sum())
 
 
-def cpu_baseline(w, q, k, v, E, m, seed, mode="importance"):
+def cpu_baseline(w, q, k, v, E, m, seed, mode="importance", top_p=None):
     """The oracle as it stands on one head of the workload: every stage on the whole
     head except attention, which runs on a sample of query groups and is scaled to all
     groups of the head by its share of the head's attention flops."""
@@ -127,7 +135,7 @@ def cpu_baseline(w, q, k, v, E, m, seed, mode="importance"):
     t0 = time.perf_counter()
     cq = oracle.cluster(qh, Cq, w["iters"])
     ck = oracle.cluster(kh, Ck, w["iters"], companion=vh)
-    S, _ = oracle.probs(cq["centroids"], ck["centroids"], ck["offsets"], scale)
+    S, pi = oracle.probs(cq["centroids"], ck["centroids"], ck["offsets"], scale)
     votes = None
     if mode == "votes":
         P, Cc = w["pq"]
@@ -136,8 +144,11 @@ def cpu_baseline(w, q, k, v, E, m, seed, mode="importance"):
         kbar = oracle.pq_kbar(kc, kcb, ck["perm"], ck["offsets"])
         tables = oracle.pq_tables(qcb, kbar, scale)
         votes = oracle.pq_votes(qc, tables, cq["perm"], cq["offsets"], ck["offsets"], E)
-    sel = oracle.select_sample(S, ck["offsets"], N, E, m, seed=seed, mode={"importance": 0, "uniform": 1,
-                                                                          "votes": 2}[mode], votes=votes)
+    mcode = {"importance": 0, "uniform": 1, "votes": 2}[mode]
+    if top_p is not None:
+        sel = oracle.select_sample_topp(S, pi, ck["offsets"], N, top_p, m, mode=mcode, seed=seed)
+    else:
+        sel = oracle.select_sample(S, ck["offsets"], N, E, m, seed=seed, mode=mcode, votes=votes)
     t_pre = time.perf_counter() - t0
     nq = np.diff(cq["offsets"][0, 0])
     nk = np.diff(ck["offsets"][0, 0])
@@ -166,6 +177,117 @@ def cpu_baseline(w, q, k, v, E, m, seed, mode="importance"):
                        f"{len(pick)} heaviest query groups ({frac * 100:.1f} % of the head's attention flops, "
                        f"{t_att:.1f} s) scaled to the head; fp64 C with OpenMP"),
             "seconds_measured": round(t_pre + t_att + t_un, 2), "seconds_per_head_est": round(t_head, 2)}
+
+
+def dense_rows(q, k, v, rows, scale):
+    """Dense attention of the given query rows of every head, fp32 on the GPU (the
+    reference of the density study; plain torch matmuls, not the product path)."""
+    import torch
+    B, H, N, d = q.shape
+    out = torch.empty((B, H, len(rows), d), device=q.device, dtype=torch.float32)
+    for b in range(B):
+        for h in range(H):
+            qs = q[b, h, rows].float()
+            kk = k[b, h].float()
+            s = torch.matmul(qs, kk.t().contiguous()) * scale
+            pmat = torch.softmax(s, dim=-1)
+            out[b, h] = torch.matmul(pmat, v[b, h].float())
+    return out
+
+
+def density_study(args, w, isg, make_workload, WORKLOADS, budget_keys, dev):
+    """Relative L2 error of one call against dense attention, on a sample of query
+    rows, for exact-only (E+S exact), exact+importance and exact+uniform calls across
+    the workload's budget sweep; standard and high-entropy generators."""
+    import numpy as np
+    import torch
+    from block_sparse_attention_means_amd.synth import structured_values
+    out = {}
+    gens = {"standard": dict(w), "high_entropy": dict(WORKLOADS["wan14b_720p_stress_pq"])}
+    for (gname, wg), vkind in [(g, vk) for g in gens.items() for vk in ("v_iid", "v_clustered")]:
+        H, N, d = args.study_heads, wg["N"], wg["d"]
+        q, k, v, comp = make_workload(wg, seed=args.seed, H=H)
+        if vkind == "v_clustered":
+            v = structured_values(comp, d, n_centers=wg["n_centers"], seed=args.seed, dtype=wg["dtype"])
+        qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+        scale = isg.default_scale(d)
+        cq = isg.isg_cluster(qg, wg["Cq"], wg["iters"])
+        ck = isg.isg_cluster(kg, wg["Ck"], wg["iters"], companion=vg)
+        S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+        rows = torch.from_numpy(np.random.default_rng(1).choice(N, 512, replace=False)).to(dev)
+        ref = dense_rows(qg, kg, vg, rows, scale)
+        refn = float(torch.linalg.vector_norm(ref))
+        table = {}
+        for (es, ss) in w["sweep"]:
+            E, m = budget_keys(es, N), budget_keys(ss, N)
+            res = {}
+            for name, e2, m2, mode in (("exact_only", budget_keys(es + ss, N), 0, "importance"),
+                                       ("importance", E, m, "importance"), ("uniform", E, m, "uniform")):
+                errs = []
+                for seed in range(1 if m2 == 0 else 3):
+                    sel = isg.isg_select_sample(S, ck["offsets"], N, e2, m2, mode=mode, seed=seed)
+                    o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"],
+                                                   cq["offsets"], ck["offsets"], sel, scale)
+                    o, _ = isg.isg_unpermute(o_p, lse_p, cq["perm"])
+                    errs.append(float(torch.linalg.vector_norm(o[:, :, rows].float() - ref)) / refn)
+                res[name] = round(float(np.mean(errs)), 5)
+            table[f"{int(es * 100)}+{int(ss * 100)}%"] = res
+        out[f"{gname}/{vkind}"] = table
+        del q, k, v, qg, kg, vg
+    out["note"] = (f"relative L2 error of O over 512 query rows x {args.study_heads} heads against dense fp32 "
+                   "attention; exact_only uses the whole E+S budget as exact keys; sampled modes average 3 seeds; "
+                   "v_iid: values N(0, I) as in the benchmark inputs; v_clustered: values with per-component means")
+    return out
+
+
+def n_sweep(args, w, isg, make_workload, budget_keys, dev):
+    """Attention and whole-step time as N grows (more latent frames of the same
+    45 x 80 latent plane), 8+8 % budgets, study heads."""
+    import torch
+    out = []
+    for mult in (1, 2, 4, 8):
+        T = 21 * mult
+        N = T * 45 * 80
+        wn = dict(w, N=N, grid=(T, 45, 80))
+        H = args.study_heads
+        q, k, v, _ = make_workload(wn, seed=args.seed, H=H)
+        qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+        del q, k, v
+        scale = isg.default_scale(w["d"])
+        E, m = budget_keys(args.exact, N), budget_keys(args.sample, N)
+        stream = torch.cuda.current_stream()
+        ws_a = torch.empty(isg.attention_workspace_size(1, H, N, w["Cq"], w["Ck"]), device=dev, dtype=torch.uint8)
+
+        def run():
+            cq = isg.isg_cluster(qg, w["Cq"], w["iters"])
+            ck = isg.isg_cluster(kg, w["Ck"], w["iters"], companion=vg)
+            S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+            sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, seed=args.seed)
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
+                                           ck["offsets"], sel, scale, workspace=ws_a)
+            a1.record(stream)
+            isg.isg_unpermute(o_p, lse_p, cq["perm"])
+            return cq, ck, sel, (a0, a1)
+
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cq, ck, sel, (a0, a1) = run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        flops, _ = attention_flops(w["d"], cq["offsets"], ck["offsets"], sel["exact_groups"], sel["n_exact"],
+                                   sel["n_sample"])
+        att_ms = a0.elapsed_time(a1)
+        out.append({"N": N, "latent_frames": T, "H": H, "exact_keys": E, "m": m,
+                    "step_ms": round(e0.elapsed_time(e1), 3), "attention_ms": round(att_ms, 3),
+                    "attention_tflops": round(flops / (att_ms * 1e-3) / 1e12, 2)})
+        del qg, kg, vg, ws_a
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -199,6 +321,9 @@ def main():
     B, H, N, d = w.get("B", 1), w["H"], w["N"], w["d"]
     E, m = budget_keys(args.exact, N), budget_keys(args.sample, N)
     mode = args.mode or ("votes" if w.get("pq") else "importance")
+    if args.top_p is not None and mode == "votes":
+        print("bench.py: --top-p sizes the exact set by mass; it does not combine with votes mode", file=sys.stderr)
+        sys.exit(2)
     if mode == "votes" and not w.get("pq"):
         print(f"bench.py: workload {args.workload} has no product-quantisation setting", file=sys.stderr)
         sys.exit(2)
@@ -225,7 +350,8 @@ def main():
         ck = isg.isg_cluster(kg, w["Ck"], w["iters"], companion=vg, workspace=ws_c)
         if record:
             marks[2].record(stream)
-        S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+        S, pi = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale,
+                              want_pi=args.top_p is not None)
         mi = 3
         if record:
             marks[mi].record(stream)
@@ -242,7 +368,10 @@ def main():
             mi += 1
             if record:
                 marks[mi].record(stream)
-        sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, mode=mode, seed=args.seed, votes=votes)
+        if args.top_p is not None:
+            sel = isg.isg_select_sample_topp(S, pi, ck["offsets"], N, args.top_p, m, mode=mode, seed=args.seed)
+        else:
+            sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, mode=mode, seed=args.seed, votes=votes)
         mi += 1
         if record:
             marks[mi].record(stream)
@@ -303,7 +432,7 @@ def main():
         "config": {"workload": args.workload, "B": B, "H": H, "N": N, "d": d, "Cq": w["Cq"], "Ck": w["Ck"],
                    "kmeans_iters": w["iters"], "exact_share": args.exact, "sample_share": args.sample,
                    "exact_keys": E, "m": m, "seed": args.seed, "mode": mode,
-                   "pq": list(w["pq"]) if mode == "votes" else None},
+                   "pq": list(w["pq"]) if mode == "votes" else None, "top_p": args.top_p},
         "attention_ms": round(att_ms, 3),
         "attention_tflops": round(att_tflops, 2),
         "attention_tflop_per_call": round(flops / 1e12, 4),
@@ -339,9 +468,15 @@ def main():
                                                            "tflops": round(f2 / ms / 1e9, 2),
                                                            "frac_peak": round(f2 / ms / 1e9 / peak, 4)}
         result["attention_sweep"] = sweep
+    if args.density_study:
+        print("# density study", file=sys.stderr, flush=True)
+        result["density_study"] = density_study(args, w, isg, make_workload, WORKLOADS, budget_keys, dev)
+    if args.n_sweep:
+        print("# N sweep", file=sys.stderr, flush=True)
+        result["n_sweep"] = n_sweep(args, w, isg, make_workload, budget_keys, dev)
     if not args.no_cpu_baseline:
         print("# timing the oracle on the host (bounded sample)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, E, m, args.seed, mode)
+        result["cpu_baseline"] = cpu_baseline(w, q, k, v, E, m, args.seed, mode, args.top_p)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

@@ -105,6 +105,7 @@ struct SelShared {
     int order[kMaxGroups];
     int n[kMaxGroups];
     float S[kMaxGroups];
+    float P[kMaxGroups];    // pi (top-p rule)
     int votes[kMaxGroups];
     int flag[kMaxGroups];   // 1 = exact
     int buf[kMaxGroups];    // scan scratch (ints)
@@ -117,21 +118,32 @@ struct SelShared {
     int red_i[kThreads];
 };
 
-__device__ __forceinline__ bool rank_before(const SelShared &sh, int a, int b, int mode, int Ck)
+// Ranking of non-empty groups: (S desc, j asc); (votes desc, S desc, j asc) in
+// votes mode; (pi desc, j asc) under the top-p rule.  Empty groups sort last.
+__device__ __forceinline__ bool rank_before(const SelShared &sh, int a, int b, int mode, bool topp, int Ck)
 {
     const bool ea = a < Ck && sh.n[a] > 0, eb = b < Ck && sh.n[b] > 0;
     if (ea != eb) return ea;
     if (!ea) return a < b;
+    if (topp) {
+        if (sh.P[a] != sh.P[b]) return sh.P[a] > sh.P[b];
+        return a < b;
+    }
     if (mode == ISG_SAMPLE_VOTES && sh.votes[a] != sh.votes[b]) return sh.votes[a] > sh.votes[b];
     if (sh.S[a] != sh.S[b]) return sh.S[a] > sh.S[b];
     return a < b;
 }
 
+// Exact set, then the shared sample.  Budget rule (pi == nullptr): the first
+// group of the ranking always, then groups while the running key count stays
+// <= exact_keys.  Top-p rule (pi given): groups in (pi desc, j asc) order until
+// the fp64 running sum of pi, added in that order by one lane, reaches top_p.
 __global__ __launch_bounds__(kThreads) void select_sample_kernel(
-    const float *scores, const int32_t *k_offsets, const int32_t *votes, int H, int Cq, int Ck,
-    int exact_keys, int m, int mode, uint64_t seed, uint64_t call_id, ProposalTable tbl,
+    const float *scores, const float *pi, double top_p, const int32_t *k_offsets, const int32_t *votes, int H,
+    int Cq, int Ck, int exact_keys, int m, int mode, uint64_t seed, uint64_t call_id, ProposalTable tbl,
     int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx, float *sample_bias, int32_t *n_sample)
 {
+    const bool topp = pi != nullptr;
     __shared__ SelShared sh;
     const int tid = threadIdx.x;
     const int64_t gi = blockIdx.x;
@@ -145,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void select_sample_kernel(
         if (j < Ck) {
             sh.n[j] = ko[j + 1] - ko[j];
             sh.S[j] = scores[gi * Ck + j];
+            sh.P[j] = topp ? pi[gi * Ck + j] : 0.0f;
             sh.votes[j] = votes ? votes[gi * Ck + j] : 0;
             sh.flag[j] = 0;
         }
@@ -158,25 +171,39 @@ __global__ __launch_bounds__(kThreads) void select_sample_kernel(
                 const int hi = lo + stride;
                 const bool up = (lo & size) == 0;
                 const int a = sh.order[lo], c = sh.order[hi];
-                const bool swap = up ? rank_before(sh, c, a, mode, Ck) : rank_before(sh, a, c, mode, Ck);
+                const bool swap = up ? rank_before(sh, c, a, mode, topp, Ck) : rank_before(sh, a, c, mode, topp, Ck);
                 if (swap) { sh.order[lo] = c; sh.order[hi] = a; }
             }
             __syncthreads();
         }
     }
-    // running key count along the order; the first group is always taken
-    for (int p = tid; p < Ck; p += kThreads) {
-        const int j = sh.order[p];
-        sh.buf[p] = sh.n[j];
+    if (topp) {
+        if (tid == 0) {
+            double mass = 0.0;
+            for (int p = 0; p < Ck; ++p) {
+                const int j = sh.order[p];
+                if (sh.n[j] == 0) break;  // empty groups sort last
+                sh.flag[j] = 1;
+                mass += (double)sh.P[j];
+                if (mass >= top_p) break;
+            }
+        }
+        __syncthreads();
+    } else {
+        // running key count along the order; the first group is always taken
+        for (int p = tid; p < Ck; p += kThreads) {
+            const int j = sh.order[p];
+            sh.buf[p] = sh.n[j];
+        }
+        __syncthreads();
+        block_exclusive_scan_int(sh.buf, Ck, sh.tmp);
+        for (int p = tid; p < Ck; p += kThreads) {
+            const int j = sh.order[p];
+            const int incl = sh.buf[p] + sh.n[j];
+            if (sh.n[j] > 0 && (p == 0 || incl <= exact_keys)) sh.flag[j] = 1;
+        }
+        __syncthreads();
     }
-    __syncthreads();
-    block_exclusive_scan_int(sh.buf, Ck, sh.tmp);
-    for (int p = tid; p < Ck; p += kThreads) {
-        const int j = sh.order[p];
-        const int incl = sh.buf[p] + sh.n[j];
-        if (sh.n[j] > 0 && (p == 0 || incl <= exact_keys)) sh.flag[j] = 1;
-    }
-    __syncthreads();
     // exact groups ascending
     for (int j = tid; j < Ck; j += kThreads) sh.buf[j] = sh.flag[j];
     __syncthreads();
@@ -318,8 +345,37 @@ extern "C" isg_status isg_select_sample(void *stream, const float *scores, const
     ProposalTable tbl;
     isg_proposal_table(tbl.v);
     hipStream_t st = (hipStream_t)stream;
-    select_sample_kernel<<<(unsigned)G, kThreads, 0, st>>>(scores, k_offsets, votes, H, Cq, Ck, exact_keys, m,
-                                                           mode, seed, call_id, tbl, exact_groups, n_exact,
-                                                           sample_idx, sample_bias, n_sample);
+    select_sample_kernel<<<(unsigned)G, kThreads, 0, st>>>(scores, nullptr, 0.0, k_offsets, votes, H, Cq, Ck,
+                                                           exact_keys, m, mode, seed, call_id, tbl, exact_groups,
+                                                           n_exact, sample_idx, sample_bias, n_sample);
     return isg_check_launch("isg_select_sample");
+}
+
+extern "C" isg_status isg_select_sample_topp(void *stream, const float *scores, const float *pi,
+                                             const int32_t *k_offsets, int B, int H, int Cq, int Ck, int N,
+                                             float top_p, int m, int mode, uint64_t seed, uint64_t call_id,
+                                             int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx,
+                                             float *sample_bias, int32_t *n_sample)
+{
+    ISG_REQUIRE(scores && pi && k_offsets && exact_groups && n_exact && n_sample, ISG_E_ARG,
+                "isg_select_sample_topp: null pointer argument");
+    ISG_REQUIRE(m == 0 || (sample_idx && sample_bias), ISG_E_ARG,
+                "isg_select_sample_topp: sample_idx / sample_bias required when m > 0");
+    ISG_REQUIRE(B >= 1 && H >= 1 && N >= 1, ISG_E_ARG, "isg_select_sample_topp: B, H, N must be >= 1");
+    ISG_REQUIRE(Cq >= 1 && Ck >= 1 && Ck <= kMaxGroups, ISG_E_ARG,
+                "isg_select_sample_topp: need Cq >= 1 and 1 <= Ck <= %d (got %d, %d)", kMaxGroups, Cq, Ck);
+    ISG_REQUIRE(std::isfinite(top_p) && top_p > 0.0f, ISG_E_ARG,
+                "isg_select_sample_topp: top_p must be finite and > 0");
+    ISG_REQUIRE(m >= 0 && m <= N, ISG_E_ARG, "isg_select_sample_topp: need 0 <= m <= N (got m=%d, N=%d)", m, N);
+    ISG_REQUIRE(mode == ISG_SAMPLE_IMPORTANCE || mode == ISG_SAMPLE_UNIFORM, ISG_E_ARG,
+                "isg_select_sample_topp: mode must be importance or uniform (got %d)", mode);
+    const int64_t G = (int64_t)B * H * Cq;
+    ISG_REQUIRE(G <= 0x7fffffff, ISG_E_ARG, "isg_select_sample_topp: too many groups");
+    ProposalTable tbl;
+    isg_proposal_table(tbl.v);
+    hipStream_t st = (hipStream_t)stream;
+    select_sample_kernel<<<(unsigned)G, kThreads, 0, st>>>(scores, pi, (double)top_p, k_offsets, nullptr, H, Cq,
+                                                           Ck, 0, m, mode, seed, call_id, tbl, exact_groups,
+                                                           n_exact, sample_idx, sample_bias, n_sample);
+    return isg_check_launch("isg_select_sample_topp");
 }

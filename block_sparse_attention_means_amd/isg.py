@@ -18,7 +18,7 @@ ISG_F32, ISG_BF16 = 0, 1
 MODES = {"importance": 0, "uniform": 1, "votes": 2}
 EXPORTS = ["isg_last_error", "isg_version", "isg_proposal_table", "isg_cluster_workspace_size",
            "isg_cluster", "isg_probs", "isg_select_sample", "isg_attention_workspace_size",
-           "isg_attention", "isg_unpermute", "isg_pq_votes"]
+           "isg_attention", "isg_unpermute", "isg_pq_votes", "isg_select_sample_topp"]
 
 _lib = None
 
@@ -57,10 +57,12 @@ def _declare(L):
     L.isg_attention.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                                 _i, _f, _p, _p, _p, _sz]
     L.isg_unpermute.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p]
+    L.isg_select_sample_topp.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _u64, _u64,
+                                         _p, _p, _p, _p, _p]
     L.isg_pq_votes.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                _p, _p, _p]
     for name in ["isg_cluster", "isg_probs", "isg_select_sample", "isg_attention", "isg_unpermute",
-                 "isg_pq_votes"]:
+                 "isg_pq_votes", "isg_select_sample_topp"]:
         getattr(L, name).restype = _i
 
 
@@ -156,17 +158,37 @@ def isg_probs(cq, ck, k_offsets, scale, *, want_pi=True, stream=None):
     return scores, pi
 
 
+def _sel_outputs(scores, m):
+    B, H, Cq, Ck = scores.shape
+    dev = scores.device
+    mm = max(int(m), 1)
+    return dict(exact_groups=torch.empty((B, H, Cq, Ck), device=dev, dtype=torch.int32),
+                n_exact=torch.empty((B, H, Cq), device=dev, dtype=torch.int32),
+                sample_idx=torch.empty((B, H, Cq, mm), device=dev, dtype=torch.int32),
+                sample_bias=torch.empty((B, H, Cq, mm), device=dev, dtype=torch.float32),
+                n_sample=torch.empty((B, H, Cq), device=dev, dtype=torch.int32), m=int(m))
+
+
+def isg_select_sample_topp(scores, pi, k_offsets, N, top_p, m, *, mode="importance", seed=0, call_id=0,
+                           stream=None):
+    """Exact set sized by the top-p rule on pi, then the shared sample."""
+    _dev(scores, "scores"); _dev(pi, "pi"); _dev(k_offsets, "k_offsets")
+    B, H, Cq, Ck = scores.shape
+    out = _sel_outputs(scores, m)
+    st = lib().isg_select_sample_topp(_stream(stream), _ptr(scores.contiguous()), _ptr(pi.contiguous()),
+                                      _ptr(k_offsets.contiguous()), B, H, Cq, Ck, N, float(top_p), int(m),
+                                      MODES[mode] if isinstance(mode, str) else int(mode), C.c_uint64(seed),
+                                      C.c_uint64(call_id), _ptr(out["exact_groups"]), _ptr(out["n_exact"]),
+                                      _ptr(out["sample_idx"]), _ptr(out["sample_bias"]), _ptr(out["n_sample"]))
+    _check(st, "isg_select_sample_topp")
+    return out
+
+
 def isg_select_sample(scores, k_offsets, N, exact_keys, m, *, mode="importance", seed=0, call_id=0,
                       votes=None, stream=None):
     _dev(scores, "scores"); _dev(k_offsets, "k_offsets")
     B, H, Cq, Ck = scores.shape
-    dev = scores.device
-    mm = max(int(m), 1)
-    out = dict(exact_groups=torch.empty((B, H, Cq, Ck), device=dev, dtype=torch.int32),
-               n_exact=torch.empty((B, H, Cq), device=dev, dtype=torch.int32),
-               sample_idx=torch.empty((B, H, Cq, mm), device=dev, dtype=torch.int32),
-               sample_bias=torch.empty((B, H, Cq, mm), device=dev, dtype=torch.float32),
-               n_sample=torch.empty((B, H, Cq), device=dev, dtype=torch.int32), m=int(m))
+    out = _sel_outputs(scores, m)
     st = lib().isg_select_sample(_stream(stream), _ptr(scores.contiguous()), _ptr(k_offsets.contiguous()),
                                  _ptr(None if votes is None else votes.contiguous()), B, H, Cq, Ck, N,
                                  int(exact_keys), int(m), MODES[mode] if isinstance(mode, str) else int(mode),
@@ -270,10 +292,11 @@ def default_scale(d: int) -> float:
 
 
 def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0, call_id=0, scale=None,
-             pq=None, stream=None):
+             pq=None, top_p=None, stream=None):
     """All steps on one batch: cluster Q, cluster K (+V), probs, [PQ votes],
     select/sample, attention, unpermute.  ``pq=(P, Cc)`` is required by
-    mode "votes".  Returns every intermediate (all on the GPU)."""
+    mode "votes"; ``top_p`` sizes the exact set by mass instead of
+    ``exact_keys``.  Returns every intermediate (all on the GPU)."""
     d = q.shape[-1]
     scale = default_scale(d) if scale is None else scale
     cq = isg_cluster(q, Cq, iters, stream=stream)
@@ -289,8 +312,12 @@ def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0
         pqr = isg_pq_votes(qc, qcb, kc, kcb, cq["perm"], cq["offsets"], ck["perm"], ck["offsets"], exact_keys,
                            scale, stream=stream)
         pqr.update(q_codes=qc, q_codebooks=qcb, k_codes=kc, k_codebooks=kcb)
-    sel = isg_select_sample(scores, ck["offsets"], q.shape[2], exact_keys, m, mode=mode, seed=seed,
-                            call_id=call_id, votes=None if pqr is None else pqr["votes"], stream=stream)
+    if top_p is not None:
+        sel = isg_select_sample_topp(scores, pi, ck["offsets"], q.shape[2], top_p, m, mode=mode, seed=seed,
+                                     call_id=call_id, stream=stream)
+    else:
+        sel = isg_select_sample(scores, ck["offsets"], q.shape[2], exact_keys, m, mode=mode, seed=seed,
+                                call_id=call_id, votes=None if pqr is None else pqr["votes"], stream=stream)
     o_p, lse_p = isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
                                sel, scale, stream=stream)
     o, lse = isg_unpermute(o_p, lse_p, cq["perm"], stream=stream)

@@ -97,6 +97,26 @@ def make_qkv(H: int, N: int, d: int, *, n_centers: int = 64, grid=None,
     return q, k, v, comp
 
 
+def structured_values(comp, d: int, *, n_centers: int = 64, seed: int = 0, noise_std: float = 0.3,
+                      dtype: str = "bf16"):
+    """Values that carry the keys' cluster structure: v_t = nu_{z_t} + noise_std * eps,
+    with nu_c ~ N(0, I_d) drawn per (batch, head) from their own seeded stream.  comp
+    is the component index per token ([B, H, N], as returned by make_qkv).  Used by
+    the error-vs-density study: with values independent of the keys (v ~ N(0, I)) the
+    dense output of a near-uniform row is close to zero and a relative error says
+    little, while real values carry structure that a skipped region contributes."""
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    B, H, N = comp.shape
+    v = torch.empty((B, H, N, d), dtype=tdt)
+    for b in range(B):
+        for h, ss in enumerate(np.random.SeedSequence([seed + b, 7919]).spawn(H)):
+            rng = np.random.Generator(np.random.Philox(ss))
+            nu = rng.standard_normal((n_centers, d))
+            eps = rng.standard_normal((N, d))
+            v[b, h] = torch.from_numpy((nu[comp[b, h].numpy()] + noise_std * eps).astype(np.float32)).to(tdt)
+    return v
+
+
 def make_workload(w: dict, *, seed: int = 0, threads: int | None = None, H=None, N=None):
     """Inputs for a workload dict from ``workloads.WORKLOADS`` (optionally fewer heads/tokens)."""
     H = H or w["H"]

@@ -22,6 +22,10 @@ WORKLOADS = {
         B=1, H=40, N=75600, d=128, dtype="bf16", n_centers=64, grid=(21, 45, 80),
         q_scale=1.0, Cq=100, Ck=500, iters=5,
         sweep=[(0.04, 0.04), (0.08, 0.08), (0.16, 0.16), (0.32, 0.32)]),
+    # 84 latent frames (4x the 720p clip): the sequence-length scaling check
+    "wan14b_720p_84f": dict(
+        B=1, H=2, N=302400, d=128, dtype="bf16", n_centers=64, grid=(84, 45, 80),
+        q_scale=1.0, Cq=100, Ck=500, iters=5, sweep=[(0.08, 0.08)]),
     "wan14b_720p_stress_pq": dict(
         B=1, H=40, N=75600, d=128, dtype="bf16", n_centers=64, grid=(21, 45, 80),
         q_scale=0.2, zipf=1.2, Cq=100, Ck=500, iters=5, pq=(8, 256),

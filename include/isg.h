@@ -159,6 +159,24 @@ isg_status isg_select_sample(void *stream, const float *scores, const int32_t *k
                              float *sample_bias, int32_t *n_sample);
 
 /* ------------------------------------------------------------------------ */
+/* isg_select_sample_topp -- isg_select_sample with the exact set sized by mass.
+ * Pages: Paper Reading AI Learner page, abstract (the method wraps any
+ * block-sparse selector); thelatestinai.com page, Figure 2 (SVG2, whose
+ * selector keeps the smallest set of clusters reaching a probability mass).
+ * Exact set of query group i: non-empty key groups ordered by (pi_ij desc,
+ * j asc), taken one by one until the fp64 running sum of pi_ij, added in that
+ * order, reaches top_p (so the first is always taken; top_p >= the total mass
+ * takes every group).  The sample over the other groups is exactly that of
+ * isg_select_sample in ISG_SAMPLE_IMPORTANCE or ISG_SAMPLE_UNIFORM mode.
+ * pi device fp32 [B,H,Cq,Ck] as written by isg_probs; top_p finite, > 0;
+ * every other argument and output as for isg_select_sample. */
+isg_status isg_select_sample_topp(void *stream, const float *scores, const float *pi,
+                                  const int32_t *k_offsets, int B, int H, int Cq, int Ck, int N,
+                                  float top_p, int m, int mode, uint64_t seed, uint64_t call_id,
+                                  int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx,
+                                  float *sample_bias, int32_t *n_sample);
+
+/* ------------------------------------------------------------------------ */
 /* isg_attention -- one attention over the exact and sampled keys.
  * Pages: acceptodds.com page, abstract (the sample is computed together with
  * the top blocks in a single attention kernel, sampled scores reweighted to

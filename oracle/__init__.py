@@ -47,6 +47,8 @@ def _declare(L):
     L.orc_probs.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]
     L.orc_select_sample.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _u64, _u64,
                                     _p, _p, _p, _p, _p]
+    L.orc_select_sample_topp.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _u64, _u64,
+                                         _p, _p, _p, _p, _p]
     L.orc_attention.argtypes = [_p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                                 _i, _f, _p, _p, _p]
     L.orc_dense.argtypes = [_p, _p, _p, _i, _i, _i, _i, _f, _p, _i, _p, _p]
@@ -160,6 +162,23 @@ def select_sample(scores, k_offsets, N, exact_keys, m, mode=0, seed=0, call_id=0
     ns = np.zeros((B, H, Cq), np.int32)
     lib().orc_select_sample(_ptr(S), _ptr(ko), _ptr(vt), B, H, Cq, Ck, N, int(exact_keys), int(m),
                             int(mode), seed, call_id, _ptr(eg), _ptr(ne), _ptr(si), _ptr(sb), _ptr(ns))
+    return dict(exact_groups=eg, n_exact=ne, sample_idx=si, sample_bias=sb, n_sample=ns)
+
+
+def select_sample_topp(scores, pi, k_offsets, N, top_p, m, mode=0, seed=0, call_id=0):
+    """Exact set by the top-p rule (groups by pi desc until the running pi reaches top_p), then the sample."""
+    S = _c(scores, np.float32)
+    P = _c(pi, np.float32)
+    ko = _c(k_offsets, np.int32)
+    B, H, Cq, Ck = S.shape
+    eg = np.zeros((B, H, Cq, Ck), np.int32)
+    ne = np.zeros((B, H, Cq), np.int32)
+    mm = max(m, 1)
+    si = np.zeros((B, H, Cq, mm), np.int32)
+    sb = np.zeros((B, H, Cq, mm), np.float32)
+    ns = np.zeros((B, H, Cq), np.int32)
+    lib().orc_select_sample_topp(_ptr(S), _ptr(P), _ptr(ko), B, H, Cq, Ck, N, float(top_p), int(m), int(mode),
+                                 seed, call_id, _ptr(eg), _ptr(ne), _ptr(si), _ptr(sb), _ptr(ns))
     return dict(exact_groups=eg, n_exact=ne, sample_idx=si, sample_bias=sb, n_sample=ns)
 
 

@@ -238,7 +238,7 @@ void orc_probs(const float *cq, const float *ck, const int32_t *k_offsets, int B
  * key (seed, call_id) and counter (floor(t/2) + 1, i, h, b); words 2(t%2) and
  * 2(t%2)+1 form a 128-bit uniform r, z = floor(r T / 2^128). */
 static int g_cmp_mode;            /* set before qsort; qsort here is serial */
-static const float *g_cmp_S;
+static const float *g_cmp_S;      /* scores, or pi for the top-p rule */
 static const int32_t *g_cmp_V;
 static int cmp_rank(const void *a, const void *b)
 {
@@ -262,12 +262,17 @@ static uint64_t draw_z(uint64_t seed, uint64_t call_id, int b, int h, int i, int
     return (uint64_t)(a >> 64) + (uint64_t)(mid >> 64);
 }
 
-void orc_select_sample(const float *scores, const int32_t *k_offsets, const int32_t *votes,
-                       int B, int H, int Cq, int Ck, int N, int exact_keys, int m, int mode,
-                       uint64_t seed, uint64_t call_id, int32_t *exact_groups, int32_t *n_exact,
-                       int32_t *sample_idx, float *sample_bias, int32_t *n_sample)
+/* Exact set, then the sample.  Budget rule (pi == NULL), [B], [F3](c): groups by
+ * (S desc, j asc) -- (votes desc, S desc, j asc) in votes mode -- the first
+ * always, then while the running key count stays <= exact_keys.  Top-p rule
+ * (pi != NULL; the SVG2-style sizing that [B] allows, since the method wraps any
+ * block-sparse selector): groups by (pi desc, j asc), taken one by one until the
+ * fp64 running sum of pi, added in that order, reaches top_p. */
+static void select_core(const float *scores, const float *pi, double top_p, const int32_t *k_offsets,
+                        const int32_t *votes, int B, int H, int Cq, int Ck, int exact_keys, int m, int mode,
+                        uint64_t seed, uint64_t call_id, int32_t *exact_groups, int32_t *n_exact,
+                        int32_t *sample_idx, float *sample_bias, int32_t *n_sample)
 {
-    (void)N;
     uint32_t tbl[256];
     orc_proposal_table(tbl);
     int *order = (int *)malloc(sizeof(int) * Ck);
@@ -284,16 +289,26 @@ void orc_select_sample(const float *scores, const int32_t *k_offsets, const int3
             int n_ne = 0;
             for (int j = 0; j < Ck; ++j)
                 if (ko[j + 1] > ko[j]) order[n_ne++] = j;
-            g_cmp_mode = mode; g_cmp_S = S; g_cmp_V = votes ? votes + gi * Ck : NULL;
+            g_cmp_mode = mode; g_cmp_S = pi ? pi + gi * Ck : S; g_cmp_V = votes ? votes + gi * Ck : NULL;
             qsort(order, (size_t)n_ne, sizeof(int), cmp_rank);
             memset(taken, 0, sizeof(int) * Ck);
-            int64_t cum = 0;
-            for (int p = 0; p < n_ne; ++p) {
-                int j = order[p];
-                int nj = ko[j + 1] - ko[j];
-                if (p > 0 && cum + nj > exact_keys) break;
-                cum += nj;
-                taken[j] = 1;
+            if (pi) {
+                double mass = 0.0;
+                for (int p = 0; p < n_ne; ++p) {
+                    int j = order[p];
+                    taken[j] = 1;
+                    mass += (double)pi[gi * Ck + j];
+                    if (mass >= top_p) break;
+                }
+            } else {
+                int64_t cum = 0;
+                for (int p = 0; p < n_ne; ++p) {
+                    int j = order[p];
+                    int nj = ko[j + 1] - ko[j];
+                    if (p > 0 && cum + nj > exact_keys) break;
+                    cum += nj;
+                    taken[j] = 1;
+                }
             }
             int ne = 0;
             int32_t *eg = exact_groups + gi * Ck;
@@ -357,6 +372,26 @@ void orc_select_sample(const float *scores, const int32_t *k_offsets, const int3
         }
     }
     free(order); free(taken); free(W); free(U);
+}
+
+void orc_select_sample(const float *scores, const int32_t *k_offsets, const int32_t *votes,
+                       int B, int H, int Cq, int Ck, int N, int exact_keys, int m, int mode,
+                       uint64_t seed, uint64_t call_id, int32_t *exact_groups, int32_t *n_exact,
+                       int32_t *sample_idx, float *sample_bias, int32_t *n_sample)
+{
+    (void)N;
+    select_core(scores, NULL, 0.0, k_offsets, votes, B, H, Cq, Ck, exact_keys, m, mode, seed, call_id,
+                exact_groups, n_exact, sample_idx, sample_bias, n_sample);
+}
+
+void orc_select_sample_topp(const float *scores, const float *pi, const int32_t *k_offsets, int B, int H,
+                            int Cq, int Ck, int N, float top_p, int m, int mode, uint64_t seed,
+                            uint64_t call_id, int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx,
+                            float *sample_bias, int32_t *n_sample)
+{
+    (void)N;
+    select_core(scores, pi, (double)top_p, k_offsets, NULL, B, H, Cq, Ck, 0, m, mode, seed, call_id,
+                exact_groups, n_exact, sample_idx, sample_bias, n_sample);
 }
 
 /* ------------------------------------------------------------------------- */

@@ -97,6 +97,22 @@ def test_select_rejects(kw):
     assert _sel(**kw) == 1
 
 
+def _topp(**kw):
+    a = dict(S=FAKE, pi=FAKE, ko=FAKE, B=1, H=1, Cq=4, Ck=8, N=100, p=0.9, m=10, mode=0, eg=FAKE, ne=FAKE,
+             si=FAKE, sb=FAKE, ns=FAKE)
+    a.update(kw)
+    return isg.lib().isg_select_sample_topp(None, a["S"], a["pi"], a["ko"], a["B"], a["H"], a["Cq"], a["Ck"],
+                                            a["N"], a["p"], a["m"], a["mode"], C.c_uint64(0), C.c_uint64(0),
+                                            a["eg"], a["ne"], a["si"], a["sb"], a["ns"])
+
+
+@pytest.mark.parametrize("kw", [dict(pi=None), dict(S=None), dict(ns=None), dict(p=0.0), dict(p=-1.0),
+                                dict(p=float("nan")), dict(p=float("inf")), dict(m=101), dict(mode=2),
+                                dict(mode=3), dict(Ck=1025), dict(si=None)])
+def test_select_topp_rejects(kw):
+    assert _topp(**kw) == 1
+
+
 def test_select_allows_empty_sample_arrays_when_m_is_zero():
     # m = 0 with NULL sample arrays passes validation; a NULL stream with FAKE
     # pointers would launch, so only check that the NULL-array rule is m-dependent

@@ -336,7 +336,7 @@ def test_unbiased_over_1000_seeds_gpu(orc):
 
 
 # ------------------------------------------------------------------ full sizes, sampled checks
-def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode="importance"):
+def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode="importance", max_rows=None):
     w = WORKLOADS[name]
     N, d = w["N"], w["d"]
     say(f"full size {name}: generating inputs")
@@ -393,6 +393,8 @@ def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode
         gm = np.zeros((1, w["H"], Cq), np.uint8)
         sizes = np.diff(qo_all[0, h])
         nz = np.nonzero(sizes)[0]
+        if max_rows is not None:  # keep the oracle's share of the work bounded at long sequences
+            nz = nz[sizes[nz] <= max_rows]
         pick = [nz[np.argmax(sizes[nz])], nz[np.argmin(sizes[nz])]] + list(rng.choice(nz, groups_per_head - 2))
         gm[0, h, pick] = 1
         selo = {kk: npy(vv) for kk, vv in r["sel"].items() if kk != "m"}
@@ -508,3 +510,97 @@ def test_pipeline_votes_mode_vs_oracle(orc):
 
 def test_full_size_14b_720p_pq_votes(orc):
     _full_size_check(orc, "wan14b_720p_stress_pq", 0.08, 0.08, heads=[0, 39], groups_per_head=3, mode="votes")
+
+
+# ------------------------------------------------------------------ top-p exact-set sizing
+@pytest.mark.parametrize("p,m,mode", [(1e-6, 400, "importance"), (0.5, 400, "importance"), (0.9, 400, "uniform"),
+                                      (0.99, 300, "importance"), (1.0, 200, "importance"), (2.0, 100, "uniform"),
+                                      (0.9, 4096, "importance"), (0.7, 0, "importance")])
+def test_select_topp_bit_exact(orc, p, m, mode):
+    """Lists and samples of the top-p rule bit-exact against the oracle given the GPU's pi."""
+    say(f"select top-p p={p} m={m} mode={mode}")
+    (q, k, v), cq, ck = _clustered(2, 4096, 128, "bf16", 16, 64, zipf=1.2, q_scale=0.5)
+    scale = isg.default_scale(128)
+    S, pi = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale)
+    g = isg.isg_select_sample_topp(S, pi, ck["offsets"], 4096, p, m, mode=mode, seed=7, call_id=2)
+    o = orc.select_sample_topp(npy(S), npy(pi), npy(ck["offsets"]), 4096, p, m, mode=isg.MODES[mode], seed=7,
+                               call_id=2)
+    for key in ("exact_groups", "n_exact", "n_sample"):
+        assert np.array_equal(npy(g[key]), o[key]), key
+    ns = o["n_sample"]
+    for b in range(ns.shape[0]):
+        for h in range(ns.shape[1]):
+            for i in range(ns.shape[2]):
+                n = ns[b, h, i]
+                assert np.array_equal(npy(g["sample_idx"])[b, h, i, :n], o["sample_idx"][b, h, i, :n])
+                assert np.abs(npy(g["sample_bias"])[b, h, i, :n] - o["sample_bias"][b, h, i, :n]).max(
+                    initial=0) <= 1e-6
+
+
+def test_pipeline_topp_vs_oracle(orc):
+    """Top-p sizing end to end: lists from the GPU's pi, attention and un-permute against the oracle."""
+    H, N, d, Cq, Ck, m = 2, 4096, 128, 16, 64, 300
+    q, k, v = _inputs(H, N, d, "bf16", seed=19, q_scale=0.5, zipf=1.2)
+    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), Cq, Ck, 3, 0, m, top_p=0.8, seed=5)
+    torch.cuda.synchronize()
+    sel = orc.select_sample_topp(npy(r["scores"]), npy(r["pi"]), npy(r["ck"]["offsets"]), N, 0.8, m, seed=5)
+    for key in ("exact_groups", "n_exact", "n_sample", "sample_idx"):
+        assert np.array_equal(sel[key], npy(r["sel"][key])), key
+    o_p, lse_p = orc.attention(f32(r["cq"]["x_perm"]), f32(r["ck"]["x_perm"]), f32(r["ck"]["companion_perm"]),
+                               npy(r["cq"]["offsets"]), npy(r["ck"]["offsets"]), sel, m, r["scale"])
+    o, lse = orc.unpermute(o_p, lse_p, npy(r["cq"]["perm"]))
+    assert np.abs(f32(r["o"]) - o).max() <= 2e-2
+    assert np.abs(npy(r["lse"]) - lse).max() <= LSE_TOL_BF16
+
+
+# ------------------------------------------------------------------ error against density (trend checks)
+def _density_errors(orc, zipf, q_scale, seed=3):
+    """Relative L2 error of GPU calls against the oracle's dense rows (fp64), for
+    exact-only (E+S exact) and exact+importance / exact+uniform at matched density."""
+    from block_sparse_attention_means_amd.synth import structured_values
+    H, N, d, Cq, Ck = 2, 8192, 64, 16, 64
+    q, k, v, comp = make_qkv(H, N, d, n_centers=16, q_scale=q_scale, zipf=zipf, seed=seed, dtype="bf16")
+    v = structured_values(comp, d, n_centers=16, seed=seed, dtype="bf16")
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    scale = isg.default_scale(d)
+    cq = isg.isg_cluster(qg, Cq, 5)
+    ck = isg.isg_cluster(kg, Ck, 5, companion=vg)
+    S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+    rows = np.random.default_rng(1).choice(N, 128, replace=False)
+    od, _ = orc.dense(f32(q), f32(k), f32(v), scale, rows=rows)
+    out = {}
+    for share in (0.04, 0.08, 0.16):
+        E = budget_keys(share, N)
+        res = {}
+        for name, e2, m2, mode in (("exact_only", budget_keys(2 * share, N), 0, "importance"),
+                                   ("importance", E, E, "importance"), ("uniform", E, E, "uniform")):
+            errs = []
+            for s in range(1 if m2 == 0 else 3):
+                sel = isg.isg_select_sample(S, ck["offsets"], N, e2, m2, mode=mode, seed=s)
+                o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
+                                               ck["offsets"], sel, scale)
+                o, _ = isg.isg_unpermute(o_p, lse_p, cq["perm"])
+                og = f32(o)[:, :, rows]
+                errs.append(np.linalg.norm(og - od) / np.linalg.norm(od))
+            res[name] = float(np.mean(errs))
+        out[share] = res
+        say(f"  share {share}: " + ", ".join(f"{kk} {vv:.4f}" for kk, vv in res.items()))
+    return out
+
+
+@pytest.mark.parametrize("zipf,q_scale", [(None, 1.0), (1.2, 0.2)])
+def test_error_against_density_trends(orc, zipf, q_scale):
+    """With values that carry the keys' structure, exact + importance sample beats
+    exact-only at matched density (the unbiased estimate keeps the skipped region's
+    contribution), and its error falls as the budget grows."""
+    out = _density_errors(orc, zipf, q_scale)
+    shares = sorted(out)
+    for sh in shares:
+        assert out[sh]["importance"] < out[sh]["exact_only"], sh
+    assert out[shares[-1]]["importance"] < out[shares[0]]["importance"]
+
+
+def test_long_sequence_84_frames(orc):
+    """Sequence-length scaling: 84 latent frames (N = 302,400) at 8+8 %, checked like
+    the full-size cases (query groups of at most 1,500 rows go to the oracle)."""
+    _full_size_check(orc, "wan14b_720p_84f", 0.08, 0.08, heads=[0, 1], groups_per_head=3, max_rows=1500)

@@ -592,3 +592,58 @@ def test_pq_votes_brute_force(orc):
     # float rounding of the table path can reorder near-equal scores: demand near-total agreement
     assert (votes[0, 0] == want).mean() > 0.97
     assert np.all(votes[0, 0].sum(1) >= np.diff(qo))
+
+
+# ---------------------------------------------------------------- top-p exact-set sizing
+def test_topp_exact_set_brute_force(orc):
+    """Top-p rule against a direct Python evaluation: groups by (pi desc, j asc), taken
+    until the fp64 running sum of pi reaches p; the taken mass reaches p and dropping the
+    last taken group falls short of it (minimality); the first group is always taken."""
+    rng = np.random.default_rng(11)
+    B, H, Cq, Ck, N = 1, 2, 3, 40, 2000
+    q = rng.standard_normal((B, H, Cq, 16)).astype(np.float32)
+    k = rng.standard_normal((B, H, Ck, 16)).astype(np.float32)
+    sizes = rng.multinomial(N, rng.dirichlet(np.ones(Ck) * 0.5), size=(B, H))
+    sizes[0, 0, 5] = 0  # an empty group
+    ko = np.concatenate([np.zeros((B, H, 1), np.int64), np.cumsum(sizes, -1)], -1).astype(np.int32)
+    S, pi = orc.probs(q, k, ko, 0.7)
+    for p in (1e-6, 0.3, 0.8, 0.95, 0.999, 1.0, 2.0):
+        sel = orc.select_sample_topp(S, pi, ko, N, p, 0)
+        for h in range(H):
+            for i in range(Cq):
+                P = pi[0, h, i].astype(np.float64)
+                ne = [j for j in range(Ck) if sizes[0, h, j] > 0]
+                order = sorted(ne, key=lambda j: (-float(pi[0, h, i, j]), j))
+                want, mass = [], 0.0
+                for j in order:
+                    want.append(j)
+                    mass += float(pi[0, h, i, j])
+                    if mass >= p:
+                        break
+                got = sel["exact_groups"][0, h, i, :sel["n_exact"][0, h, i]].tolist()
+                assert got == sorted(want), (p, h, i)
+                assert order[0] in got
+                tm = sum(P[j] for j in got)
+                assert tm >= min(p, sum(P[j] for j in ne)) - 1e-12
+                if len(got) > 1:
+                    assert tm - P[want[-1]] < p
+
+
+def test_topp_one_reaches_dense_and_sample_covers_rest(orc):
+    """p = 1 (up to fp32 rounding of pi) keeps essentially every group; the sample then
+    draws only from groups outside the exact set, as in the budget rule."""
+    rng = np.random.default_rng(12)
+    N, d, Cq, Ck = 512, 16, 4, 12
+    x = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    cq = orc.cluster(x, Cq, 3)
+    ck = orc.cluster(x, Ck, 3)
+    S, pi = orc.probs(cq["centroids"], ck["centroids"], ck["offsets"], 0.25)
+    sel = orc.select_sample_topp(S, pi, ck["offsets"], N, 0.5, 300, seed=3)
+    ko = ck["offsets"][0, 0]
+    for i in range(Cq):
+        ex = set(sel["exact_groups"][0, 0, i, :sel["n_exact"][0, 0, i]].tolist())
+        grp = np.searchsorted(ko, sel["sample_idx"][0, 0, i, :sel["n_sample"][0, 0, i]], side="right") - 1
+        assert not (set(grp.tolist()) & ex)
+    full = orc.select_sample_topp(S, pi, ck["offsets"], N, 2.0, 0)
+    nonempty = int((np.diff(ko) > 0).sum())
+    assert (full["n_exact"] == nonempty).all()
