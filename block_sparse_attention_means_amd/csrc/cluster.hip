@@ -17,7 +17,9 @@ namespace {
 constexpr int kSortChunk = 1024;  // tokens per histogram / scatter chunk
 constexpr int kMaxC = 4096;
 constexpr int kAssignTile = 32;   // centroids per LDS tile in the assign kernel
-constexpr int kPieceRows = 256;   // rows per piece of the centroid update
+// Rows per piece of the centroid update: 16 rows for each of the work-group's row
+// slots (256 threads, d/8 per row), so 256 at d = 128 and 2048 at d = 16.
+__host__ __device__ constexpr int piece_rows(int d) { return 16 * (256 / (d / 8)); }
 
 struct Strides {
     int64_t b, h, t;
@@ -138,9 +140,9 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *labels, int N,
 }
 
 // hist[bh][chunk][c] -> first sorted row of (chunk, c); offsets = prefix of counts;
-// poff = prefix of the number of kPieceRows-row pieces of every group.
-__global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, int C, int32_t *offsets,
-                                                   int32_t *poff)
+// poff = prefix of the number of prow-row pieces of every group.
+__global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, int C, int prow,
+                                                   int32_t *offsets, int32_t *poff)
 {
     __shared__ int cnt[kMaxC];
     __shared__ int pcs[kMaxC];
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, i
             run += v;
         }
         cnt[c] = run;
-        pcs[c] = (run + kPieceRows - 1) / kPieceRows;
+        pcs[c] = (run + prow - 1) / prow;
     }
     __syncthreads();
     const int total = block_exclusive_scan_int(cnt, C, tmp);
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
 }
 
 // Centroid update in two passes, both in a fixed order: every group is cut into
-// pieces of kPieceRows sorted rows; a work-group sums one piece in fp64 (rows
+// pieces of piece_rows(D) sorted rows; a work-group sums one piece in fp64 (rows
 // strided over RP slots, then slot order) and the final pass adds the pieces of
 // each group in order and divides: c_j = mean of the rows of group j, rounded
 // to fp32 (an empty group keeps its centroid).
@@ -233,7 +235,8 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
     }
     const int j = lo;
     const int32_t *ob = offsets + (int64_t)bh * (C + 1);
-    const int r0 = ob[j] + (q - pb[j]) * kPieceRows, r1 = min(ob[j + 1], r0 + kPieceRows);
+    constexpr int PR = piece_rows(D);
+    const int r0 = ob[j] + (q - pb[j]) * PR, r1 = min(ob[j + 1], r0 + PR);
     const int rs = threadIdx.x / TPR, ck = threadIdx.x % TPR;
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const T *xb = x + b * xs.b + h * xs.h + ck * 8;
@@ -303,8 +306,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const T *x, Strides xs, con
 // token the four best candidates are kept; whenever a rival lies within
 // tau = 1e-4 (|x|^2 + max_j |c_j|^2) -- several times the worst-case error of the
 // split and of fp32 accumulation -- the decision is re-taken in fp64 with the
-// same unfused arithmetic as the exact definition (two or three candidates, or
-// every centroid when a fourth is also close), ties to the lower index.
+// same unfused arithmetic as the exact definition (the close candidates, or
+// every centroid when all kept candidates are close), ties to the lower index.
 constexpr int kCT = 32;  // centroids per MFMA tile
 
 // One wave per centroid: bf16 planes hi + lo and the squared norm (fp64 over the
@@ -341,10 +344,12 @@ __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent,
 // distance with the low bits replaced by the centroid index.  Positive floats
 // order like their bit patterns, so unsigned min/med3 on keys order by distance
 // (up to the dropped bits, a resolution of 2^bits ulps) and carry the index
-// along.  The four smallest keys are kept sorted: one min and three med3 per
-// candidate.
-struct Top4 {
-    uint32_t k1, k2, k3, k4;
+// along.  The K = 4 smallest keys are kept sorted: one min and K-1 med3 per
+// candidate.  (Two would halve the epilogue, but at d = 16 with 256 codewords
+// close pairs are common and each would cost a full rescan.)
+template <int K>
+struct TopK {
+    uint32_t k[K];
 };
 
 __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c)
@@ -352,16 +357,19 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c)
     return max(min(a, b), min(max(a, b), c));
 }
 
-__device__ __forceinline__ void top_insert(Top4 &t, uint32_t key)
+template <int K>
+__device__ __forceinline__ void top_insert(TopK<K> &t, uint32_t key)
 {
-    const uint32_t n4 = umed3(t.k3, t.k4, key);
-    const uint32_t n3 = umed3(t.k2, t.k3, key);
-    const uint32_t n2 = umed3(t.k1, t.k2, key);
-    t.k1 = min(t.k1, key);
-    t.k2 = n2;
-    t.k3 = n3;
-    t.k4 = n4;
+    uint32_t n[K];
+#pragma unroll
+    for (int i = K - 1; i >= 1; --i) n[i] = umed3(t.k[i - 1], t.k[i], key);
+    n[0] = min(t.k[0], key);
+#pragma unroll
+    for (int i = 0; i < K; ++i) t.k[i] = n[i];
 }
+
+template <int D>
+constexpr int topk_of() { return 4; }
 
 // fp64 partial sum of (x_k - c_k)^2 over the DPL dims of one lane (x bf16, c fp32;
 // both 8/16-byte aligned at these offsets).
@@ -446,7 +454,8 @@ __device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, 
 // MFMA, then every (token, centroid) key into the token's top three.
 template <int D>
 __device__ __forceinline__ void assign_tile(const uint8_t *cur, const float *ncur, int tile, const bf16x8 (*xf)[D / 16],
-                                            const float *xn1, uint32_t hi_mask, Top4 *top, int hl, int l32)
+                                            const float *xn1, uint32_t hi_mask, TopK<topk_of<D>()> *top, int hl,
+                                            int l32)
 {
     constexpr int NDS = D / 16;
     f32x16 acc[2];
@@ -520,9 +529,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     while ((1 << ibits) < Cpad) ++ibits;
     const uint32_t imask = (1u << ibits) - 1u, hi_mask = ~imask;
     const float xn1[2] = {xn[0] + 1.0f, xn[1] + 1.0f};
-    Top4 top[2];
+    constexpr int TK = topk_of<D>();
+    TopK<TK> top[2];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) top[tb] = Top4{0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int c = 0; c < TK; ++c) top[tb].k[c] = 0xFFFFFFFFu;
 
     // largest centroid norm of the head (for the decision window)
     __shared__ float cm_part[4];
@@ -579,38 +591,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     int qpos[2] = {0, 0}, qcnt[2] = {0, 0}, fpos[2] = {-1, -1};
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-        Top4 &T = top[tb];
-        const uint32_t o1 = __shfl_xor(T.k1, 32), o2 = __shfl_xor(T.k2, 32), o3 = __shfl_xor(T.k3, 32),
-                       o4 = __shfl_xor(T.k4, 32);
-        top_insert(T, o1);
-        top_insert(T, o2);
-        top_insert(T, o3);
-        top_insert(T, o4);
+        TopK<TK> &T = top[tb];
+        uint32_t other[TK];
+#pragma unroll
+        for (int c = 0; c < TK; ++c) other[c] = __shfl_xor(T.k[c], 32);
+#pragma unroll
+        for (int c = 0; c < TK; ++c) top_insert(T, other[c]);
         if (hl != 0 || tok[tb] >= N) continue;
         // window: tau plus the key resolution (2^ibits ulps of the largest value compared)
         const float tau = 1e-4f * (xn[tb] + cm);
-        const float d1 = __uint_as_float(T.k1 & hi_mask);
+        const float d1 = __uint_as_float(T.k[0] & hi_mask);
         const float lim0 = d1 + tau;
         const float res = __uint_as_float((__float_as_uint(lim0) & 0x7F800000u)) * ldexpf(1.0f, ibits - 23);
         const float lim = lim0 + 2.0f * res;
         const int slot = wave * 64 + tb * 32 + l32;
-        const float d2 = __uint_as_float(T.k2 & hi_mask);
-        const float d3 = __uint_as_float(T.k3 & hi_mask);
-        const float d4 = __uint_as_float(T.k4 & hi_mask);
-        if (d4 < lim) {  // four or more close candidates: every centroid in fp64
+        int n = 1;
+#pragma unroll
+        for (int c = 1; c < TK; ++c) n += __uint_as_float(T.k[c] & hi_mask) < lim;
+        if (n == TK) {  // every kept candidate is close: all centroids in fp64
             const int f = atomicAdd(&full_n, 1);
             full_slot[f] = slot;
             fpos[tb] = f;
-        } else {
-            const int n = 1 + (d2 < lim) + (d3 < lim);
-            if (n > 1) {
-                const int pos = atomicAdd(&rq_n, n);
-                rq_slot[pos] = slot; rq_cand[pos] = (int)(T.k1 & imask);
-                rq_slot[pos + 1] = slot; rq_cand[pos + 1] = (int)(T.k2 & imask);
-                if (n > 2) { rq_slot[pos + 2] = slot; rq_cand[pos + 2] = (int)(T.k3 & imask); }
-                qpos[tb] = pos;
-                qcnt[tb] = n;
-            }
+        } else if (n > 1) {
+            const int pos = atomicAdd(&rq_n, n);
+#pragma unroll
+            for (int c = 0; c < TK - 1; ++c)
+                if (c < n) {
+                    rq_slot[pos + c] = slot;
+                    rq_cand[pos + c] = (int)(T.k[c] & imask);
+                }
+            qpos[tb] = pos;
+            qcnt[tb] = n;
         }
     }
     __syncthreads();
@@ -650,7 +661,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int tb = 0; tb < 2; ++tb) {
         const int t = tok[tb];
         if (hl != 0 || t >= N) continue;
-        int best = (int)(top[tb].k1 & imask);
+        int best = (int)(top[tb].k[0] & imask);
         if (fpos[tb] >= 0) {
             best = full_best[fpos[tb]];
         } else if (qcnt[tb] > 1) {
@@ -677,7 +688,7 @@ ClusterWs cluster_ws(int B, int H, int N, int d, int C)
     const size_t BH = (size_t)B * H;
     const size_t nchunks = ((size_t)N + kSortChunk - 1) / kSortChunk;
     w.Cpad = (C + kCT - 1) / kCT * kCT;
-    w.maxp = (N + kPieceRows - 1) / kPieceRows + C;  // >= sum over groups of ceil(n_j / kPieceRows)
+    w.maxp = (N + piece_rows(d) - 1) / piece_rows(d) + C;  // >= sum over groups of ceil(n_j / piece rows)
     size_t o = 0;
     w.off_hist = o; o += isg_align256(BH * nchunks * C * sizeof(int32_t));
     w.off_planes = o; o += isg_align256(BH * 2 * w.Cpad * d * sizeof(uint16_t));
@@ -725,7 +736,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     for (int it = 0; it < iters; ++it) {
         launch_assign<T, D>(st, x, xs, B, H, N, C, cent, labels, ws, w);
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
-        scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, offsets, poff);
+        scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, piece_rows(D), offsets, poff);
         scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, N, C, nchunks, bits, perm);
         update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
                                                                     partial);

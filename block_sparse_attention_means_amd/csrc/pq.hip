@@ -74,6 +74,39 @@ __global__ __launch_bounds__(256) void pq_tables_kernel(const float *q_cb, const
     tables[(((int64_t)bh * P + s) * Cc + a) * Ck + j] = __fmul_rn(acc, scale);
 }
 
+// The same tables for subspaces of at most 32 dims: a thread keeps its key group's
+// Kbar slice in registers and walks the codewords, staged 64 at a time in LDS, so
+// every Kbar element is read once and the table rows are written coalesced.
+template <int DS>
+__global__ __launch_bounds__(256) void pq_tables_tiled_kernel(const float *q_cb, const float *kbar, int B, int H,
+                                                              int P, int Cc, int Ck, float scale, float *tables)
+{
+    constexpr int AT = 64;  // codewords per LDS tile
+    __shared__ float cws[AT][DS];
+    const int s = blockIdx.y, bh = blockIdx.z, b = bh / H, h = bh % H;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    const int d = P * DS;
+    float kb[DS];
+#pragma unroll
+    for (int e = 0; e < DS; ++e) kb[e] = j < Ck ? kbar[((int64_t)bh * Ck + j) * d + s * DS + e] : 0.0f;
+    const float *cwb = q_cb + (((int64_t)s * B + b) * H + h) * (int64_t)Cc * DS;
+    float *out = tables + ((int64_t)bh * P + s) * (int64_t)Cc * Ck;
+    for (int a0 = 0; a0 < Cc; a0 += AT) {
+        const int na = min(AT, Cc - a0);
+        __syncthreads();
+        for (int x = threadIdx.x; x < na * DS; x += 256) cws[x / DS][x % DS] = cwb[(int64_t)a0 * DS + x];
+        __syncthreads();
+        if (j < Ck) {
+            for (int a = 0; a < na; ++a) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int e = 0; e < DS; ++e) acc = __fmaf_rn(cws[a][e], kb[e], acc);
+                out[(int64_t)(a0 + a) * Ck + j] = __fmul_rn(acc, scale);
+            }
+        }
+    }
+}
+
 // Order-preserving bits of a float (+0 and -0 map to the same key).
 __device__ __forceinline__ uint32_t orderable(float f)
 {
@@ -92,11 +125,15 @@ __device__ __forceinline__ int wave_sum(int v)
            __builtin_amdgcn_readlane(v, 47) + __builtin_amdgcn_readlane(v, 63);
 }
 
-// One wave per query; lane owns key groups j = k*64 + lane, k < KPL.  Four waves
-// per block share a query group; logical blocks are laid out so that one XCD
-// works on consecutive query groups of the same head (its tables stay in L2).
+// One wave per query; lane owns key groups j = k*64 + lane, k < KPL.  The 16
+// waves of a block share a query group, and logical blocks are laid out so that
+// one XCD works on consecutive query groups of the same head: with 16-wave
+// blocks an XCD holds well under one head's groups at a time, so the head's
+// tables (P*Cc*Ck fp32, 4 MB at 8 x 256 x 500) stay in its L2.
+constexpr int kVoteWaves = 16;
+
 template <int KPL>
-__global__ __launch_bounds__(256) void pq_votes_kernel(const int32_t *q_codes, const float *tables,
+__global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t *q_codes, const float *tables,
                                                        const int32_t *perm_q, const int32_t *q_offsets,
                                                        const int32_t *k_offsets, int B, int H, int N, int P,
                                                        int Cc, int Cq, int Ck, int exact_keys, int nblocks,
@@ -111,7 +148,7 @@ __global__ __launch_bounds__(256) void pq_votes_kernel(const int32_t *q_codes, c
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int32_t *ko = k_offsets + (int64_t)bh * (Ck + 1);
-    for (int j = tid; j < KPL * 64; j += 256) {
+    for (int j = tid; j < KPL * 64; j += 64 * kVoteWaves) {
         cnt[j] = 0;
         nsz[j] = j < Ck ? ko[j + 1] - ko[j] : 0;
     }
@@ -129,7 +166,7 @@ __global__ __launch_bounds__(256) void pq_votes_kernel(const int32_t *q_codes, c
     const int32_t *qo = q_offsets + (int64_t)bh * (Cq + 1);
     const float *tb = tables + (int64_t)bh * P * Cc * Ck;
     const int r_end = qo[i + 1];
-    for (int r = qo[i] + wave; r < r_end; r += 4) {
+    for (int r = qo[i] + wave; r < r_end; r += kVoteWaves) {
         if (total <= E) {  // every non-empty group fits
 #pragma unroll
             for (int k = 0; k < KPL; ++k) vk[k] += nk[k] > 0;
@@ -198,7 +235,7 @@ __global__ __launch_bounds__(256) void pq_votes_kernel(const int32_t *q_codes, c
     for (int k = 0; k < KPL; ++k)
         if (vk[k]) atomicAdd(&cnt[k * 64 + lane], vk[k]);
     __syncthreads();
-    for (int j = tid; j < Ck; j += 256) votes[((int64_t)bh * Cq + i) * Ck + j] = cnt[j];
+    for (int j = tid; j < Ck; j += 64 * kVoteWaves) votes[((int64_t)bh * Cq + i) * Ck + j] = cnt[j];
 }
 
 template <int KPL>
@@ -208,7 +245,7 @@ void launch_votes(hipStream_t st, const int32_t *q_codes, const float *tables, c
 {
     const int nblocks = B * H * Cq;
     const int nb8 = (nblocks + 7) & ~7;
-    pq_votes_kernel<KPL><<<nb8, 256, 0, st>>>(q_codes, tables, perm_q, q_offsets, k_offsets, B, H, N, P, Cc, Cq,
+    pq_votes_kernel<KPL><<<nb8, 64 * kVoteWaves, 0, st>>>(q_codes, tables, perm_q, q_offsets, k_offsets, B, H, N, P, Cc, Cq,
                                               Ck, E, nblocks, votes);
 }
 
@@ -239,8 +276,16 @@ extern "C" isg_status isg_pq_votes(void *stream, const int32_t *q_codes, const f
     const int kthreads = (d + 63) & ~63;
     pq_kbar_kernel<<<dim3(Ck, (unsigned)BH), kthreads, 0, st>>>(k_codes, k_codebooks, perm_k, k_offsets, B, H, N, P,
                                                                Cc, ds, Ck, kbar);
-    pq_tables_kernel<<<dim3((Ck + 255) / 256, P * Cc, (unsigned)BH), 256, 0, st>>>(q_codebooks, kbar, B, H, P, Cc,
-                                                                                  ds, Ck, scale, tables);
+    const dim3 tgrid((Ck + 255) / 256, P, (unsigned)BH);
+    if (ds == 16)
+        pq_tables_tiled_kernel<16><<<tgrid, 256, 0, st>>>(q_codebooks, kbar, B, H, P, Cc, Ck, scale, tables);
+    else if (ds == 8)
+        pq_tables_tiled_kernel<8><<<tgrid, 256, 0, st>>>(q_codebooks, kbar, B, H, P, Cc, Ck, scale, tables);
+    else if (ds == 32)
+        pq_tables_tiled_kernel<32><<<tgrid, 256, 0, st>>>(q_codebooks, kbar, B, H, P, Cc, Ck, scale, tables);
+    else
+        pq_tables_kernel<<<dim3((Ck + 255) / 256, P * Cc, (unsigned)BH), 256, 0, st>>>(q_codebooks, kbar, B, H, P,
+                                                                                      Cc, ds, Ck, scale, tables);
     if (Ck <= 64)
         launch_votes<1>(st, q_codes, tables, perm_q, q_offsets, k_offsets, B, H, N, P, Cc, Cq, Ck, exact_keys, votes);
     else if (Ck <= 128)

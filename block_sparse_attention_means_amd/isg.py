@@ -239,7 +239,9 @@ def isg_unpermute(o_p, lse_p, perm_q, *, out=None, lse_out=None, stream=None):
 
 def pq_codebooks(x, P, Cc, iters, *, stream=None):
     """Product-quantisation codes [P,B,H,N] and codebooks [P,B,H,Cc,d/P] of x [B,H,N,d]:
-    one isg_cluster call per subspace, on a strided view, writing in place."""
+    k-means of every d/P-dim subspace through strided views, writing in place.  With
+    B = 1 the subspaces are the batch dimension of one isg_cluster call (batch stride
+    d/P elements); otherwise one call per subspace."""
     _dev(x, "x")
     B, H, N, d = x.shape
     if x.stride(3) != 1 or d % P:
@@ -248,6 +250,15 @@ def pq_codebooks(x, P, Cc, iters, *, stream=None):
     dev = x.device
     codes = torch.empty((P, B, H, N), device=dev, dtype=torch.int32)
     cbs = torch.empty((P, B, H, Cc, ds), device=dev, dtype=torch.float32)
+    if B == 1:
+        perm = torch.empty((P, H, N), device=dev, dtype=torch.int32)
+        offsets = torch.empty((P, H, Cc + 1), device=dev, dtype=torch.int32)
+        ws = torch.empty(max(cluster_workspace_size(P, H, N, ds, Cc), 1), device=dev, dtype=torch.uint8)
+        st = lib().isg_cluster(_stream(stream), _ptr(x), _dtype(x), _i64x3((ds, x.stride(1), x.stride(2))), P, H, N,
+                               ds, Cc, iters, 0, None, _ptr(cbs), _ptr(codes), _ptr(perm), _ptr(offsets), None,
+                               None, _ptr(ws), ws.numel())
+        _check(st, "isg_cluster (subspaces)")
+        return codes, cbs
     perm = torch.empty((B, H, N), device=dev, dtype=torch.int32)
     offsets = torch.empty((B, H, Cc + 1), device=dev, dtype=torch.int32)
     ws = torch.empty(max(cluster_workspace_size(B, H, N, ds, Cc), 1), device=dev, dtype=torch.uint8)

@@ -604,3 +604,22 @@ def test_long_sequence_84_frames(orc):
     """Sequence-length scaling: 84 latent frames (N = 302,400) at 8+8 %, checked like
     the full-size cases (query groups of at most 1,500 rows go to the oracle)."""
     _full_size_check(orc, "wan14b_720p_84f", 0.08, 0.08, heads=[0, 1], groups_per_head=3, max_rows=1500)
+
+
+@pytest.mark.parametrize("P,Cc", [(16, 32), (2, 64), (4, 300)])
+def test_pq_votes_other_subspace_widths(orc, P, Cc):
+    """Subspace widths 8, 64 and 32 dims (random codes and codebooks): Kbar, tables and
+    votes bit-exact, through both table kernels."""
+    H, N, d, Cq, Ck, E = 2, 3000, 128, 10, 80, 250
+    say(f"pq votes P={P} Cc={Cc}")
+    (q, k, v), cq, ck = _clustered(H, N, d, "bf16", Cq, Ck, seed=P)
+    rng = np.random.default_rng(P)
+    ds = d // P
+    qc = torch.from_numpy(rng.integers(0, Cc, (P, 1, H, N)).astype(np.int32)).to(DEV)
+    kc = torch.from_numpy(rng.integers(0, Cc, (P, 1, H, N)).astype(np.int32)).to(DEV)
+    qcb = torch.from_numpy(rng.standard_normal((P, 1, H, Cc, ds)).astype(np.float32)).to(DEV)
+    kcb = torch.from_numpy(rng.standard_normal((P, 1, H, Cc, ds)).astype(np.float32)).to(DEV)
+    g, kbar, tables, votes = _pq_stage(orc, qc, qcb, kc, kcb, cq, ck, E, isg.default_scale(d))
+    assert np.array_equal(npy(g["kbar"]), kbar)
+    assert np.array_equal(npy(g["tables"]), tables)
+    assert np.array_equal(npy(g["votes"]), votes)
