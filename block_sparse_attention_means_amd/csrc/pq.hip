@@ -125,12 +125,13 @@ __device__ __forceinline__ int wave_sum(int v)
            __builtin_amdgcn_readlane(v, 47) + __builtin_amdgcn_readlane(v, 63);
 }
 
-// One wave per query; lane owns key groups j = k*64 + lane, k < KPL.  The 16
+// One wave per query; lane owns key groups j = k*64 + lane, k < KPL.  The 8
 // waves of a block share a query group, and logical blocks are laid out so that
-// one XCD works on consecutive query groups of the same head: with 16-wave
-// blocks an XCD holds well under one head's groups at a time, so the head's
-// tables (P*Cc*Ck fp32, 4 MB at 8 x 256 x 500) stay in its L2.
-constexpr int kVoteWaves = 16;
+// one XCD works on consecutive query groups of the same head: an XCD then holds
+// about one head's groups at a time, so the head's tables (P*Cc*Ck fp32, 4 MB at
+// 8 x 256 x 500) stay in its L2.
+constexpr int kVoteWaves = 8;
+constexpr int kPBatch = 8;  // subspaces whose table rows are in flight together
 
 template <int KPL>
 __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t *q_codes, const float *tables,
@@ -166,22 +167,53 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
     const int32_t *qo = q_offsets + (int64_t)bh * (Cq + 1);
     const float *tb = tables + (int64_t)bh * P * Cc * Ck;
     const int r_end = qo[i + 1];
-    for (int r = qo[i] + wave; r < r_end; r += kVoteWaves) {
-        if (total <= E) {  // every non-empty group fits
+    if (total <= E) {  // every non-empty group fits every query's budget
+        for (int r = qo[i] + wave; r < r_end; r += kVoteWaves)
 #pragma unroll
             for (int k = 0; k < KPL; ++k) vk[k] += nk[k] > 0;
-            continue;
-        }
+    }
+    const int32_t *qcode = q_codes + ((int64_t)b * H + h) * N;  // + s*B*H*N + t
+    const int64_t sstride = (int64_t)B * H * N;
+    // codes of the next query are fetched while the current one runs its bisection
+    int codes[kPBatch];
+    int r = qo[i] + wave;
+    if (total > E && r < r_end) {
         const int t = perm_q[(int64_t)bh * N + r];
+#pragma unroll
+        for (int s = 0; s < kPBatch; ++s) codes[s] = s < P ? qcode[s * sstride + t] : 0;
+    }
+    for (; total > E && r < r_end; r += kVoteWaves) {
+        // this query's table rows, all issued before any is added (rows of the
+        // first kPBatch subspaces; further subspaces in batches of kPBatch)
         float sc[KPL];
 #pragma unroll
         for (int k = 0; k < KPL; ++k) sc[k] = 0.0f;
-        for (int s = 0; s < P; ++s) {
-            const int code = q_codes[(((int64_t)s * B + b) * H + h) * N + t];
-            const float *row = tb + ((int64_t)s * Cc + code) * Ck + lane;
+        for (int s0 = 0; s0 < P; s0 += kPBatch) {
+            if (s0 > 0) {
+                const int t = perm_q[(int64_t)bh * N + r];
 #pragma unroll
-            for (int k = 0; k < KPL; ++k)
-                if (k * 64 + lane < Ck) sc[k] = __fadd_rn(sc[k], row[k * 64]);
+                for (int s = 0; s < kPBatch; ++s) codes[s] = s0 + s < P ? qcode[(s0 + s) * sstride + t] : 0;
+            }
+            float rv[kPBatch][KPL];
+#pragma unroll
+            for (int s = 0; s < kPBatch; ++s) {
+                const float *row = tb + ((int64_t)(s0 + s) * Cc + codes[s]) * Ck + lane;
+#pragma unroll
+                for (int k = 0; k < KPL; ++k)
+                    rv[s][k] = (s0 + s < P && k * 64 + lane < Ck) ? row[k * 64] : 0.0f;
+            }
+#pragma unroll
+            for (int s = 0; s < kPBatch; ++s)
+                if (s0 + s < P) {
+#pragma unroll
+                    for (int k = 0; k < KPL; ++k)
+                        if (k * 64 + lane < Ck) sc[k] = __fadd_rn(sc[k], rv[s][k]);
+                }
+        }
+        if (r + kVoteWaves < r_end) {
+            const int tn = perm_q[(int64_t)bh * N + r + kVoteWaves];
+#pragma unroll
+            for (int s = 0; s < kPBatch; ++s) codes[s] = s < P ? qcode[s * sstride + tn] : 0;
         }
         uint32_t ok[KPL];
 #pragma unroll
