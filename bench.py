@@ -157,7 +157,8 @@ def cpu_baseline(w, q, k, v, E, m, seed, mode="importance", top_p=None):
     work = nq * cols
     threads = oracle.num_threads()
     order = np.argsort(-work)
-    pick = [i for i in order if work[i] > 0][:max(1, min(threads, Cq))]
+    # three query groups per host thread: about 10-20 s of oracle attention on the box
+    pick = [i for i in order if work[i] > 0][:max(1, min(3 * threads, Cq))]
     gm = np.zeros((1, 1, Cq), np.uint8)
     gm[0, 0, pick] = 1
     t1 = time.perf_counter()
