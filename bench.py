@@ -443,7 +443,7 @@ def main():
                      "traffic": measured_traffic(args.workload, args.exact, args.sample),
                      "traffic_unit": "bytes per launch (FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0)",
                      "algorithmic_bytes": abytes,
-                     "kernel": "isg_attention: attn_bf16_kernel with its key-norm, column-list and tile-table prep"},
+                     "kernel": "isg_attention: attn_pp_kernel with its key-norm, column-list and tile-table prep"},
     }
     if args.sweep:
         sweep = {}

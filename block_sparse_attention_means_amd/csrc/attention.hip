@@ -8,17 +8,25 @@
 //
 // Structure:
 //   1. columns_kernel   per query group: the column list (row of K_p/V_p, offset
-//                       in log2 units) = rows of the exact groups in ascending
-//                       group order, then the samples, padded to a multiple of
-//                       64 with offset -inf.
+//                       in score units, i.e. divided by the softmax scale, so it
+//                       can start the K Q^T accumulator) = rows of the exact
+//                       groups in ascending group order (offset 0), then the
+//                       samples, padded to a multiple of 64 with offset -inf.
 //   2. tile_table_kernel per head: (group, first row, end row) of every 128-row
 //                       query tile; the launch walks tiles in an XCD-aware order
 //                       so the tiles of one group share an L2.
-//   3. attn_bf16_kernel 4 waves x 32 query rows; K/V tiles of 64 columns are
-//                       gathered row by row straight into LDS (double buffered);
-//                       S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16
-//                       so each lane owns one query and the softmax weights stay
-//                       in registers; V is read through the LDS transpose read.
+//   3. attn_pp_kernel   (d = 128) two 128-row query tiles per work-group of 8
+//                       waves, run one slot apart so that on each SIMD one wave
+//                       issues matrix products while the other computes weights;
+//                       K/V tiles of 64 columns are gathered row by row straight
+//                       into LDS; S^T = K Q^T and O^T += V^T P^T on
+//                       v_mfma_f32_32x32x16_bf16 so each lane owns one query and
+//                       the weights stay in registers; V is read through the LDS
+//                       transpose read.  All weights use one fixed reference per
+//                       query; tiles whose row sums underflow are flagged.
+//      attn_bf16_kernel 4 waves x 32 query rows, one tile per work-group, the
+//                       same products: the fast kernel for d = 64, and (with a
+//                       running maximum) the fallback for flagged tiles.
 //      attn_f32_kernel  fp32 inputs: plain VALU version of the same loop.
 #include <algorithm>
 #include <cmath>
@@ -43,7 +51,7 @@ constexpr int kQB = 1;
 __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, const int32_t *exact_groups,
                                                       const int32_t *n_exact, const int32_t *sample_idx,
                                                       const float *sample_bias, const int32_t *n_sample,
-                                                      int Cq, int Ck, int m, int64_t cap, int32_t *col_row,
+                                                      int Cq, int Ck, int m, float scale, int64_t cap, int32_t *col_row,
                                                       float *col_bias, int32_t *col_len, int32_t *col_x,
                                                       float *col_bmax)
 {
@@ -82,8 +90,8 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
             bias = 0.0f;
         } else if (c < L) {
             row = si[c - X];
-            bias = sb[c - X] * kLog2e;
-            bmax = fmaxf(bmax, bias);
+            bias = sb[c - X] / scale;
+            bmax = fmaxf(bmax, sb[c - X] * kLog2e);
         }
         cr[c] = row;
         cb[c] = bias;
@@ -174,17 +182,26 @@ __device__ __forceinline__ int kswz(int row, int chunk)
     return row * CPR + (chunk ^ (row & (CPR - 1)));
 }
 
-// V tile in LDS: row-major (key rows of D elements); the 16-byte chunks of row r
-// are XOR-swizzled by 2 (r mod 4).  The P.V product reads it with the LDS
-// transpose read (ds_read_b64_tr_b16): inside each group of 16 lanes, lane j
-// supplies the address of 4 elements of key row k0 + j/4 at column d0 + 4 (j mod 4),
-// and lane i receives column d0 + i of the four rows k0 .. k0+3.  Four consecutive
-// rows at one chunk pair then cover 8 distinct 16-byte bank slots.
+// V tile in LDS: row-major (key rows of D elements) with the 16-byte chunks of each
+// row XOR-swizzled.  The P.V product reads it with the LDS transpose read
+// (ds_read_b64_tr_b16): inside each group of 16 lanes, lane j supplies the address
+// of 4 elements of key row k0 + j/4 at column d0 + 4 (j mod 4), and lane i
+// receives column d0 + i of the four rows k0 .. k0+3.  The 32 lanes that share a
+// cycle read 4 rows x 4 consecutive chunks; the swizzle puts those 16 chunks in
+// 16 distinct 16-byte bank slots (a 256-byte bank cycle): rows r mod 4 move by
+// 4 r chunks for D = 128 (16 chunks a row); for D = 64 (8 chunks, so two rows
+// share a bank cycle) rows 2 and 3 of each group of 4 move by 4.
+template <int D>
+__device__ __forceinline__ int vswz_mask(int row)
+{
+    return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 template <int D>
 __device__ __forceinline__ int vswz(int row, int chunk)
 {
     constexpr int CPR = D / 8;
-    return row * CPR + (chunk ^ (2 * (row & 3)));
+    return row * CPR + (chunk ^ vswz_mask<D>(row));
 }
 
 // Tile rows go straight from memory into LDS (global_load_lds_dwordx4: lane l of a
@@ -201,10 +218,56 @@ __device__ __forceinline__ void tile_direct(uint8_t *buf, const uint8_t *base, c
         const int blk = it * NW + wave;  // 64-chunk (1 KB) block of the tile
         const int P = blk * 64 + lane;
         const int row = P / CPR;
-        const int c = ISV ? (P % CPR) ^ (2 * (row & 3)) : (P % CPR) ^ (row & (CPR - 1));
+        const int c = ISV ? (P % CPR) ^ vswz_mask<D>(row) : (P % CPR) ^ (row & (CPR - 1));
         const uint16_t *src = reinterpret_cast<const uint16_t *>(base) + (uint32_t)rows[row] * (uint32_t)D + (uint32_t)(c * 8);
         __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
                                          (void __attribute__((address_space(3))) *)(buf + blk * 1024), 16, 0, 0);
+    }
+}
+
+// Split form of tile_direct for the ping-pong kernel.  tile_rows reads the row
+// indices of this wave's chunks (for a tile past the end of the column list the
+// caller passes a row of zeros: the instruction count stays fixed); tile_issue
+// then starts the loads, addressed as a uniform base plus a 32-bit byte offset.
+// Reading the indices of both tiles before issuing any load lets one LDS wait
+// cover all of them.  The LDS destination is hidden from the compiler:
+// it then does not tie these loads to a buffer and inserts no waits before reads
+// of the other buffers -- the caller's own waits and barriers order every read
+// after the load that fills it.
+template <int D, int NW>
+struct TileRows {
+    static constexpr int ROUNDS = kTK * (D / 8) / (64 * NW);
+    uint32_t r[ROUNDS];
+};
+
+template <int D, int NW>
+__device__ __forceinline__ TileRows<D, NW> tile_rows(const int *rows, int wave, int lane)
+{
+    constexpr int CPR = D / 8;
+    TileRows<D, NW> t;
+#pragma unroll
+    for (int it = 0; it < TileRows<D, NW>::ROUNDS; ++it) {
+        const int P = (it * NW + wave) * 64 + lane;
+        t.r[it] = (uint32_t)rows[P / CPR];
+    }
+    return t;
+}
+
+template <int D, int NW, bool ISV>
+__device__ __forceinline__ void tile_issue(uint8_t *buf, const uint8_t *base, const TileRows<D, NW> &t, int wave,
+                                           int lane)
+{
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int it = 0; it < TileRows<D, NW>::ROUNDS; ++it) {
+        const int blk = it * NW + wave;
+        const int P = blk * 64 + lane;
+        const int row = P / CPR;
+        const int c = ISV ? (P % CPR) ^ vswz_mask<D>(row) : (P % CPR) ^ (row & (CPR - 1));
+        const uint8_t *src = base + (t.r[it] * (uint32_t)(2 * D) + (uint32_t)(c * 16));
+        auto *dst = (void __attribute__((address_space(3))) *)(buf + blk * 1024);
+        asm volatile("" : "+s"(dst));
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src, dst, 16, 0, 0);
     }
 }
 
@@ -253,13 +316,23 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
         nbias = cbias[(int64_t)(t + 2) * kTK + lane];
     }
     if (wave_active) {
+        // The K Q^T accumulator starts at the column offsets (score units): lane
+        // holds keys k2*32 + 8g + 4hl + e (e = 0..3) of its query.  Tiles of exact
+        // columns only have offset 0.
+        const int slot = t % 3;
+        const bool exact_tile = (t + 1) * kTK <= X;
         f32x16 sacc[QB][2];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 bv = exact_tile ? f32x4{0.0f, 0.0f, 0.0f, 0.0f}
+                                            : *reinterpret_cast<const f32x4 *>(&idx_bias[slot][k2 * 32 + g * 8 + hl * 4]);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sacc[qb][k2][r] = 0.0f;
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sacc[qb][k2][4 * g + e] = bv[e];
+            }
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
@@ -273,25 +346,8 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
             }
         }
         __builtin_amdgcn_s_setprio(0);
-        // Logits in log2 units; lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of
-        // its query.  Exact tiles keep raw scores (cf = scale log2 e); tiles with
-        // sampled or padded columns get scale and offset folded in (cf = 1).
-        const int slot = t % 3;
-        const bool exact_tile = (t + 1) * kTK <= X;
-        const float cf = exact_tile ? scale_log2 : 1.0f;
-        if (!exact_tile) {
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(&idx_bias[slot][k2 * 32 + g * 8 + hl * 4]);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sacc[qb][k2][4 * g + e] = fmaf(sacc[qb][k2][4 * g + e], scale_log2, bv[e]);
-                }
-        }
+        // logits in log2 units: (score + offset) * scale * log2 e
+        const float cf = scale_log2;
         if (!FIXED) {
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
@@ -506,6 +562,367 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
     }
 }
 
+// ------------------------------------------------------------------ ping-pong bf16 kernel
+// Two independent 128-row query tiles share a work-group of 8 waves: waves 0-3
+// hold tile A, waves 4-7 tile B (the hardware places waves w and w+4 of a
+// work-group on the same SIMD).  A tile is processed as a sequence of slots --
+// slot 2t: the P.V product of tile t-1 and the S = K Q^T product of tile t (MFMA);
+// slot 2t+1: the weights of tile t (VALU) -- and tile B runs one slot behind tile
+// A.  One barrier per phase keeps the halves in step, so while one wave of a SIMD
+// issues matrix products the other computes weights.  K and V tiles are loaded
+// straight into LDS three phases before their products (issued in the weight
+// slot two tiles ahead), and a phase ends waiting only for loads issued in the
+// current slot.  Weights as in attn_bf16_kernel<D, true, 1> (fixed reference);
+// the row sums come from an extra product instead of VALU additions.
+constexpr int kPPWaves = 8;
+constexpr bool kUsePingPong = true;
+constexpr int kPPAhead = 4;  // products whose operands are in flight ahead of use
+constexpr int kPPRing = 8;   // column-index ring: tiles u .. u+4 are live in weight slot u
+
+// Wait for LDS traffic and for all but the newest `keep` vector-memory operations
+// of this wave, then barrier.  The empty asm statements stop the compiler from
+// moving memory accesses across the barrier; the explicit wait replaces the full
+// drain a release fence would emit, so direct loads stay in flight across phases.
+template <int KEEP>
+__device__ __forceinline__ void pp_barrier()
+{
+    static_assert(KEEP >= 0 && KEEP < 16, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((KEEP & 0xF) | (0x7 << 4));  // vmcnt(KEEP), expcnt off, lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Barrier that waits for LDS traffic only (a product slot issues no vector-memory
+// operations, and everything older than the previous slot's direct loads has
+// already been waited for).
+__device__ __forceinline__ void pp_barrier_lds()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt and expcnt at their maxima, lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int D>
+struct PPTile {
+    int T, r0, r1, bh, lb;
+    const int32_t *crow;
+    const float *cbias;
+    bool active;
+};
+
+// One phase of one half.  SLOT parity and buffer parities are compile-time
+// functions of (J, HALF); the tile index is runtime.
+template <int D, int HALF, int J>
+__device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0, uint8_t *k1, uint8_t *v0,
+                                         uint8_t *v1, int (*ring_row)[kTK], float (*ring_bias)[kTK],
+                                         const uint16_t *kh, const uint16_t *vh, const bf16x8 *qf, f32x16 *oacc,
+                                         f32x16 *sacc, bf16x8 *pb, f32x16 &lacc, const bf16x8 &ones_a,
+                                         const int *zrow, float m_ref, const int *vtr, float scale_log2,
+                                         bool wave_active, int wq, int lane, int hl, int l32)
+{
+    constexpr int NDS = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int RSTR = D * 2;
+    constexpr int NDMA = kTK * (D / 8) / 256;  // direct-load instructions per wave per tile (K or V)
+    constexpr int K = J - HALF;                // slot index relative to 4c (may be -1)
+    constexpr bool GEMM = ((K % 2) + 2) % 2 == 0;
+    const int slot = 4 * c + K;
+    const bool live = tt.active && slot >= 0 && slot <= 2 * tt.T;
+    if (GEMM) {
+        if (live && wave_active) {
+            // P.V of tile t-1 (weights pb, V buffer (t-1) % 2) and S = K Q^T of tile
+            // t (K buffer t % 2) as one list of 32 products, P.V and K Q^T
+            // alternating so that consecutive products feed different accumulators,
+            // plus one row-sum product per key step.
+            // Operands are read kPPAhead products ahead of use, and scheduling
+            // fences keep that order, so each product waits only for reads issued
+            // several products earlier.  For t = 0 the P.V terms multiply zero
+            // weights by a zero buffer; for t = T the S tile is never used.
+            constexpr int QP = ((K / 2) % 2 + 2) % 2;   // t % 2 (4c is even)
+            const uint8_t *kc = QP == 0 ? k0 : k1;
+            const uint8_t *vc = QP == 0 ? v1 : v0;      // tile t-1
+            constexpr int NJ = 2 * NDS + 4 * NDB;       // 32 products for D = 128
+            static_assert(2 * NDS == 4 * NDB, "P.V and K Q^T lists alternate");
+            constexpr int R = kPPAhead + 1;
+            bf16x8 opnd[R];
+            auto load = [&](int j, bf16x8 &dst) {
+                const int i = j >> 1;
+                if ((j & 1) == 0) {  // P.V: d block i % NDB, key step i / NDB
+                    const int db = i % NDB, s = i / NDB;
+                    const uint8_t *vp = vc + vtr[db] + s * 16 * RSTR;
+                    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)vp);
+                    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(vp + 8 * RSTR));
+                    dst = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                } else {             // K Q^T: key half i % 2, d step i / 2
+                    const int k2 = i & 1, s = i >> 1;
+                    dst = *reinterpret_cast<const bf16x8 *>(kc + kswz<D>(k2 * 32 + l32, s * 2 + hl) * 16);
+                }
+            };
+            // the K Q^T accumulator starts at tile t's column offsets (score units);
+            // lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of its query
+            const float *bias = ring_bias[(slot / 2) % kPPRing];
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(&bias[k2 * 32 + g * 8 + hl * 4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sacc[k2][4 * g + e] = bv[e];
+                }
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int j = 0; j < kPPAhead; ++j) load(j, opnd[j]);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                // fences keep the reads of product j + kPPAhead ahead of product j
+                __builtin_amdgcn_sched_barrier(0);
+                if (j + kPPAhead < NJ) load(j + kPPAhead, opnd[(j + kPPAhead) % R]);
+                __builtin_amdgcn_sched_barrier(0);
+                const int i = j >> 1;
+                if ((j & 1) == 0) {
+                    const int db = i % NDB, s = i / NDB;
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[j % R], pb[s], oacc[db], 0, 0, 0);
+                } else {
+                    const int k2 = i & 1, s = i >> 1;
+                    sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[j % R], qf[s], sacc[k2], 0, 0, 0);
+                }
+                // row sums of the weights: a product with A = 1 in row 0, so row 0 of
+                // lacc (lanes 0-31) accumulates the sum over keys of each query
+                if ((j & 7) == 7)
+                    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, pb[j >> 3], lacc, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
+        }
+        pp_barrier_lds();
+    } else {
+        // The barrier sits in the same branch as the direct loads, so the compiler's
+        // count of outstanding loads matches the wait on every path.
+        if (live) {
+            const int u = (slot - 1) / 2;  // weights of tile u
+            constexpr int UP = (((K - 1) / 2) % 2 + 2) % 2;  // u % 2
+            // column indices and offsets of tile u+4 straight into the ring: each
+            // wave of the half loads 16 entries (lanes 0-15).  They are first read
+            // two exponential slots later, after a barrier that has waited for them.
+            {
+                const int ent = wq * 16 + lane;
+                const int64_t src = (int64_t)(u + 4 < tt.T ? u + 4 : 0) * kTK + ent;
+                auto *drow = (void __attribute__((address_space(3))) *)&ring_row[(u + 4) % kPPRing][wq * 16];
+                auto *dbias = (void __attribute__((address_space(3))) *)&ring_bias[(u + 4) % kPPRing][wq * 16];
+                asm volatile("" : "+s"(drow));
+                asm volatile("" : "+s"(dbias));
+                if (lane < 16) {
+                    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(tt.crow + src),
+                                                     drow, 4, 0, 0);
+                    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(tt.cbias + src),
+                                                     dbias, 4, 0, 0);
+                }
+            }
+            // K of tile u+2 into buffer u % 2, V of tile u+1 into buffer (u+1) % 2;
+            // past the end these load row 0 into buffers no later slot reads
+            const TileRows<D, 4> kr = tile_rows<D, 4>(u + 2 < tt.T ? ring_row[(u + 2) % kPPRing] : zrow, wq, lane);
+            const TileRows<D, 4> vr = tile_rows<D, 4>(u + 1 < tt.T ? ring_row[(u + 1) % kPPRing] : zrow, wq, lane);
+            tile_issue<D, 4, false>(UP == 0 ? k0 : k1, reinterpret_cast<const uint8_t *>(kh), kr, wq, lane);
+            tile_issue<D, 4, true>(UP == 0 ? v1 : v0, reinterpret_cast<const uint8_t *>(vh), vr, wq, lane);
+            if (wave_active) {
+                // logits in log2 units: (score + offset) * scale * log2 e
+                const float mneg = -m_ref;
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        pb[s][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], scale_log2, mneg));
+            }
+            // this slot's direct loads stay in flight; everything older has landed
+            pp_barrier<2 * NDMA + 2>();
+        } else {
+            pp_barrier<0>();
+        }
+    }
+}
+
+template <int D, int HALF>
+__device__ __forceinline__ void pp_chunks(int nchunks, const PPTile<D> &tt, uint8_t *k0, uint8_t *k1, uint8_t *v0,
+                                          uint8_t *v1, int (*ring_row)[kTK], float (*ring_bias)[kTK],
+                                          int *zrow, const uint16_t *kh, const uint16_t *vh, const bf16x8 *qf,
+                                          f32x16 *oacc, f32x16 &lacc, float m_ref, const int *vtr, float scale_log2,
+                                          bool wave_active, int wq, int lane, int hl, int l32)
+{
+    constexpr int KB = kTK * D * 2;
+    // column indices of tiles 0..3, then K of tiles 0 and 1 and V of tile 0; the
+    // second V buffer starts at zero (the first product slot multiplies it by zero
+    // weights)
+    if (wq == 0 && tt.active) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t < tt.T) {
+                ring_row[t][lane] = tt.crow[t * kTK + lane];
+                ring_bias[t][lane] = tt.cbias[t * kTK + lane];
+            }
+    }
+    for (int x = wq * 64 + lane; x < KB / 16; x += 256) *reinterpret_cast<u32x4 *>(v1 + 16 * x) = u32x4{0, 0, 0, 0};
+    if (wq == 0) zrow[lane] = 0;  // both halves write the same zeros
+    __syncthreads();
+    if (tt.active) {
+        tile_direct<D, 4, false>(k0, reinterpret_cast<const uint8_t *>(kh), ring_row[0], wq, lane);
+        tile_issue<D, 4, false>(k1, reinterpret_cast<const uint8_t *>(kh),
+                                tile_rows<D, 4>(tt.T > 1 ? ring_row[1] : zrow, wq, lane), wq, lane);
+        tile_direct<D, 4, true>(v0, reinterpret_cast<const uint8_t *>(vh), ring_row[0], wq, lane);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    f32x16 sacc[2];
+    bf16x8 pb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[s][e] = (__bf16)0.0f;
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[k2][r] = 0.0f;
+    // A operand of the row-sum product: row 0 (lanes 0 and 32) all ones
+    bf16x8 ones_a;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones_a[e] = (__bf16)(l32 == 0 ? 1.0f : 0.0f);
+    for (int c = 0; c < nchunks; ++c) {
+        pp_phase<D, HALF, 0>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+                             zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
+        pp_phase<D, HALF, 1>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+                             zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
+        pp_phase<D, HALF, 2>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+                             zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
+        pp_phase<D, HALF, 3>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+                             zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the last (unused) direct loads have landed
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_pp_kernel(
+    const uint16_t *__restrict__ q_p, const uint16_t *__restrict__ k_p, const uint16_t *__restrict__ v_p, int N,
+    int Cq, const int4 *__restrict__ table, int nblocks, const int32_t *__restrict__ col_row,
+    const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
+    const float *__restrict__ col_bmax, const int *__restrict__ kmax2, int64_t cap, float scale_log2,
+    uint16_t *__restrict__ o_p, float *__restrict__ lse_p, int *__restrict__ redo)
+{
+    constexpr int NDS = D / 16;
+    constexpr int NDB = D / 32;
+    constexpr int KB = kTK * D * 2;
+    __shared__ __attribute__((aligned(1024))) uint8_t ka0[KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t ka1[KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t va0[KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t va1[KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t kb0[KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t kb1[KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb0[KB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vb1[KB];
+    __shared__ int ring_row[2][kPPRing][kTK];
+    __shared__ __attribute__((aligned(16))) float ring_bias[2][kPPRing][kTK];
+    __shared__ int zrow[kTK];
+
+    const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave >> 2, wq = wave & 3;
+    const int lp = xcd_logical_block(blockIdx.x, gridDim.x);
+    // both halves' tiles (every wave reads both, so the phase count is uniform)
+    int Th[2];
+    int4 teh[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int tile = 2 * lp + h;
+        teh[h] = tile < nblocks ? table[tile] : make_int4(-1, 0, 0, 0);
+        Th[h] = teh[h].x >= 0 ? (col_len[(int64_t)teh[h].w * Cq + teh[h].x] + kTK - 1) / kTK : 0;
+    }
+    if (teh[0].x < 0 && teh[1].x < 0) return;
+    // phases: half h runs slot k in phase k + h; the last slot of a tile sequence is 2T
+    const int nphase = max(2 * Th[0], 2 * Th[1] + 1) + 1;
+    const int nchunks = (nphase + 3) / 4;
+
+    const int4 te = half ? teh[1] : teh[0];  // selects, not an indexed private array
+    PPTile<D> tt;
+    tt.T = half ? Th[1] : Th[0];
+    tt.active = te.x >= 0 && tt.T > 0;
+    const int i = tt.active ? te.x : 0, bh = tt.active ? te.w : 0;
+    tt.r0 = te.y;
+    tt.r1 = te.z;
+    tt.bh = bh;
+    tt.lb = 2 * lp + half;
+    const int64_t gi = (int64_t)bh * Cq + i;
+    tt.crow = col_row + gi * cap;
+    tt.cbias = col_bias + gi * cap;
+    const uint16_t *kh = k_p + (int64_t)bh * N * D;
+    const uint16_t *vh = v_p + (int64_t)bh * N * D;
+
+    // Q^T fragments of this wave's 32 rows and the fixed reference
+    // a tile with an empty column list does no products and is flagged below
+    // (zero row sums), as in the single-tile kernel
+    const bool wave_active = te.x >= 0 && tt.r0 + wq * 32 < tt.r1;
+    bf16x8 qf[NDS];
+    float m_ref = 0.0f;
+    {
+        const int qrow = tt.active ? min(tt.r0 + wq * 32 + l32, tt.r1 - 1) : 0;
+        const uint16_t *qsrc = q_p + ((int64_t)bh * N + qrow) * D + hl * 8;
+        float qss = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+            qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[s][e], (float)qf[s][e], qss);
+        }
+        qss += __shfl_xor(qss, 32);
+        const float kmx = sqrtf(__int_as_float(kmax2[bh]));
+        m_ref = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, tt.active ? col_bmax[gi] : 0.0f) + 1e-6f;
+    }
+    int vtr[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vtr[db] = v_tr_offset<D>(db, lane);
+
+    f32x16 oacc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
+    f32x16 lacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
+    // each half names its own buffers, so the compiler sees which LDS object every
+    // direct load writes and every product reads; both paths pass 4 * nchunks barriers
+    if (half == 0)
+        pp_chunks<D, 0>(nchunks, tt, ka0, ka1, va0, va1, ring_row[0], ring_bias[0], zrow, kh, vh, qf, oacc, lacc, m_ref,
+                        vtr, scale_log2, wave_active, wq, lane, hl, l32);
+    else
+        pp_chunks<D, 1>(nchunks, tt, kb0, kb1, vb0, vb1, ring_row[1], ring_bias[1], zrow, kh, vh, qf, oacc, lacc, m_ref,
+                        vtr, scale_log2, wave_active, wq, lane, hl, l32);
+
+    if (!wave_active) return;
+    const float l_tot = lacc[0] + __shfl_xor(lacc[0], 32);  // row 0 lives in lanes 0-31
+    const int qrow_raw = tt.r0 + wq * 32 + l32;
+    if (__any(qrow_raw < tt.r1 && !(l_tot >= 8.271806e-25f))) {  // 2^-80: hand the tile to the fallback
+        if (lane == 0) redo[tt.lb] = 1;
+        return;
+    }
+    if (qrow_raw < tt.r1) {
+        const float inv = 1.0f / l_tot;
+        uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + g * 8 + hl * 4;
+                const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g] * inv) |
+                                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 1] * inv) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 2] * inv) |
+                                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 3] * inv) << 16);
+                *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
+            }
+        if (lse_p && hl == 0) lse_p[(int64_t)bh * N + qrow_raw] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+    }
+}
+
 // ------------------------------------------------------------------ fp32 VALU kernel
 template <int D>
 __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__ q_p, const float *__restrict__ k_p,
@@ -560,7 +977,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
             for (int e = 0; e < DQ; ++e) s = fmaf(q[e], ks[kk][part * DQ + e], s);
             s += __shfl_xor(s, 1);
             s += __shfl_xor(s, 2);
-            const float xl = fmaf(s, scale_log2, bs[kk]);
+            const float xl = (s + bs[kk]) * scale_log2;
             const float m_new = fmaxf(m_run, xl);
             const float a = exp2f(m_run - m_new);
             const float p = exp2f(xl - m_new);
@@ -616,6 +1033,12 @@ void launch_bf16(hipStream_t st, const Layout &Lq, const void *q_p, const void *
                  const int32_t *col_x, const float *col_bmax, const int *kmax2, float scale_log2, void *o_p,
                  float *lse_p, int *redo)
 {
+    if constexpr (D == 128 && kUsePingPong) {
+        const int npairs = (Lq.ntotal / 2 + 7) / 8 * 8;
+        attn_pp_kernel<D><<<npairs, 64 * kPPWaves, 0, st>>>(
+            (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
+            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+    } else
     attn_bf16_kernel<D, true, QB><<<Lq.ntotal, 256 / QB, 0, st>>>(
         (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
         col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
@@ -676,7 +1099,8 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     int *redo = (int *)(ws + Lq.off_redo);
     int4 *table = (int4 *)(ws + Lq.off_table);
     columns_kernel<<<(unsigned)G, 256, 0, st>>>(k_offsets, exact_groups, n_exact, sample_idx, sample_bias,
-                                               n_sample, Cq, Ck, m, Lq.cap, col_row, col_bias, col_len, col_x, col_bmax);
+                                               n_sample, Cq, Ck, m, scale, Lq.cap, col_row, col_bias, col_len, col_x,
+                                               col_bmax);
     tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table, redo, kmax2);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if (dt == ISG_BF16) {
