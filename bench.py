@@ -55,7 +55,7 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_wan14b_720p_e8s8_traffic.md")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "isg_attention_wan14b_720p_e8s8_traffic.md")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_means_amd", "csrc", "attention.hip")
 
 
