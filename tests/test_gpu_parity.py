@@ -3,12 +3,14 @@
 Bars: block lists, sample indices, permutations and offsets bit-exact given the
 same upstream inputs; k-means labels equal except near-ties (fp64 distance gap
 < 1e-5); centroids within fp32 rounding; pi and offsets within 1e-6; attention
-output max-abs <= 2e-2 (bf16) / <= 1e-4 (fp32), LSE <= 2.5e-3 (bf16) / 1e-4 (fp32).
+output max-abs <= 2e-2 (bf16) / <= 1e-4 (fp32), LSE <= 4.0e-3 (bf16) / 1e-4 (fp32).
 
 The bf16 LSE bar follows from the arithmetic: the attention kernel sums the
 bf16-rounded weights that its P.V product uses (so O is an exact convex
-combination of V rows), and rounding each non-negative term to bf16 changes the
-sum by a relative 2^-9 at most, i.e. |d LSE| <= 1.95e-3 plus fp32 round-off.
+combination of V rows).  bf16 carries 8 significant bits, so rounding a
+non-negative term to the nearest bf16 changes it by a relative 2^-8 at most, and
+the sum of such terms likewise: |d LSE| <= ln(1 + 2^-8) = 3.90e-3, plus fp32
+round-off.  A row whose sum is dominated by one weight reaches that bound.
 """
 import math
 
@@ -22,7 +24,7 @@ from block_sparse_attention_means_amd.workloads import WORKLOADS, budget_keys
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL_BF16 = 2.5e-3
+LSE_TOL_BF16 = 4.0e-3
 
 DEV = "cuda:0"
 
@@ -193,6 +195,26 @@ def test_attention_given_lists(orc, H, N, d, dtype, Cq, Ck, E, m):
         assert err <= 2e-2 and lerr <= LSE_TOL_BF16
     else:
         assert err <= 1e-4 and lerr <= 1e-4
+
+
+@pytest.mark.parametrize("H,N,Cq,Ck,E,m", [
+    (1, 2048, 8, 64, 1, 0),        # exact set = the top group only, no samples: one 64-column tile
+    (3, 2048, 8, 64, 1, 16),       # one tile; odd head count, so tile pairs mix heads
+    (1, 3001, 13, 64, 40, 40),     # one or two tiles per group, ragged query groups
+    (3, 1500, 5, 48, 100, 60),     # two or three tiles; odd tile counts per head
+])
+def test_attention_short_column_lists(orc, H, N, Cq, Ck, E, m):
+    """Column lists of one to three 64-column tiles: the paired-tile kernel's
+    pipeline prologue and epilogue, tile pairs that cross heads or end in an
+    empty slot, and the loads past the end of a list."""
+    say(f"short lists H={H} N={N} Cq={Cq} Ck={Ck} E={E} m={m}")
+    *_, sel, o_p, lse_p, oo, lo = _attn_case(orc, H, N, 128, "bf16", Cq, Ck, E, m)
+    cols = npy(sel["n_sample"]).max()
+    err = np.abs(f32(o_p) - oo).max()
+    lerr = np.abs(npy(lse_p) - lo).max()
+    say(f"  max samples per group {cols}; max|O-O_oracle| = {err:.3e}, max|LSE-LSE_oracle| = {lerr:.3e}")
+    assert np.isfinite(f32(o_p)).all()
+    assert err <= 2e-2 and lerr <= LSE_TOL_BF16
 
 
 def test_attention_extreme_logit_range_falls_back(orc):
