@@ -301,8 +301,11 @@ __global__ __launch_bounds__(256) void gather_kernel(const T *x, Strides xs, con
 
 // ---------------------------------------------------------------- MFMA assign (bf16 x)
 // Distances |x - c|^2 = |c|^2 - 2<x, c> + |x|^2 on v_mfma_f32_32x32x16_bf16.  x is
-// exact in bf16; each fp32 centroid is split into bf16 planes hi + lo (16
-// significant bits, residual <= 2^-16 |c|); padded rows have norm 1e30.  Per
+// exact in bf16; each fp32 centroid, times -2 (exact), is split into bf16 planes
+// hi + lo (16 significant bits, residual <= 2^-16 |c|); padded rows have norm 1e30.
+// The norms enter the same accumulation through one more k step: |c|^2 and
+// |x|^2 + 1 are each split exactly into three bf16 parts (24 significant bits),
+// paired with ones, so the accumulator holds |x - c|^2 + 1 itself.  Per
 // token the four best candidates are kept; whenever a rival lies within
 // tau = 1e-4 (|x|^2 + max_j |c_j|^2) -- several times the worst-case error of the
 // split and of fp32 accumulation -- the decision is re-taken in fp64 with the
@@ -310,11 +313,25 @@ __global__ __launch_bounds__(256) void gather_kernel(const T *x, Strides xs, con
 // every centroid when all kept candidates are close), ties to the lower index.
 constexpr int kCT = 32;  // centroids per MFMA tile
 
-// One wave per centroid: bf16 planes hi + lo and the squared norm (fp64 over the
-// lanes, then a fixed butterfly); padded rows get zero planes and norm 1e30.
+// Exact split of an fp32 value into three bf16 parts, largest first.
+__device__ __forceinline__ void split3_bf16(float v, uint16_t *out)
+{
+    const uint16_t h = f32_to_bf16_bits(v);
+    const float r1 = v - bf16_bits_to_f32(h);  // exact
+    const uint16_t m = f32_to_bf16_bits(r1);
+    const float r2 = r1 - bf16_bits_to_f32(m);  // exact; at most 8 significant bits left
+    out[0] = h;
+    out[1] = m;
+    out[2] = f32_to_bf16_bits(r2);
+}
+
+// One wave per centroid: bf16 planes hi + lo of -2c, the squared norm (fp64 over
+// the lanes, then a fixed butterfly), and the norm row of the extra k step
+// (|c|^2 in three bf16 parts, then three ones); padded rows get zero planes and
+// norm 1e30.
 template <int D>
 __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent, int C, int Cpad, uint16_t *planes,
-                                                              float *norms)
+                                                              float *norms, uint16_t *aug)
 {
     const int bh = blockIdx.y, lane = threadIdx.x & 63;
     const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -325,8 +342,8 @@ __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent,
     for (int k = lane; k < D; k += 64) {
         if (j < C) {
             const float v = cent[((int64_t)bh * C + j) * D + k];
-            const uint16_t hb = f32_to_bf16_bits(v);
-            const float r = v - bf16_bits_to_f32(hb);  // exact
+            const uint16_t hb = f32_to_bf16_bits(-2.0f * v);
+            const float r = -2.0f * v - bf16_bits_to_f32(hb);  // exact
             hi[k] = hb;
             lo[k] = f32_to_bf16_bits(r);
             nn += (double)v * (double)v;
@@ -337,7 +354,18 @@ __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent,
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) nn += __shfl_xor(nn, off);
-    if (lane == 0) norms[(int64_t)bh * Cpad + j] = j < C ? (float)nn : 1e30f;  // padded: never wins
+    if (lane == 0) {
+        const float nf = j < C ? (float)nn : 1e30f;  // padded: never wins
+        norms[(int64_t)bh * Cpad + j] = nf;
+        uint16_t row[16];
+        split3_bf16(nf, row);
+        row[3] = row[4] = row[5] = 0x3F80;  // 1.0
+#pragma unroll
+        for (int e = 6; e < 16; ++e) row[e] = 0;  // k = 6..15 of the extra step
+        uint16_t *ar = aug + ((int64_t)bh * Cpad + j) * 16;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ar[e] = row[e];
+    }
 }
 
 // Candidates are kept as integer keys: the bits of a positive approximate
@@ -430,11 +458,16 @@ __device__ __forceinline__ int cswz(int plane, int row, int chunk)
 }
 
 template <int D>
-__device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, int Cpad, int tile, int wave,
-                                              int lane)
+__device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, const uint16_t *ab, int Cpad,
+                                              int tile, int wave, int lane)
 {
     constexpr int CPR = D / 8;
     constexpr int NCH = 2 * kCT * CPR;  // chunks per tile (both planes)
+    // the tile's 32 norm rows (32 B each) after the planes: one 64-lane load
+    if (wave == 0)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(ab + (int64_t)tile * kCT * 16 +
+                                                                                        lane * 8),
+                                         (void __attribute__((address_space(3))) *)(buf + NCH * 16), 16, 0, 0);
 #pragma unroll
     for (int it = 0; it < (NCH + 255) / 256; ++it) {
         const int blk = it * 4 + wave;
@@ -450,19 +483,22 @@ __device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, 
     }
 }
 
-// One tile of 32 centroids against the 64 tokens of this wave: distances via
-// MFMA, then every (token, centroid) key into the token's top three.
+// One tile of 32 centroids against the 64 tokens of this wave: the accumulators
+// end as |x - c|^2 + 1 (norm step first, then the -2 <x, c> steps), and every
+// (token, centroid) key goes into the token's top four.  The key's index bits
+// hold the centroid's row in the tile without the half-wave's offset of 4 rows;
+// the caller adds it once per token.
 template <int D>
-__device__ __forceinline__ void assign_tile(const uint8_t *cur, const float *ncur, int tile, const bf16x8 (*xf)[D / 16],
-                                            const float *xn1, uint32_t hi_mask, TopK<topk_of<D>()> *top, int hl,
+__device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, const bf16x8 (*xf)[D / 16],
+                                            const bf16x8 *xaug, uint32_t hi_mask, TopK<topk_of<D>()> *top, int hl,
                                             int l32)
 {
     constexpr int NDS = D / 16;
+    constexpr int NCH = 2 * kCT * (D / 8);
     f32x16 acc[2];
+    const bf16x8 an = *reinterpret_cast<const bf16x8 *>(cur + NCH * 16 + (l32 * 2 + hl) * 16);
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[tb][r] = 0.0f;
+    for (int tb = 0; tb < 2; ++tb) acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(an, xaug[tb], f32x16{}, 0, 0, 0);
 #pragma unroll
     for (int s = 0; s < NDS; ++s) {
         const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(cur + cswz<D>(0, l32, 2 * s + hl) * 16);
@@ -475,27 +511,22 @@ __device__ __forceinline__ void assign_tile(const uint8_t *cur, const float *ncu
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int cl = (r >> 2) * 8 + hl * 4 + (r & 3);
-        const float nc = ncur[cl];
-        const uint32_t j = (uint32_t)(tile * kCT + cl);
+        const uint32_t j = (uint32_t)(tile * kCT + (r >> 2) * 8 + (r & 3));  // wave-uniform
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-            const uint32_t d = __float_as_uint(fmaf(-2.0f, acc[tb][r], nc) + xn1[tb]);
-            top_insert(top[tb], (d & hi_mask) | j);
-        }
+        for (int tb = 0; tb < 2; ++tb) top_insert(top[tb], (__float_as_uint(acc[tb][r]) & hi_mask) | j);
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void assign_mfma_kernel(
     const uint16_t *__restrict__ x, Strides xs, int H, int N, int C, int Cpad, const uint16_t *__restrict__ planes,
-    const float *__restrict__ norms, const float *__restrict__ cent, int32_t *__restrict__ labels)
+    const float *__restrict__ norms, const uint16_t *__restrict__ aug, const float *__restrict__ cent,
+    int32_t *__restrict__ labels)
 {
     constexpr int NDS = D / 16;
-    constexpr int TBYTES = 2 * kCT * D * 2;  // both planes of a tile
+    constexpr int TBYTES = 2 * kCT * D * 2 + kCT * 32;  // both planes of a tile, then its norm rows
     __shared__ __attribute__((aligned(1024))) uint8_t tb0[TBYTES];
     __shared__ __attribute__((aligned(1024))) uint8_t tb1[TBYTES];
-    __shared__ float nsm[2][kCT];
     const int bh = blockIdx.y, b = bh / H, h = bh % H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
     const uint16_t *xb = x + b * xs.b + h * xs.h;
@@ -522,13 +553,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
 
     const uint16_t *pb = planes + (int64_t)bh * 2 * Cpad * D;
+    const uint16_t *ab = aug + (int64_t)bh * Cpad * 16;
     const float *nb = norms + (int64_t)bh * Cpad;
     const int ntiles = Cpad / kCT;
     // keys hold |x|^2 + 1 + |c|^2 - 2<x,c> >= 1 (so they are positive normal floats)
     int ibits = 1;
     while ((1 << ibits) < Cpad) ++ibits;
     const uint32_t imask = (1u << ibits) - 1u, hi_mask = ~imask;
-    const float xn1[2] = {xn[0] + 1.0f, xn[1] + 1.0f};
+    // B operand of the norm step: [1, 1, 1, (|x|^2 + 1) in three parts] in k = 0..7
+    // (lanes of the first half-wave), zero in k = 8..15
+    bf16x8 xaug[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const float xn1 = xn[tb] + 1.0f;
+        const uint16_t h = f32_to_bf16_bits(xn1);
+        const float r1 = xn1 - bf16_bits_to_f32(h);
+        const uint16_t m = f32_to_bf16_bits(r1);
+        const uint16_t l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
+        const uint16_t parts[8] = {0x3F80, 0x3F80, 0x3F80, h, m, l, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xaug[tb][e] = __builtin_bit_cast(__bf16, (uint16_t)(hl ? 0 : parts[e]));
+    }
     constexpr int TK = topk_of<D>();
     TopK<TK> top[2];
 #pragma unroll
@@ -543,32 +588,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off));
     if (lane == 0) cm_part[wave] = lmax;
-    planes_direct<D>(tb0, pb, Cpad, 0, wave, lane);
-    if (tid < kCT) nsm[0][tid] = nb[tid];
+    planes_direct<D>(tb0, pb, ab, Cpad, 0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const float cm = fmaxf(fmaxf(cm_part[0], cm_part[1]), fmaxf(cm_part[2], cm_part[3]));
     for (int tile = 0; tile < ntiles; tile += 2) {
         // tile in tb0 while tile+1 loads into tb1, then the reverse
-        float npre = 0.0f;
-        if (tile + 1 < ntiles) {
-            planes_direct<D>(tb1, pb, Cpad, tile + 1, wave, lane);
-            if (tid < kCT) npre = nb[(tile + 1) * kCT + tid];
-        }
-        assign_tile<D>(tb0, nsm[0], tile, xf, xn1, hi_mask, top, hl, l32);
-        if (tid < kCT) nsm[1][tid] = npre;
+        if (tile + 1 < ntiles) planes_direct<D>(tb1, pb, ab, Cpad, tile + 1, wave, lane);
+        assign_tile<D>(tb0, tile, xf, xaug, hi_mask, top, hl, l32);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tile + 1 >= ntiles) break;
-        npre = 0.0f;
-        if (tile + 2 < ntiles) {
-            planes_direct<D>(tb0, pb, Cpad, tile + 2, wave, lane);
-            if (tid < kCT) npre = nb[(tile + 2) * kCT + tid];
-        }
-        assign_tile<D>(tb1, nsm[1], tile + 1, xf, xn1, hi_mask, top, hl, l32);
-        if (tid < kCT) nsm[0][tid] = npre;
+        if (tile + 2 < ntiles) planes_direct<D>(tb0, pb, ab, Cpad, tile + 2, wave, lane);
+        assign_tile<D>(tb1, tile + 1, xf, xaug, hi_mask, top, hl, l32);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+    }
+    // the second half-wave's candidates are 4 rows further into each group of 8
+    if (hl) {
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int c = 0; c < TK; ++c) top[tb].k[c] += 4u;
     }
 
     // Decisions.  Close calls go to a work list: 16 lanes per (token, candidate)
@@ -678,7 +719,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 }
 
 struct ClusterWs {
-    size_t off_hist, off_planes, off_norms, off_poff, off_partial, total;
+    size_t off_hist, off_planes, off_norms, off_aug, off_poff, off_partial, total;
     int Cpad, maxp;
 };
 
@@ -693,6 +734,7 @@ ClusterWs cluster_ws(int B, int H, int N, int d, int C)
     w.off_hist = o; o += isg_align256(BH * nchunks * C * sizeof(int32_t));
     w.off_planes = o; o += isg_align256(BH * 2 * w.Cpad * d * sizeof(uint16_t));
     w.off_norms = o; o += isg_align256(BH * w.Cpad * sizeof(float));
+    w.off_aug = o; o += isg_align256(BH * w.Cpad * 16 * sizeof(uint16_t));
     w.off_poff = o; o += isg_align256(BH * (C + 1) * sizeof(int32_t));
     w.off_partial = o; o += isg_align256(BH * (size_t)w.maxp * d * sizeof(double));
     w.total = o;
@@ -707,9 +749,10 @@ void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, 
     if constexpr (std::is_same<T, uint16_t>::value) {
         uint16_t *planes = (uint16_t *)(ws + w.off_planes);
         float *norms = (float *)(ws + w.off_norms);
-        centroid_planes_kernel<D><<<dim3(w.Cpad / 4, BH), 256, 0, st>>>(cent, C, w.Cpad, planes, norms);
+        uint16_t *aug = (uint16_t *)(ws + w.off_aug);
+        centroid_planes_kernel<D><<<dim3(w.Cpad / 4, BH), 256, 0, st>>>(cent, C, w.Cpad, planes, norms, aug);
         assign_mfma_kernel<D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, w.Cpad, planes, norms,
-                                                                         cent, labels);
+                                                                         aug, cent, labels);
     } else {
         assign_kernel<T, D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, cent, labels);
     }
