@@ -149,12 +149,21 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, i
     __shared__ int tmp[256];
     const int bh = blockIdx.x;
     int32_t *hb = hist + (int64_t)bh * nchunks * C;
+    // the chunk counts of a label are read 8 at a time before any is rewritten, so
+    // the loads of a batch overlap instead of waiting on the store before them
+    constexpr int kB = 8;
     for (int c = threadIdx.x; c < C; c += 256) {
         int run = 0;
-        for (int ch = 0; ch < nchunks; ++ch) {
-            int v = hb[(int64_t)ch * C + c];
-            hb[(int64_t)ch * C + c] = run;
-            run += v;
+        for (int ch0 = 0; ch0 < nchunks; ch0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[u] = ch0 + u < nchunks ? hb[(int64_t)(ch0 + u) * C + c] : 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (ch0 + u < nchunks) {
+                    hb[(int64_t)(ch0 + u) * C + c] = run;
+                    run += v[u];
+                }
         }
         cnt[c] = run;
         pcs[c] = (run + prow - 1) / prow;
@@ -167,7 +176,15 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, i
     for (int c = threadIdx.x; c < C; c += 256) {
         ob[c] = cnt[c];
         pb[c] = pcs[c];
-        for (int ch = 0; ch < nchunks; ++ch) hb[(int64_t)ch * C + c] += cnt[c];
+        const int add = cnt[c];
+        for (int ch0 = 0; ch0 < nchunks; ch0 += kB) {
+            int v[kB];
+#pragma unroll
+            for (int u = 0; u < kB; ++u) v[u] = ch0 + u < nchunks ? hb[(int64_t)(ch0 + u) * C + c] : 0;
+#pragma unroll
+            for (int u = 0; u < kB; ++u)
+                if (ch0 + u < nchunks) hb[(int64_t)(ch0 + u) * C + c] = v[u] + add;
+        }
     }
     if (threadIdx.x == 0) {
         ob[C] = total;
@@ -187,10 +204,18 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
     __syncthreads();
     const int t0 = chunk * kSortChunk;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    // the chunk's labels, all loads in flight at once
+    int labs[kSortChunk / 64];
+#pragma unroll
+    for (int step = 0; step < kSortChunk / 64; ++step) {
+        const int t = t0 + step * 64 + lane;
+        labs[step] = t < N ? labels[(int64_t)bh * N + t] : 0;
+    }
+#pragma unroll
     for (int step = 0; step < kSortChunk / 64; ++step) {
         const int t = t0 + step * 64 + lane;
         const bool valid = t < N;
-        const int lab = valid ? labels[(int64_t)bh * N + t] : 0;
+        const int lab = labs[step];
         uint64_t m = __ballot(valid);
         for (int bt = 0; bt < bits; ++bt) {
             const bool one = (lab >> bt) & 1;
