@@ -134,6 +134,32 @@ __device__ __forceinline__ bool rank_before(const SelShared &sh, int a, int b, i
     return a < b;
 }
 
+// The same ranking as one ascending 64-bit key, for the rankings without votes:
+// bit 63 marks an empty (or padding) group, bits 62..31 hold the complement of
+// the score's order-preserving bits (scores descending; -0 counts as +0, as in
+// the float comparison), bits 30..0 the group id (ascending on ties).  Scores
+// are finite.
+__device__ __forceinline__ uint64_t rank_key(float v, int j, bool nonempty)
+{
+    if (!nonempty) return (1ull << 63) | (uint64_t)j;
+    const uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+    const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)(~ord) << 31) | (uint64_t)j;
+}
+
+// floor(diff / u) for u >= 1 and a quotient below 2^32: an fp32 estimate from
+// rcp ~ 1/u, one fp32 step on the remainder, then exact integer correction.
+__device__ __forceinline__ uint64_t div_floor(uint64_t diff, uint32_t u, float rcp)
+{
+    uint64_t q = (uint64_t)((float)diff * rcp);
+    int64_t r = (int64_t)(diff - q * (uint64_t)u);
+    q += (uint64_t)(int64_t)floorf((float)r * rcp);
+    r = (int64_t)(diff - q * (uint64_t)u);
+    while (r < 0) { --q; r += u; }
+    while (r >= (int64_t)u) { ++q; r -= u; }
+    return q;
+}
+
 // Exact set, then the shared sample.  Budget rule (pi == nullptr): the first
 // group of the ranking always, then groups while the running key count stays
 // <= exact_keys.  Top-p rule (pi given): groups in (pi desc, j asc) order until
@@ -163,19 +189,42 @@ __global__ __launch_bounds__(kThreads) void select_sample_kernel(
         }
     }
     __syncthreads();
-    // bitonic sort of group ids by rank_before
-    for (int size = 2; size <= P2; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int p = tid; p < P2 / 2; p += kThreads) {
-                const int lo = 2 * p - (p & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = (lo & size) == 0;
-                const int a = sh.order[lo], c = sh.order[hi];
-                const bool swap = up ? rank_before(sh, c, a, mode, topp, Ck) : rank_before(sh, a, c, mode, topp, Ck);
-                if (swap) { sh.order[lo] = c; sh.order[hi] = a; }
+    if (mode == ISG_SAMPLE_VOTES && !topp) {
+        // bitonic sort of group ids by rank_before
+        for (int size = 2; size <= P2; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int p = tid; p < P2 / 2; p += kThreads) {
+                    const int lo = 2 * p - (p & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool up = (lo & size) == 0;
+                    const int a = sh.order[lo], c = sh.order[hi];
+                    const bool swap =
+                        up ? rank_before(sh, c, a, mode, topp, Ck) : rank_before(sh, a, c, mode, topp, Ck);
+                    if (swap) { sh.order[lo] = c; sh.order[hi] = a; }
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
+    } else {
+        // the same bitonic network on rank keys (sh.W is free until the sample)
+        uint64_t *key = sh.W;
+        for (int j = tid; j < P2; j += kThreads)
+            key[j] = rank_key(topp ? sh.P[j < Ck ? j : 0] : sh.S[j < Ck ? j : 0], j, j < Ck && sh.n[j] > 0);
+        __syncthreads();
+        for (int size = 2; size <= P2; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int p = tid; p < P2 / 2; p += kThreads) {
+                    const int lo = 2 * p - (p & (stride - 1));
+                    const int hi = lo + stride;
+                    const bool up = (lo & size) == 0;
+                    const uint64_t a = key[lo], c = key[hi];
+                    if (up ? c < a : a < c) { key[lo] = c; key[hi] = a; }
+                }
+                __syncthreads();
+            }
+        }
+        for (int p = tid; p < P2; p += kThreads) sh.order[p] = (int)(key[p] & 0x7FFFFFFFu);
+        __syncthreads();
     }
     if (topp) {
         if (tid == 0) {
@@ -261,7 +310,10 @@ __global__ __launch_bounds__(kThreads) void select_sample_kernel(
         if (tid == 0) n_sample[gi] = M;
         return;
     }
-    // proposal weights W = n u, exclusive prefix in ascending group order
+    // proposal weights W = n u, exclusive prefix in ascending group order; per
+    // skipped group also 1/u and the log weight (the ranking arrays are free now)
+    float *sk_rcp = sh.P;
+    float *sk_bias = reinterpret_cast<float *>(sh.votes);
     for (int s = tid; s < nsk; s += kThreads) {
         const int j = sh.sk_group[s];
         uint32_t u = 1;
@@ -275,11 +327,14 @@ __global__ __launch_bounds__(kThreads) void select_sample_kernel(
             if (u < 1) u = 1;
         }
         sh.sk_u[s] = u;
+        sk_rcp[s] = 1.0f / (float)u;
         sh.W[s] = (uint64_t)sh.n[j] * u;
     }
     __syncthreads();
     const uint64_t T = block_exclusive_scan_u64(sh.W, nsk, sh.tmp64);
     const double lnT = log((double)T), lnm = log((double)m);
+    for (int s = tid; s < nsk; s += kThreads) sk_bias[s] = (float)(lnT - log((double)sh.sk_u[s]) - lnm);
+    __syncthreads();
     for (int t2 = 2 * tid; t2 < m; t2 += 2 * kThreads) {
         uint64_t c[4] = {(uint64_t)(t2 / 2) + 1, (uint64_t)i, (uint64_t)h, (uint64_t)b};
         philox4x64_10(c, seed, call_id);
@@ -294,9 +349,8 @@ __global__ __launch_bounds__(kThreads) void select_sample_kernel(
                 if (sh.W[mid] <= z) lo = mid; else hi = mid - 1;
             }
             const int j = sh.sk_group[lo];
-            const uint32_t u = sh.sk_u[lo];
-            si[t] = ko[j] + (int)((z - sh.W[lo]) / u);
-            sb[t] = (float)(lnT - log((double)u) - lnm);
+            si[t] = ko[j] + (int)div_floor(z - sh.W[lo], sh.sk_u[lo], sk_rcp[lo]);
+            sb[t] = sk_bias[lo];
         }
     }
     if (tid == 0) n_sample[gi] = m;

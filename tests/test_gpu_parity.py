@@ -162,6 +162,49 @@ def test_select_sample_bit_exact(orc, E, m, mode, seed):
                 assert np.abs(bi_[b, h, i, :n] - bo_[b, h, i, :n]).max(initial=0) <= 1e-6
 
 
+def _ties_case(seed, B=1, H=2, Cq=8, Ck=300, N=6000):
+    """Scores drawn from a few values (exact ties, -0 and +0) and key groups cut at
+    repeated points (many empty groups)."""
+    rng = np.random.default_rng(seed)
+    offs = np.zeros((B, H, Ck + 1), np.int32)
+    for b in range(B):
+        for h in range(H):
+            offs[b, h, 1:Ck] = np.sort(rng.choice(np.arange(0, N + 1, 37), size=Ck - 1))
+            offs[b, h, Ck] = N
+    vals = np.array([-1.5, -0.0, 0.0, 0.25, 2.0], np.float32)
+    S = rng.choice(vals, size=(B, H, Cq, Ck)).astype(np.float32)
+    pi = rng.choice(np.array([0.0, 1e-3, 1e-2, 5e-2], np.float32), size=(B, H, Cq, Ck)).astype(np.float32)
+    return S, pi, offs, N
+
+
+@pytest.mark.parametrize("rule,mode,E,m", [("budget", "importance", 1500, 500), ("budget", "uniform", 800, 700),
+                                           ("budget", "importance", 0, 4000), ("topp", "importance", 0, 500),
+                                           ("topp", "uniform", 0, 300)])
+def test_select_ties_signed_zeros_empty_groups(orc, rule, mode, E, m):
+    """Group ranking with exact score ties, -0 against +0 and empty groups (score or
+    pi descending, group id ascending, empty groups last), lists and samples
+    bit-exact against the oracle."""
+    say(f"select ties rule={rule} mode={mode} E={E} m={m}")
+    S, pi, offs, N = _ties_case(31)
+    Sg, pig, og = torch.from_numpy(S).to(DEV), torch.from_numpy(pi).to(DEV), torch.from_numpy(offs).to(DEV)
+    if rule == "budget":
+        g = isg.isg_select_sample(Sg, og, N, E, m, mode=mode, seed=3, call_id=1)
+        o = orc.select_sample(S, offs, N, E, m, mode=isg.MODES[mode], seed=3, call_id=1)
+    else:
+        g = isg.isg_select_sample_topp(Sg, pig, og, N, 0.6, m, mode=mode, seed=3, call_id=1)
+        o = orc.select_sample_topp(S, pi, offs, N, 0.6, m, mode=isg.MODES[mode], seed=3, call_id=1)
+    for key in ("exact_groups", "n_exact", "n_sample"):
+        assert np.array_equal(npy(g[key]), o[key]), key
+    ns = o["n_sample"]
+    for b in range(ns.shape[0]):
+        for h in range(ns.shape[1]):
+            for i in range(ns.shape[2]):
+                n = ns[b, h, i]
+                assert np.array_equal(npy(g["sample_idx"])[b, h, i, :n], o["sample_idx"][b, h, i, :n])
+                assert np.abs(npy(g["sample_bias"])[b, h, i, :n] - o["sample_bias"][b, h, i, :n]).max(
+                    initial=0) <= 1e-6
+
+
 # ------------------------------------------------------------------ attention
 def _attn_case(orc, H, N, d, dtype, Cq, Ck, E, m, seed=0, q_scale=1.0, zipf=None, mode="importance"):
     (q, k, v), cq, ck = _clustered(H, N, d, dtype, Cq, Ck, seed=seed, q_scale=q_scale, zipf=zipf)
