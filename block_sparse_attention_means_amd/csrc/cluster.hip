@@ -43,6 +43,34 @@ __device__ __forceinline__ void load8(const uint16_t *p, float out[8])
         out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
     }
 }
+// 8 elements as loaded (bf16: one 16-byte word; fp32: two), widened when used.
+template <typename T>
+struct Raw8;
+template <>
+struct Raw8<uint16_t> {
+    uint4 a;
+    __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ float get(int e) const
+    {
+        const uint32_t w = e < 2 ? a.x : e < 4 ? a.y : e < 6 ? a.z : a.w;
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+};
+template <>
+struct Raw8<float> {
+    float4 a, c;
+    __device__ __forceinline__ void load(const float *p)
+    {
+        a = *reinterpret_cast<const float4 *>(p);
+        c = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ float get(int e) const
+    {
+        const float4 &f = e < 4 ? a : c;
+        const int k = e & 3;
+        return k == 0 ? f.x : k == 1 ? f.y : k == 2 ? f.z : f.w;
+    }
+};
 // Copy 8 elements (16 B for bf16, 32 B for fp32).
 __device__ __forceinline__ void copy8(uint16_t *dst, const uint16_t *src)
 {
@@ -247,39 +275,41 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
 {
     constexpr int TPR = D / 8;     // threads per row
     constexpr int RP = 256 / TPR;  // row slots
-    constexpr int U = 4;           // rows per slot loaded ahead
+    constexpr int PR = piece_rows(D);
+    constexpr int RPT = PR / RP;   // rows per slot: all indices, then all rows, in flight at once
     __shared__ double red[RP][D];
+    __shared__ int grp;
     const int q = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
     const int32_t *pb = poff + (int64_t)bh * (C + 1);
     if (q >= pb[C]) return;
-    // group of piece q: the last j with poff[j] <= q (binary search)
-    int lo = 0, hi = C;  // poff[lo] <= q < poff[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pb[mid] <= q) lo = mid; else hi = mid;
-    }
-    const int j = lo;
+    // group of piece q: the one j with poff[j] <= q < poff[j + 1] (one parallel pass)
+    for (int jj = threadIdx.x; jj < C; jj += 256)
+        if (pb[jj] <= q && q < pb[jj + 1]) grp = jj;
+    __syncthreads();
+    const int j = grp;
     const int32_t *ob = offsets + (int64_t)bh * (C + 1);
-    constexpr int PR = piece_rows(D);
     const int r0 = ob[j] + (q - pb[j]) * PR, r1 = min(ob[j + 1], r0 + PR);
     const int rs = threadIdx.x / TPR, ck = threadIdx.x % TPR;
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const T *xb = x + b * xs.b + h * xs.h + ck * 8;
     const int32_t *pm = perm + (int64_t)bh * N;
-    for (int r = r0 + rs; r < r1; r += U * RP) {
-        float v[U][8];
+    int idx[RPT];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int rr = r + u * RP;
-            if (rr < r1) load8(xb + (int64_t)pm[rr] * xs.t, v[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (r + u * RP < r1) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] += (double)v[u][e];
-            }
+    for (int i = 0; i < RPT; ++i) {
+        const int rr = r0 + rs + i * RP;
+        idx[i] = rr < r1 ? pm[rr] : -1;
     }
+    Raw8<T> v[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        if (idx[i] >= 0) v[i].load(xb + (int64_t)idx[i] * xs.t);
+    // fp64 sum of the slot's rows in sorted order
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        if (idx[i] >= 0) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += (double)v[i].get(e);
+        }
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[rs][ck * 8 + e] = acc[e];
     __syncthreads();
