@@ -45,6 +45,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 // single instruction stream serialises LDS latency, exponentials and products;
 // measured slower on gfx950 than two single-block waves per SIMD.
 constexpr int kQB = 1;
+// Most work-groups of the rescaling fallback, which loops over the flagged tiles
+// (64 flags per look).
+constexpr int kFallbackBlocks = 512;
 
 
 // ------------------------------------------------------------------ prep
@@ -111,7 +114,10 @@ __global__ __launch_bounds__(256) void columns_kernel(const int32_t *k_offsets, 
 
 // Largest squared key norm of each head (fp32 of the bf16 rows), as float bits
 // (non-negative floats order like their bits); kmax must start at 0.  D/8 lanes
-// share a row, each summing one 16-byte chunk, then a butterfly over the row.
+// share a row, each summing one 16-byte chunk, then a butterfly over the row;
+// every lane has kKU rows in flight per step.
+constexpr int kKU = 4;
+
 template <int D>
 __global__ __launch_bounds__(256) void kmax_kernel(const uint16_t *k_p, int N, int *kmax)
 {
@@ -121,21 +127,27 @@ __global__ __launch_bounds__(256) void kmax_kernel(const uint16_t *k_p, int N, i
     const int bh = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ck = threadIdx.x % TPR;
     float best = 0.0f;
-    for (int r0 = blockIdx.x * RPB; r0 < N; r0 += gridDim.x * RPB) {
-        const int r = r0 + threadIdx.x / TPR;
-        float ss = 0.0f;
-        if (r < N) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(k_p + ((int64_t)bh * N + r) * D + ck * 8);
+    for (int r0 = blockIdx.x * RPB * kKU + threadIdx.x / TPR; r0 < N; r0 += gridDim.x * RPB * kKU) {
+        u32x4 w[kKU];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float a = __uint_as_float(w[q] << 16), c = __uint_as_float(w[q] & 0xFFFF0000u);
-                ss = fmaf(a, a, ss);
-                ss = fmaf(c, c, ss);
+        for (int u = 0; u < kKU; ++u)
+            if (r0 + u * RPB < N)
+                w[u] = *reinterpret_cast<const u32x4 *>(k_p + ((int64_t)bh * N + r0 + u * RPB) * D + ck * 8);
+#pragma unroll
+        for (int u = 0; u < kKU; ++u) {
+            float ss = 0.0f;
+            if (r0 + u * RPB < N) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float a = __uint_as_float(w[u][q] << 16), c = __uint_as_float(w[u][q] & 0xFFFF0000u);
+                    ss = fmaf(a, a, ss);
+                    ss = fmaf(c, c, ss);
+                }
             }
-        }
 #pragma unroll
-        for (int off = TPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
-        best = fmaxf(best, ss);
+            for (int off = TPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+            best = fmaxf(best, ss);
+        }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
@@ -450,114 +462,132 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
     __shared__ int idx_row[3][kTK];
     __shared__ __attribute__((aligned(16))) float idx_bias[3][kTK];
 
-    const int lb = xcd_logical_block(blockIdx.x, nblocks);
-    const int4 te = table[lb];
-    if (te.x < 0) return;
-    if (!FIXED && redo[lb] == 0) return;
-    const int i = te.x, r0 = te.y, r1 = te.z, bh = te.w;
-    const int64_t gi = (int64_t)bh * Cq + i;
-    const int L = col_len[gi];
-    const int X = col_x[gi];
-    const int T = (L + kTK - 1) / kTK;
-    const int32_t *crow = col_row + gi * cap;
-    const float *cbias = col_bias + gi * cap;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
-    const uint8_t *kbase = reinterpret_cast<const uint8_t *>(k_p + (int64_t)bh * N * D);
-    const uint8_t *vbase = reinterpret_cast<const uint8_t *>(v_p + (int64_t)bh * N * D);
+    // One query tile; the exits below leave a tile (a wave that has no rows, or
+    // a flagged tile, skips only the epilogue, which has no barrier).
+    auto run_tile = [&](const int lb) {
+        const int4 te = table[lb];
+        if (te.x < 0) return;
+        const int i = te.x, r0 = te.y, r1 = te.z, bh = te.w;
+        const int64_t gi = (int64_t)bh * Cq + i;
+        const int L = col_len[gi];
+        const int X = col_x[gi];
+        const int T = (L + kTK - 1) / kTK;
+        const int32_t *crow = col_row + gi * cap;
+        const float *cbias = col_bias + gi * cap;
+        const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
+        const uint8_t *kbase = reinterpret_cast<const uint8_t *>(k_p + (int64_t)bh * N * D);
+        const uint8_t *vbase = reinterpret_cast<const uint8_t *>(v_p + (int64_t)bh * N * D);
 
-    // Q^T fragments (B operand of S^T = K Q^T): lane owns query row l32 of each block.
-    const bool wave_active = r0 + wave * WROWS < r1;
-    bf16x8 qf[QB][NDS];
-    float m_run[QB], l_run[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow = min(r0 + wave * WROWS + qb * 32 + l32, r1 - 1);
-        const uint16_t *qsrc = q_p + ((int64_t)bh * N + qrow) * D + hl * 8;
-        float qss = 0.0f;
-#pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-            qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+        // Q^T fragments (B operand of S^T = K Q^T): lane owns query row l32 of each block.
+        const bool wave_active = r0 + wave * WROWS < r1;
+        bf16x8 qf[QB][NDS];
+        float m_run[QB], l_run[QB];
+    #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qrow = min(r0 + wave * WROWS + qb * 32 + l32, r1 - 1);
+            const uint16_t *qsrc = q_p + ((int64_t)bh * N + qrow) * D + hl * 8;
+            float qss = 0.0f;
+    #pragma unroll
+            for (int s = 0; s < NDS; ++s) {
+                qf[qb][s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+                if (FIXED) {
+    #pragma unroll
+                    for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[qb][s][e], (float)qf[qb][s][e], qss);
+                }
+            }
+            m_run[qb] = -INFINITY;
+            l_run[qb] = 0.0f;
             if (FIXED) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[qb][s][e], (float)qf[qb][s][e], qss);
+                qss += __shfl_xor(qss, 32);
+                const float kmx = sqrtf(__int_as_float(kmax2[bh]));
+                m_run[qb] = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, col_bmax[gi]) + 1e-6f;
             }
         }
-        m_run[qb] = -INFINITY;
-        l_run[qb] = 0.0f;
-        if (FIXED) {
-            qss += __shfl_xor(qss, 32);
-            const float kmx = sqrtf(__int_as_float(kmax2[bh]));
-            m_run[qb] = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, col_bmax[gi]) + 1e-6f;
+
+        // column list of tiles 0 and 1 into the index ring
+        if (wave == 0) {
+            idx_row[0][lane] = crow[lane];
+            idx_bias[0][lane] = cbias[lane];
+            if (T > 1) {
+                idx_row[1][lane] = crow[kTK + lane];
+                idx_bias[1][lane] = cbias[kTK + lane];
+            }
         }
-    }
+        __syncthreads();
+        constexpr int NW = 4 / QB;
+        tile_direct<D, NW, false>(kb0, kbase, idx_row[0], wave, lane);
+        tile_direct<D, NW, true>(vb0, vbase, idx_row[0], wave, lane);
+        int vtr[NDB];
+    #pragma unroll
+        for (int db = 0; db < NDB; ++db) vtr[db] = v_tr_offset<D>(db, lane);
+        __builtin_amdgcn_s_waitcnt(0);  // direct K and V loads have landed in LDS
+        __syncthreads();
 
-    // column list of tiles 0 and 1 into the index ring
-    if (wave == 0) {
-        idx_row[0][lane] = crow[lane];
-        idx_bias[0][lane] = cbias[lane];
-        if (T > 1) {
-            idx_row[1][lane] = crow[kTK + lane];
-            idx_bias[1][lane] = cbias[kTK + lane];
-        }
-    }
-    __syncthreads();
-    constexpr int NW = 4 / QB;
-    tile_direct<D, NW, false>(kb0, kbase, idx_row[0], wave, lane);
-    tile_direct<D, NW, true>(vb0, vbase, idx_row[0], wave, lane);
-    int vtr[NDB];
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) vtr[db] = v_tr_offset<D>(db, lane);
-    __builtin_amdgcn_s_waitcnt(0);  // direct K and V loads have landed in LDS
-    __syncthreads();
-
-    f32x16 oacc[QB][NDB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
-
-    for (int t = 0; t < T; t += 2) {
-        tile_step<D, FIXED, QB>(t, T, X, kb0, vb0, kb1, vb1, kbase, vbase, crow, cbias, idx_row, idx_bias, qf,
-                                oacc, l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
-        if (t + 1 < T)
-            tile_step<D, FIXED, QB>(t + 1, T, X, kb1, vb1, kb0, vb0, kbase, vbase, crow, cbias, idx_row, idx_bias,
-                                    qf, oacc, l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
-    }
-
-    if (!wave_active) return;
-    float l_tot[QB];
-    bool low = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
-        const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
-        low = low || (qrow_raw < r1 && !(l_tot[qb] >= 8.271806e-25f));  // 2^-80
-    }
-    if (FIXED && __any(low)) {
-        if (lane == 0) redo[lb] = 1;
-        return;
-    }
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
-        if (qrow_raw < r1) {
-            const float inv = 1.0f / l_tot[qb];
-            uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
-#pragma unroll
+        f32x16 oacc[QB][NDB];
+    #pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+    #pragma unroll
             for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d0 = db * 32 + g * 8 + hl * 4;
-                    const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g] * inv) |
-                                        ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 1] * inv) << 16);
-                    const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 2] * inv) |
-                                        ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 3] * inv) << 16);
-                    *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
-                }
-            if (lse_p && hl == 0)
-                lse_p[(int64_t)bh * N + qrow_raw] = (m_run[qb] + log2f(l_tot[qb])) * 0.6931471805599453f;
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.0f;
+
+        for (int t = 0; t < T; t += 2) {
+            tile_step<D, FIXED, QB>(t, T, X, kb0, vb0, kb1, vb1, kbase, vbase, crow, cbias, idx_row, idx_bias, qf,
+                                    oacc, l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
+            if (t + 1 < T)
+                tile_step<D, FIXED, QB>(t + 1, T, X, kb1, vb1, kb0, vb0, kbase, vbase, crow, cbias, idx_row, idx_bias,
+                                        qf, oacc, l_run, m_run, vtr, scale_log2, wave_active, wave, lane, hl, l32);
+        }
+
+        if (!wave_active) return;
+        float l_tot[QB];
+        bool low = false;
+    #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
+            const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
+            low = low || (qrow_raw < r1 && !(l_tot[qb] >= 8.271806e-25f));  // 2^-80
+        }
+        if (FIXED && __any(low)) {
+            if (lane == 0) redo[lb] = 1;
+            return;
+        }
+    #pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
+            if (qrow_raw < r1) {
+                const float inv = 1.0f / l_tot[qb];
+                uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
+    #pragma unroll
+                for (int db = 0; db < NDB; ++db)
+    #pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int d0 = db * 32 + g * 8 + hl * 4;
+                        const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g] * inv) |
+                                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 1] * inv) << 16);
+                        const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 2] * inv) |
+                                            ((uint32_t)f32_to_bf16_bits(oacc[qb][db][4 * g + 3] * inv) << 16);
+                        *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
+                    }
+                if (lse_p && hl == 0)
+                    lse_p[(int64_t)bh * N + qrow_raw] = (m_run[qb] + log2f(l_tot[qb])) * 0.6931471805599453f;
+            }
+        }
+    };
+    if constexpr (FIXED) {
+        run_tile(xcd_logical_block(blockIdx.x, nblocks));
+    } else {
+        // the fallback: each work-group reads the flags of 64 tiles at once (every
+        // wave the same 64, so the ballot is uniform) and runs the flagged ones
+        const int lane = threadIdx.x & 63;
+        for (int base = blockIdx.x * 64; base < nblocks; base += gridDim.x * 64) {
+            uint64_t mask = __ballot(base + lane < nblocks && redo[base + lane] != 0);
+            while (mask) {
+                const int bit = __ffsll((unsigned long long)mask) - 1;
+                mask &= mask - 1;
+                run_tile(base + bit);
+                __syncthreads();  // LDS tiles and index rows free for the next tile
+            }
         }
     }
 }
@@ -1042,7 +1072,7 @@ void launch_bf16(hipStream_t st, const Layout &Lq, const void *q_p, const void *
     attn_bf16_kernel<D, true, QB><<<Lq.ntotal, 256 / QB, 0, st>>>(
         (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
         col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
-    attn_bf16_kernel<D, false, 1><<<Lq.ntotal, 256, 0, st>>>(
+    attn_bf16_kernel<D, false, 1><<<std::min((Lq.ntotal + 63) / 64, kFallbackBlocks), 256, 0, st>>>(
         (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
         col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
 }
@@ -1070,6 +1100,8 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     ISG_REQUIRE(m == 0 || (sample_idx && sample_bias), ISG_E_ARG,
                 "isg_attention: sample_idx / sample_bias required when m > 0");
     ISG_REQUIRE(B >= 1 && H >= 1 && N >= 1, ISG_E_ARG, "isg_attention: B, H, N must be >= 1");
+    ISG_REQUIRE((int64_t)B * H <= 65535, ISG_E_ARG, "isg_attention: B*H must be <= 65535 (got %lld)",
+                (long long)B * H);
     ISG_REQUIRE(dt == ISG_F32 || dt == ISG_BF16, ISG_E_DTYPE, "isg_attention: dtype %d", (int)dt);
     ISG_REQUIRE(d == 64 || d == 128, ISG_E_UNSUPPORTED, "isg_attention: d=%d not built (64, 128)", d);
     ISG_REQUIRE(Cq >= 1 && Cq <= kMaxGroups && Ck >= 1 && Ck <= kMaxGroups, ISG_E_ARG,
@@ -1104,7 +1136,7 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table, redo, kmax2);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if (dt == ISG_BF16) {
-        const dim3 kgrid((unsigned)std::min((N + 255) / 256, 64), (unsigned)(B * H));
+        const dim3 kgrid((unsigned)std::min((N + 255) / 256, 128), (unsigned)(B * H));
         if (d == 128) {
             kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<128, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,

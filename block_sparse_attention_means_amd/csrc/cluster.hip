@@ -886,6 +886,8 @@ extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, con
                 "isg_cluster: null pointer argument");
     ISG_REQUIRE(B >= 1 && H >= 1 && N >= 1, ISG_E_ARG, "isg_cluster: B, H, N must be >= 1 (got %d, %d, %d)",
                 B, H, N);
+    ISG_REQUIRE((int64_t)B * H <= 65535, ISG_E_ARG, "isg_cluster: B*H must be <= 65535 (got %lld)",
+                (long long)B * H);
     ISG_REQUIRE(dt == ISG_F32 || dt == ISG_BF16, ISG_E_DTYPE, "isg_cluster: dtype %d", (int)dt);
     ISG_REQUIRE(d == 16 || d == 64 || d == 128, ISG_E_UNSUPPORTED, "isg_cluster: d=%d not built (16, 64, 128)",
                 d);

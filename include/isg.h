@@ -33,6 +33,9 @@
  *    keep no global mutable state and are reentrant.
  *  - dtypes: ISG_F32 or ISG_BF16 for Q/K/V and the attention output; every
  *    accumulation is fp32 or wider.
+ *  - Heads: isg_cluster, isg_attention and isg_pq_votes give each head a row
+ *    of a launch grid, so they need B*H <= 65535 and reject more with
+ *    ISG_E_ARG.
  */
 #ifndef ISG_H
 #define ISG_H

@@ -61,7 +61,7 @@ def _cluster(**kw):
     (dict(x=None), 1), (dict(lab=None), 1), (dict(B=0), 1), (dict(N=0), 1),
     (dict(dt=7), 2), (dict(d=32), 3), (dict(C=0), 1), (dict(C=65), 1), (dict(iters=0), 1),
     (dict(init=2), 1), (dict(comp=FAKE), 1), (dict(strides=_i64x3(8 * 64 * 128, 64 * 128, 100)), 1),
-    (dict(ws=None), 4), (dict(wsb=16), 4), (dict(x=C.c_void_p(258)), 1),
+    (dict(ws=None), 4), (dict(wsb=16), 4), (dict(x=C.c_void_p(258)), 1), (dict(B=2, H=40000), 1),
 ])
 def test_cluster_rejects(kw, status):
     assert _cluster(**kw) == status
@@ -131,7 +131,7 @@ def _attn(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(o=None), 1), (dict(si=None), 1), (dict(dt=5), 2), (dict(d=96), 3),
     (dict(d=16), 3), (dict(Cq=0), 1), (dict(Ck=4096), 1), (dict(m=257), 1), (dict(scale=float("nan")), 1),
-    (dict(ws=None), 4), (dict(wsb=100), 4), (dict(v=C.c_void_p(264)), 1),
+    (dict(ws=None), 4), (dict(wsb=100), 4), (dict(v=C.c_void_p(264)), 1), (dict(B=2, H=40000), 1),
 ])
 def test_attention_rejects(kw, status):
     assert _attn(**kw) == status

@@ -292,6 +292,39 @@ def test_attention_extreme_logit_range_falls_back(orc):
     assert np.abs(npy(lse_p) - lo).max() <= LSE_TOL_BF16 + 1e-6 * np.abs(lo).max()
 
 
+def test_attention_fallback_mixed_heads_many_tiles(orc):
+    """One extreme head (every tile flagged) among three ordinary ones, with more
+    query tiles than the fallback has work-groups: the rescaling pass walks the
+    flagged tiles with a persistent grid and leaves the others alone."""
+    H, N, d, Cq, Ck = 4, 16384, 128, 8, 32
+    g = torch.Generator().manual_seed(11)
+    q, k, v = _inputs(H, N, d, "bf16", seed=13)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q[0, 2] = (200.0 * u + 0.05 * torch.randn(N, d, generator=g)).to(torch.bfloat16)
+    k[0, 2] = (-200.0 * u + 0.05 * torch.randn(N, d, generator=g)).to(torch.bfloat16)
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    scale = isg.default_scale(d)
+    cq = isg.isg_cluster(qg, Cq, 5)
+    ck = isg.isg_cluster(kg, Ck, 5, companion=vg)
+    S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+    sel = isg.isg_select_sample(S, ck["offsets"], N, 300, 300, seed=2)
+    o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
+                                   ck["offsets"], sel, scale)
+    torch.cuda.synchronize()
+    selo = {kk: npy(vv) for kk, vv in sel.items() if kk != "m"}
+    oo, lo = orc.attention(f32(cq["x_perm"]), f32(ck["x_perm"]), f32(ck["companion_perm"]), npy(cq["offsets"]),
+                           npy(ck["offsets"]), selo, 300, scale)
+    assert np.isfinite(f32(o_p)).all()
+    err = np.abs(f32(o_p) - oo).max()
+    lerr = np.abs(npy(lse_p) - lo)
+    say(f"  mixed heads: max|O-O_oracle| {err:.3e}, extreme head LSE {lo[0, 2].min():.1f}..{lo[0, 2].max():.1f}")
+    assert lo[0, 2].max() < -1000 and lo[0, [0, 1, 3]].min() > -1000
+    assert err <= 2e-2
+    assert lerr[0, [0, 1, 3]].max() <= LSE_TOL_BF16
+    assert lerr[0, 2].max() <= LSE_TOL_BF16 + 1e-6 * np.abs(lo[0, 2]).max()
+
+
 def test_attention_high_entropy_zipf(orc):
     """Near-uniform attention (Q scaled by 0.2) with Zipf cluster sizes."""
     *_, o_p, lse_p, oo, lo = _attn_case(orc, 2, 4096, 128, "bf16", 16, 64, 300, 300, q_scale=0.2, zipf=1.2)
