@@ -50,6 +50,7 @@ template <>
 struct Raw8<uint16_t> {
     uint4 a;
     __device__ __forceinline__ void load(const uint16_t *p) { a = *reinterpret_cast<const uint4 *>(p); }
+    __device__ __forceinline__ void store(uint16_t *p) const { *reinterpret_cast<uint4 *>(p) = a; }
     __device__ __forceinline__ float get(int e) const
     {
         const uint32_t w = e < 2 ? a.x : e < 4 ? a.y : e < 6 ? a.z : a.w;
@@ -63,6 +64,11 @@ struct Raw8<float> {
     {
         a = *reinterpret_cast<const float4 *>(p);
         c = *reinterpret_cast<const float4 *>(p + 4);
+    }
+    __device__ __forceinline__ void store(float *p) const
+    {
+        *reinterpret_cast<float4 *>(p) = a;
+        *reinterpret_cast<float4 *>(p + 4) = c;
     }
     __device__ __forceinline__ float get(int e) const
     {
@@ -271,7 +277,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides xs, int H, int N, int C,
                                                            const int32_t *perm, const int32_t *offsets,
-                                                           const int32_t *poff, int maxp, double *partial)
+                                                           const int32_t *poff, int maxp, double *partial,
+                                                           T *x_perm)
 {
     constexpr int TPR = D / 8;     // threads per row
     constexpr int RP = 256 / TPR;  // row slots
@@ -302,6 +309,13 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         if (idx[i] >= 0) v[i].load(xb + (int64_t)idx[i] * xs.t);
+    // last round: the rows just read are also the permuted copy (x_perm[r] = x[perm[r]])
+    if (x_perm) {
+        T *xp = x_perm + (int64_t)bh * N * D + ck * 8;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            if (idx[i] >= 0) v[i].store(xp + (int64_t)(r0 + rs + i * RP) * D);
+    }
     // fp64 sum of the slot's rows in sorted order
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -836,14 +850,15 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
         scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, piece_rows(D), offsets, poff);
         scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, N, C, nchunks, bits, perm);
+        // the last round's update also writes the permuted copy of x
         update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
-                                                                    partial);
+                                                                    partial, it + 1 == iters ? x_perm : nullptr);
         update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent);
     }
-    if (x_perm || comp_perm) {
+    if (comp_perm) {
         const int64_t total = (int64_t)BH * N * (D / 8);
         const int grid = (int)std::min<int64_t>((total + 255) / 256, 1 << 20);
-        gather_kernel<T, D><<<grid, 256, 0, st>>>(x, xs, comp, H, N, perm, x_perm, comp_perm, total);
+        gather_kernel<T, D><<<grid, 256, 0, st>>>(x, xs, comp, H, N, perm, nullptr, comp_perm, total);
     }
     return isg_check_launch("isg_cluster");
 }
