@@ -558,7 +558,7 @@ __device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, 
 // hold the centroid's row in the tile without the half-wave's offset of 4 rows;
 // the caller adds it once per token.
 template <int D>
-__device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, const bf16x8 (*xf)[D / 16],
+__device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, int C, const bf16x8 (*xf)[D / 16],
                                             const bf16x8 *xaug, uint32_t hi_mask, TopK<topk_of<D>()> *top, int hl,
                                             int l32)
 {
@@ -581,6 +581,8 @@ __device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, const 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const uint32_t j = (uint32_t)(tile * kCT + (r >> 2) * 8 + (r & 3));  // wave-uniform
+        // rows j and j + 4 both padding (norm 1e30, never kept): skip (a scalar branch)
+        if (j >= (uint32_t)C) continue;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) top_insert(top[tb], (__float_as_uint(acc[tb][r]) & hi_mask) | j);
     }
@@ -664,12 +666,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int tile = 0; tile < ntiles; tile += 2) {
         // tile in tb0 while tile+1 loads into tb1, then the reverse
         if (tile + 1 < ntiles) planes_direct<D>(tb1, pb, ab, Cpad, tile + 1, wave, lane);
-        assign_tile<D>(tb0, tile, xf, xaug, hi_mask, top, hl, l32);
+        assign_tile<D>(tb0, tile, C, xf, xaug, hi_mask, top, hl, l32);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tile + 1 >= ntiles) break;
         if (tile + 2 < ntiles) planes_direct<D>(tb0, pb, ab, Cpad, tile + 2, wave, lane);
-        assign_tile<D>(tb1, tile + 1, xf, xaug, hi_mask, top, hl, l32);
+        assign_tile<D>(tb1, tile + 1, C, xf, xaug, hi_mask, top, hl, l32);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
