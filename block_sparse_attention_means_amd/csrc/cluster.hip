@@ -602,31 +602,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
     const uint16_t *xb = x + b * xs.b + h * xs.h;
 
+    const uint16_t *pb = planes + (int64_t)bh * 2 * Cpad * D;
+    const uint16_t *ab = aug + (int64_t)bh * Cpad * 16;
+    const float *nb = norms + (int64_t)bh * Cpad;
+    const int ntiles = Cpad / kCT;
+    // Every prologue load is issued before the first wait: tile 0's planes, the
+    // token rows, then the centroid norms (for the largest, used by the decision
+    // window; an index past C re-reads norm C - 1, harmless for a maximum).
+    planes_direct<D>(tb0, pb, ab, Cpad, 0, wave, lane);
     int tok[2];
     bf16x8 xf[2][NDS];
-    float xn[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
         const int t = blockIdx.x * 256 + wave * 64 + tb * 32 + l32;
         tok[tb] = t;
         const uint16_t *row = xb + (int64_t)min(t, N - 1) * xs.t + hl * 8;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) xf[tb][s] = *reinterpret_cast<const bf16x8 *>(row + s * 16);
+    }
+    __shared__ float cm_part[4];
+    float lmax = 0.0f;
+    for (int j0 = 0; j0 < C; j0 += 1024) {
+        float nv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) nv[u] = nb[min(j0 + u * 256 + tid, C - 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) lmax = fmaxf(lmax, nv[u]);
+    }
+    float xn[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
         float ss = 0.0f;
 #pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-            xf[tb][s] = *reinterpret_cast<const bf16x8 *>(row + s * 16);
+        for (int s = 0; s < NDS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float v = (float)xf[tb][s][e];
                 ss = fmaf(v, v, ss);
             }
-        }
         xn[tb] = ss + __shfl_xor(ss, 32);
     }
-
-    const uint16_t *pb = planes + (int64_t)bh * 2 * Cpad * D;
-    const uint16_t *ab = aug + (int64_t)bh * Cpad * 16;
-    const float *nb = norms + (int64_t)bh * Cpad;
-    const int ntiles = Cpad / kCT;
     // keys hold |x|^2 + 1 + |c|^2 - 2<x,c> >= 1 (so they are positive normal floats)
     int ibits = 1;
     while ((1 << ibits) < Cpad) ++ibits;
@@ -651,15 +666,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int c = 0; c < TK; ++c) top[tb].k[c] = 0xFFFFFFFFu;
-
-    // largest centroid norm of the head (for the decision window)
-    __shared__ float cm_part[4];
-    float lmax = 0.0f;
-    for (int j = tid; j < C; j += 256) lmax = fmaxf(lmax, nb[j]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off));
     if (lane == 0) cm_part[wave] = lmax;
-    planes_direct<D>(tb0, pb, ab, Cpad, 0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const float cm = fmaxf(fmaxf(cm_part[0], cm_part[1]), fmaxf(cm_part[2], cm_part[3]));
