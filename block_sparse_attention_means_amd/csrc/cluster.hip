@@ -309,7 +309,7 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
         if (idx[i] >= 0) v[i].load(xb + (int64_t)idx[i] * xs.t);
-    // last round: the rows just read are also the permuted copy (x_perm[r] = x[perm[r]])
+    // last k-means iteration: the rows just read are also the permuted copy (x_perm[r] = x[perm[r]])
     if (x_perm) {
         T *xp = x_perm + (int64_t)bh * N * D + ck * 8;
 #pragma unroll
@@ -861,7 +861,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
         scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, piece_rows(D), offsets, poff);
         scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, N, C, nchunks, bits, perm);
-        // the last round's update also writes the permuted copy of x
+        // the last iteration's update also writes the permuted copy of x
         update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
                                                                     partial, it + 1 == iters ? x_perm : nullptr);
         update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent);
