@@ -393,6 +393,38 @@ def test_pipeline_tiny_config_vs_oracle(orc):
     assert np.abs(npy(r["lse"]) - lse).max() <= 1e-4
 
 
+def test_pipeline_batch_of_two_vs_oracle(orc):
+    """B = 2 with ragged N: each batch's clustering equals a B = 1 run on its own
+    data bit for bit, the permuted copies are exact gathers, and scores, lists,
+    samples (whose counter carries the batch index), attention and un-permute
+    match the oracle re-run from the GPU's clustering."""
+    B, H, N, d, Cq, Ck, E, m = 2, 2, 3001, 128, 8, 40, 300, 257
+    q, k, v, _ = make_qkv(H, N, d, n_centers=12, dtype="bf16", seed=21, B=B)
+    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), Cq, Ck, 5, E, m, seed=4)
+    torch.cuda.synchronize()
+    for b in range(B):
+        one = isg.isg_cluster(k[b:b + 1].to(DEV), Ck, 5, companion=v[b:b + 1].to(DEV))
+        for key in ("labels", "centroids", "perm", "offsets", "x_perm", "companion_perm"):
+            assert torch.equal(one[key][0].cpu(), r["ck"][key][b].cpu()), (b, key)
+        for h in range(H):
+            pk = r["ck"]["perm"][b, h].long().cpu()
+            assert torch.equal(r["ck"]["x_perm"][b, h].cpu(), k[b, h][pk])
+            pq = r["cq"]["perm"][b, h].long().cpu()
+            assert torch.equal(r["cq"]["x_perm"][b, h].cpu(), q[b, h][pq])
+    S, _ = orc.probs(npy(r["cq"]["centroids"]), npy(r["ck"]["centroids"]), npy(r["ck"]["offsets"]), r["scale"])
+    assert np.array_equal(S, npy(r["scores"]))
+    sel = orc.select_sample(S, npy(r["ck"]["offsets"]), N, E, m, seed=4)
+    for key in ("exact_groups", "n_exact", "n_sample", "sample_idx"):
+        assert np.array_equal(sel[key], npy(r["sel"][key])), key
+    o_p, lse_p = orc.attention(f32(r["cq"]["x_perm"]), f32(r["ck"]["x_perm"]), f32(r["ck"]["companion_perm"]),
+                               npy(r["cq"]["offsets"]), npy(r["ck"]["offsets"]), sel, m, r["scale"])
+    o, lse = orc.unpermute(o_p, lse_p, npy(r["cq"]["perm"]))
+    err = np.abs(f32(r["o"]) - o).max()
+    lerr = np.abs(npy(r["lse"]) - lse).max()
+    say(f"  B=2: max|O-O_oracle| = {err:.3e}, max|LSE-LSE_oracle| = {lerr:.3e}")
+    assert err <= 2e-2 and lerr <= LSE_TOL_BF16
+
+
 def test_pipeline_deterministic():
     q, k, v = _inputs(2, 4096, 128, "bf16", seed=11)
     a = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), 16, 64, 5, 400, 400, seed=3)
