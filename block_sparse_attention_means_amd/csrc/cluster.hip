@@ -685,11 +685,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
         __syncthreads();
     }
     // the second half-wave's candidates are 4 rows further into each group of 8
+    // (slots never filled keep the empty key 0xFFFFFFFF, which must not wrap: with
+    // C < 4 a half-wave inserts fewer than four keys, the padding rows being skipped)
     if (hl) {
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-            for (int c = 0; c < TK; ++c) top[tb].k[c] += 4u;
+            for (int c = 0; c < TK; ++c)
+                if (top[tb].k[c] != 0xFFFFFFFFu) top[tb].k[c] += 4u;
     }
 
     // Decisions.  Close calls go to a work list: 16 lanes per (token, candidate)

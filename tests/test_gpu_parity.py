@@ -61,7 +61,7 @@ def _near_tie_ok(orc, x, cent, lab_gpu, lab_orc, tol=1e-5):
 
 
 @pytest.mark.parametrize("dtype,d,N,C", [("f32", 64, 2048, 8), ("f32", 64, 2048, 32), ("bf16", 128, 3000, 50),
-                                         ("bf16", 16, 1500, 256), ("bf16", 64, 777, 13)])
+                                         ("bf16", 16, 1500, 256), ("bf16", 64, 777, 13), ("bf16", 128, 300, 2)])
 def test_cluster_one_round_stagewise(orc, dtype, d, N, C):
     """Assign given identical centroids (near-tie rule); update given identical labels;
     stable permutation and offsets bit-exact given the labels; gathers exact."""
@@ -393,6 +393,17 @@ def test_pipeline_tiny_config_vs_oracle(orc):
     assert np.abs(npy(r["lse"]) - lse).max() <= 1e-4
 
 
+def _same_lists_and_samples(o, g):
+    """Exact lists and counts equal; samples equal up to each group's n_sample
+    (the entries past it are not written)."""
+    for key in ("exact_groups", "n_exact", "n_sample"):
+        assert np.array_equal(o[key], npy(g[key])), key
+    ns, gi = o["n_sample"], npy(g["sample_idx"])
+    for idx in np.ndindex(*ns.shape):
+        n = ns[idx]
+        assert np.array_equal(o["sample_idx"][idx][:n], gi[idx][:n]), ("sample_idx", idx)
+
+
 def test_pipeline_batch_of_two_vs_oracle(orc):
     """B = 2 with ragged N: each batch's clustering equals a B = 1 run on its own
     data bit for bit, the permuted copies are exact gathers, and scores, lists,
@@ -414,8 +425,7 @@ def test_pipeline_batch_of_two_vs_oracle(orc):
     S, _ = orc.probs(npy(r["cq"]["centroids"]), npy(r["ck"]["centroids"]), npy(r["ck"]["offsets"]), r["scale"])
     assert np.array_equal(S, npy(r["scores"]))
     sel = orc.select_sample(S, npy(r["ck"]["offsets"]), N, E, m, seed=4)
-    for key in ("exact_groups", "n_exact", "n_sample", "sample_idx"):
-        assert np.array_equal(sel[key], npy(r["sel"][key])), key
+    _same_lists_and_samples(sel, r["sel"])
     o_p, lse_p = orc.attention(f32(r["cq"]["x_perm"]), f32(r["ck"]["x_perm"]), f32(r["ck"]["companion_perm"]),
                                npy(r["cq"]["offsets"]), npy(r["ck"]["offsets"]), sel, m, r["scale"])
     o, lse = orc.unpermute(o_p, lse_p, npy(r["cq"]["perm"]))
@@ -423,6 +433,41 @@ def test_pipeline_batch_of_two_vs_oracle(orc):
     lerr = np.abs(npy(r["lse"]) - lse).max()
     say(f"  B=2: max|O-O_oracle| = {err:.3e}, max|LSE-LSE_oracle| = {lerr:.3e}")
     assert err <= 2e-2 and lerr <= LSE_TOL_BF16
+
+
+@pytest.mark.parametrize("H,N,d,dtype,Cq,Ck,E,m", [
+    (1, 1, 128, "bf16", 1, 1, 1, 0),       # one token
+    (2, 5, 64, "f32", 1, 1, 0, 5),         # one group each side, every key sampled
+    (1, 64, 128, "bf16", 64, 64, 10, 10),  # C = N: a group per token
+    (1, 200, 128, "bf16", 4, 8, 200, 0),   # exact budget covers every key
+    (1, 130, 64, "bf16", 3, 5, 20, 20),    # d = 64 (the one-tile kernel), ragged
+])
+def test_pipeline_degenerate_shapes(orc, H, N, d, dtype, Cq, Ck, E, m):
+    """Degenerate shapes through the whole path against the oracle re-run from the
+    GPU's clustering: scores, lists and samples bit-exact, output within the bar."""
+    say(f"degenerate H={H} N={N} d={d} {dtype} Cq={Cq} Ck={Ck} E={E} m={m}")
+    q, k, v = _inputs(H, N, d, dtype, seed=N + d)
+    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), Cq, Ck, 5, E, m, seed=6)
+    torch.cuda.synchronize()
+    for c, x in (("cq", q), ("ck", k)):
+        for h in range(H):
+            pp = r[c]["perm"][0, h].long().cpu()
+            assert torch.equal(torch.sort(pp).values, torch.arange(N)), c
+            assert torch.equal(r[c]["x_perm"][0, h].cpu(), x[0, h][pp]), c
+    S, _ = orc.probs(npy(r["cq"]["centroids"]), npy(r["ck"]["centroids"]), npy(r["ck"]["offsets"]), r["scale"])
+    assert np.array_equal(S, npy(r["scores"]))
+    sel = orc.select_sample(S, npy(r["ck"]["offsets"]), N, E, m, seed=6)
+    _same_lists_and_samples(sel, r["sel"])
+    o_p, lse_p = orc.attention(f32(r["cq"]["x_perm"]), f32(r["ck"]["x_perm"]), f32(r["ck"]["companion_perm"]),
+                               npy(r["cq"]["offsets"]), npy(r["ck"]["offsets"]), sel, m, r["scale"])
+    o, lse = orc.unpermute(o_p, lse_p, npy(r["cq"]["perm"]))
+    err = np.abs(f32(r["o"]) - o).max()
+    lerr = np.abs(npy(r["lse"]) - lse).max()
+    say(f"  max|O-O_oracle| = {err:.3e}, max|LSE-LSE_oracle| = {lerr:.3e}")
+    if dtype == "bf16":
+        assert err <= 2e-2 and lerr <= LSE_TOL_BF16
+    else:
+        assert err <= 1e-4 and lerr <= 1e-4
 
 
 def test_pipeline_deterministic():
