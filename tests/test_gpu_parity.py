@@ -470,6 +470,28 @@ def test_pipeline_degenerate_shapes(orc, H, N, d, dtype, Cq, Ck, E, m):
         assert err <= 1e-4 and lerr <= 1e-4
 
 
+def test_pipeline_max_groups(orc):
+    """Cq = Ck = 1024 (the most groups selection and attention take): 32 centroid
+    tiles in the assign, a 1024-key ranking sort, one tile table slot per group;
+    lists and samples bit-exact, output within the bar."""
+    H, N, d, Cq, Ck, E, m = 1, 8192, 128, 1024, 1024, 600, 600
+    q, k, v = _inputs(H, N, d, "bf16", seed=29, n_centers=64)
+    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), Cq, Ck, 5, E, m, seed=8)
+    torch.cuda.synchronize()
+    assert int(npy(r["ck"]["labels"]).max()) < Ck and int(npy(r["cq"]["labels"]).max()) < Cq
+    S, _ = orc.probs(npy(r["cq"]["centroids"]), npy(r["ck"]["centroids"]), npy(r["ck"]["offsets"]), r["scale"])
+    assert np.array_equal(S, npy(r["scores"]))
+    sel = orc.select_sample(S, npy(r["ck"]["offsets"]), N, E, m, seed=8)
+    _same_lists_and_samples(sel, r["sel"])
+    o_p, lse_p = orc.attention(f32(r["cq"]["x_perm"]), f32(r["ck"]["x_perm"]), f32(r["ck"]["companion_perm"]),
+                               npy(r["cq"]["offsets"]), npy(r["ck"]["offsets"]), sel, m, r["scale"])
+    o, lse = orc.unpermute(o_p, lse_p, npy(r["cq"]["perm"]))
+    err = np.abs(f32(r["o"]) - o).max()
+    lerr = np.abs(npy(r["lse"]) - lse).max()
+    say(f"  1024 groups: max|O-O_oracle| = {err:.3e}, max|LSE-LSE_oracle| = {lerr:.3e}")
+    assert err <= 2e-2 and lerr <= LSE_TOL_BF16
+
+
 def test_pipeline_deterministic():
     q, k, v = _inputs(2, 4096, 128, "bf16", seed=11)
     a = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), 16, 64, 5, 400, 400, seed=3)
