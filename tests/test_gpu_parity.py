@@ -61,7 +61,8 @@ def _near_tie_ok(orc, x, cent, lab_gpu, lab_orc, tol=1e-5):
 
 
 @pytest.mark.parametrize("dtype,d,N,C", [("f32", 64, 2048, 8), ("f32", 64, 2048, 32), ("bf16", 128, 3000, 50),
-                                         ("bf16", 16, 1500, 256), ("bf16", 64, 777, 13), ("bf16", 128, 300, 2)])
+                                         ("bf16", 16, 1500, 256), ("bf16", 64, 777, 13), ("bf16", 128, 300, 2),
+                                         ("bf16", 128, 8192, 4096)])
 def test_cluster_one_round_stagewise(orc, dtype, d, N, C):
     """Assign given identical centroids (near-tie rule); update given identical labels;
     stable permutation and offsets bit-exact given the labels; gathers exact."""
