@@ -335,9 +335,11 @@ def main():
     qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
     scale = isg.default_scale(d)
     stream = torch.cuda.current_stream()
-    ws_c = torch.empty(isg.cluster_workspace_size(B, H, N, d, max(w["Cq"], w["Ck"])), device=dev, dtype=torch.uint8)
+    # Q's clustering runs on a second stream beside K's, each with its own workspace
+    ws_q = torch.empty(isg.cluster_workspace_size(B, H, N, d, w["Cq"]), device=dev, dtype=torch.uint8)
+    ws_k = torch.empty(isg.cluster_workspace_size(B, H, N, d, w["Ck"]), device=dev, dtype=torch.uint8)
     ws_a = torch.empty(isg.attention_workspace_size(B, H, N, w["Cq"], w["Ck"]), device=dev, dtype=torch.uint8)
-    stages = ["cluster_q", "cluster_k", "probs"] + (["pq_codes", "pq_votes"] if mode == "votes" else []) + [
+    stages = ["cluster_q_and_k", "probs"] + (["pq_codes", "pq_votes"] if mode == "votes" else []) + [
         "select_sample", "attention", "unpermute"]
     ev = {s: [] for s in stages}
 
@@ -345,15 +347,12 @@ def main():
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
         if record:
             marks[0].record(stream)
-        cq = isg.isg_cluster(qg, w["Cq"], w["iters"], workspace=ws_c)
+        cq, ck = isg.cluster_qk(qg, kg, vg, w["Cq"], w["Ck"], w["iters"], ws_q=ws_q, ws_k=ws_k, stream=stream)
         if record:
             marks[1].record(stream)
-        ck = isg.isg_cluster(kg, w["Ck"], w["iters"], companion=vg, workspace=ws_c)
-        if record:
-            marks[2].record(stream)
         S, pi = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale,
                               want_pi=args.top_p is not None)
-        mi = 3
+        mi = 2
         if record:
             marks[mi].record(stream)
         votes = None

@@ -146,6 +146,49 @@ def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, work
                 companion_perm=comp_perm)
 
 
+_side_streams = {}
+
+
+def _side_stream(device):
+    """A second stream of default priority per device (Q's clustering runs on it)."""
+    key = torch.device(device).index
+    if key is None:
+        key = torch.cuda.current_device()
+    s = _side_streams.get(key)
+    if s is None:
+        s = _side_streams[key] = torch.cuda.Stream(device=key)
+    return s
+
+
+def cluster_qk(q, k, v, Cq, Ck, iters, *, ws_q=None, ws_k=None, stream=None):
+    """isg_cluster of Q and of K (companion V), Q's on a second stream beside K's.
+
+    Both start after the work already queued on ``stream`` (default: the current
+    stream), and ``stream`` waits for both before this returns.  The calls share
+    nothing but their inputs, so the results equal two calls in a row.  Every
+    tensor Q's call returns is marked as used on ``stream``, so the caching
+    allocator does not hand its memory to later side-stream work too early."""
+    main = stream if stream is not None else torch.cuda.current_stream(q.device)
+    side = _side_stream(q.device)
+    ready = torch.cuda.Event()
+    ready.record(main)
+    side.wait_event(ready)
+    with torch.cuda.stream(side):
+        cq = isg_cluster(q, Cq, iters, workspace=ws_q, stream=side)
+    q.record_stream(side)
+    if ws_q is not None:
+        ws_q.record_stream(side)
+    with torch.cuda.stream(main):
+        ck = isg_cluster(k, Ck, iters, companion=v, workspace=ws_k, stream=main)
+    done = torch.cuda.Event()
+    done.record(side)
+    main.wait_event(done)
+    for t in cq.values():
+        if t is not None:
+            t.record_stream(main)
+    return cq, ck
+
+
 def isg_probs(cq, ck, k_offsets, scale, *, want_pi=True, stream=None):
     _dev(cq, "cq"); _dev(ck, "ck"); _dev(k_offsets, "k_offsets")
     B, H, Cq, d = cq.shape
@@ -304,14 +347,13 @@ def default_scale(d: int) -> float:
 
 def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0, call_id=0, scale=None,
              pq=None, top_p=None, stream=None):
-    """All steps on one batch: cluster Q, cluster K (+V), probs, [PQ votes],
-    select/sample, attention, unpermute.  ``pq=(P, Cc)`` is required by
+    """All steps on one batch: cluster Q and K (+V) side by side on two streams,
+    probs, [PQ votes], select/sample, attention, unpermute.  ``pq=(P, Cc)`` is required by
     mode "votes"; ``top_p`` sizes the exact set by mass instead of
     ``exact_keys``.  Returns every intermediate (all on the GPU)."""
     d = q.shape[-1]
     scale = default_scale(d) if scale is None else scale
-    cq = isg_cluster(q, Cq, iters, stream=stream)
-    ck = isg_cluster(k, Ck, iters, companion=v, stream=stream)
+    cq, ck = cluster_qk(q, k, v, Cq, Ck, iters, stream=stream)
     scores, pi = isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, stream=stream)
     pqr = None
     if (MODES[mode] if isinstance(mode, str) else int(mode)) == MODES["votes"]:
