@@ -642,6 +642,20 @@ struct PPTile {
     bool active;
 };
 
+// K Q^T accumulators set to a tile's column offsets: lane holds keys
+// k2*32 + 8g + 4hl + e (e = 0..3) of its query.
+__device__ __forceinline__ void load_offsets(f32x16 *sacc, const float *bias, int hl)
+{
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 bv = *reinterpret_cast<const f32x4 *>(&bias[k2 * 32 + g * 8 + hl * 4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sacc[k2][4 * g + e] = bv[e];
+        }
+}
+
 // One phase of one half.  SLOT parity and buffer parities are compile-time
 // functions of (J, HALF); the tile index is runtime.
 template <int D, int HALF, int J>
@@ -690,17 +704,8 @@ __device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0
                     dst = *reinterpret_cast<const bf16x8 *>(kc + kswz<D>(k2 * 32 + l32, s * 2 + hl) * 16);
                 }
             };
-            // the K Q^T accumulator starts at tile t's column offsets (score units);
-            // lane holds keys k2*32 + 8g + 4hl + e (e = 0..3) of its query
-            const float *bias = ring_bias[(slot / 2) % kPPRing];
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const f32x4 bv = *reinterpret_cast<const f32x4 *>(&bias[k2 * 32 + g * 8 + hl * 4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sacc[k2][4 * g + e] = bv[e];
-                }
+            // the K Q^T accumulator already holds tile t's column offsets (read at the
+            // end of this wave's previous weight slot, or in the prologue for t = 0)
             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int j = 0; j < kPPAhead; ++j) load(j, opnd[j]);
@@ -765,9 +770,16 @@ __device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0
                     for (int e = 0; e < 8; ++e)
                         pb[s][e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], scale_log2, mneg));
             }
+            // the next product slot's K Q^T accumulator starts at tile u+1's column
+            // offsets (score units), read here where the slot has time to spare
+            // instead of ahead of its first product
+            load_offsets(sacc, ring_bias[(u + 1) % kPPRing], hl);
             // this slot's direct loads stay in flight; everything older has landed
             pp_barrier<2 * NDMA + 2>();
         } else {
+            // before a half's first product slot this is tile 0's offsets; after its
+            // last one the value is not used
+            load_offsets(sacc, ring_bias[0], hl);
             pp_barrier<0>();
         }
     }
@@ -810,10 +822,8 @@ __device__ __forceinline__ void pp_chunks(int nchunks, const PPTile<D> &tt, uint
     for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pb[s][e] = (__bf16)0.0f;
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[k2][r] = 0.0f;
+    // the first product slot's K Q^T accumulator starts at tile 0's offsets
+    load_offsets(sacc, ring_bias[0], hl);
     // A operand of the row-sum product: row 0 (lanes 0 and 32) all ones
     bf16x8 ones_a;
 #pragma unroll
