@@ -5,8 +5,8 @@
 // k-means on the raw vectors, strided init, ties to the lowest index, empty
 // clusters keep their centroid; the permutation is the stable sort by label.
 //
-// Per round: assign (labels) -> per-chunk histograms -> per-head scan ->
-// stable scatter (perm, offsets) -> segmented fp64 mean in sorted order
+// Per round: assign (labels) -> per-chunk histograms -> scan over chunks ->
+// label offsets + stable scatter (perm, offsets) -> segmented fp64 mean in sorted order
 // (centroids).  No float atomics: every output is deterministic.
 #include <type_traits>
 
@@ -165,76 +165,135 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t *labels, int N,
     __shared__ int hs[kMaxC];
     const int chunk = blockIdx.x, bh = blockIdx.y;
     for (int c = threadIdx.x; c < C; c += 256) hs[c] = 0;
+    // the chunk's labels, all loads in flight before the first count
+    constexpr int kPer = kSortChunk / 256;
+    int lab[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int t = chunk * kSortChunk + u * 256 + threadIdx.x;
+        lab[u] = t < N ? labels[(int64_t)bh * N + t] : -1;
+    }
     __syncthreads();
-    const int t0 = chunk * kSortChunk, t1 = min(N, t0 + kSortChunk);
-    for (int t = t0 + threadIdx.x; t < t1; t += 256) atomicAdd(&hs[labels[(int64_t)bh * N + t]], 1);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+        if (lab[u] >= 0) atomicAdd(&hs[lab[u]], 1);
     __syncthreads();
     int32_t *out = hist + ((int64_t)bh * nchunks + chunk) * C;
     for (int c = threadIdx.x; c < C; c += 256) out[c] = hs[c];
 }
 
-// hist[bh][chunk][c] -> first sorted row of (chunk, c); offsets = prefix of counts;
-// poff = prefix of the number of prow-row pieces of every group.
-__global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, int C, int prow,
-                                                   int32_t *offsets, int32_t *poff)
+// hist[bh][chunk][c] -> number of tokens with label c in the chunks before this
+// one; tot[bh][c] = number of tokens with label c.  One lane per label: the four
+// waves of a work-group take consecutive quarters of the chunks, sum them, and
+// each then rewrites its quarter starting from the sum of the quarters before.
+__global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, int C, int32_t *tot)
 {
-    __shared__ int cnt[kMaxC];
-    __shared__ int pcs[kMaxC];
-    __shared__ int tmp[256];
-    const int bh = blockIdx.x;
-    int32_t *hb = hist + (int64_t)bh * nchunks * C;
-    // the chunk counts of a label are read 8 at a time before any is rewritten, so
-    // the loads of a batch overlap instead of waiting on the store before them
-    constexpr int kB = 8;
-    for (int c = threadIdx.x; c < C; c += 256) {
-        int run = 0;
-        for (int ch0 = 0; ch0 < nchunks; ch0 += kB) {
+    constexpr int kB = 8;  // loads in flight per lane
+    __shared__ int part[4][64];
+    const int bh = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * 64 + lane;
+    const int q = (nchunks + 3) / 4;
+    const int ch0 = min(nchunks, wave * q), ch1 = min(nchunks, ch0 + q);
+    int32_t *hc = hist + (int64_t)bh * nchunks * C + c;
+    int sum = 0;
+    if (c < C)
+        for (int a = ch0; a < ch1; a += kB) {
             int v[kB];
 #pragma unroll
-            for (int u = 0; u < kB; ++u) v[u] = ch0 + u < nchunks ? hb[(int64_t)(ch0 + u) * C + c] : 0;
+            for (int u = 0; u < kB; ++u) v[u] = a + u < ch1 ? hc[(int64_t)(a + u) * C] : 0;
 #pragma unroll
-            for (int u = 0; u < kB; ++u)
-                if (ch0 + u < nchunks) {
-                    hb[(int64_t)(ch0 + u) * C + c] = run;
-                    run += v[u];
-                }
+            for (int u = 0; u < kB; ++u) sum += v[u];
         }
-        cnt[c] = run;
-        pcs[c] = (run + prow - 1) / prow;
-    }
+    part[wave][lane] = sum;
     __syncthreads();
-    const int total = block_exclusive_scan_int(cnt, C, tmp);
-    const int ptotal = block_exclusive_scan_int(pcs, C, tmp);
-    int32_t *ob = offsets + (int64_t)bh * (C + 1);
-    int32_t *pb = poff + (int64_t)bh * (C + 1);
-    for (int c = threadIdx.x; c < C; c += 256) {
-        ob[c] = cnt[c];
-        pb[c] = pcs[c];
-        const int add = cnt[c];
-        for (int ch0 = 0; ch0 < nchunks; ch0 += kB) {
-            int v[kB];
+    if (c >= C) return;
+    int run = 0;
+    for (int w = 0; w < wave; ++w) run += part[w][lane];
+    if (wave == 3) tot[(int64_t)bh * C + c] = run + sum;
+    for (int a = ch0; a < ch1; a += kB) {
+        int v[kB];
 #pragma unroll
-            for (int u = 0; u < kB; ++u) v[u] = ch0 + u < nchunks ? hb[(int64_t)(ch0 + u) * C + c] : 0;
+        for (int u = 0; u < kB; ++u) v[u] = a + u < ch1 ? hc[(int64_t)(a + u) * C] : 0;
 #pragma unroll
-            for (int u = 0; u < kB; ++u)
-                if (ch0 + u < nchunks) hb[(int64_t)(ch0 + u) * C + c] = v[u] + add;
-        }
-    }
-    if (threadIdx.x == 0) {
-        ob[C] = total;
-        pb[C] = ptotal;
+        for (int u = 0; u < kB; ++u)
+            if (a + u < ch1) {
+                hc[(int64_t)(a + u) * C] = run;
+                run += v[u];
+            }
     }
 }
 
-// One wave per chunk walks its tokens in order, 64 at a time; a token's rank
-// among equal labels of the same step comes from ballots over the label bits.
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, const int32_t *base, int N,
-                                                     int C, int nchunks, int bits, int32_t *perm)
+// One wave per chunk.  It first turns the label counts into label offsets (the
+// exclusive prefix over labels, lane l taking a contiguous run of labels) and
+// adds the chunk's per-label base, so run[c] is the first sorted row of
+// (chunk, c); the wave of chunk 0 also writes offsets and poff (the prefix of
+// the number of prow-row pieces per group).  It then walks its tokens in order,
+// 64 at a time; a token's rank among equal labels of the same step comes from
+// ballots over the label bits.
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, const int32_t *base,
+                                                     const int32_t *tot, int N, int C, int nchunks, int bits,
+                                                     int prow, int32_t *perm, int32_t *offsets, int32_t *poff)
 {
     __shared__ int run[kMaxC];
     const int chunk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
     const int32_t *bb = base + ((int64_t)bh * nchunks + chunk) * C;
-    for (int c = lane; c < C; c += 64) run[c] = bb[c];
+    const int32_t *tb = tot + (int64_t)bh * C;
+    constexpr int kB = 8;
+    for (int c0 = lane; c0 < C; c0 += 64 * kB) {
+        int v[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) v[u] = c0 + 64 * u < C ? tb[c0 + 64 * u] : 0;
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+            if (c0 + 64 * u < C) run[c0 + 64 * u] = v[u];
+    }
+    __syncthreads();
+    {
+        const int S = (C + 63) / 64, l0 = min(C, lane * S), l1 = min(C, l0 + S);
+        int ls = 0, lp = 0;
+        for (int c = l0; c < l1; ++c) {
+            const int n = run[c];
+            ls += n;
+            lp += (n + prow - 1) / prow;
+        }
+        int xs = ls, xp = lp;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int ys = __shfl_up(xs, off), yp = __shfl_up(xp, off);
+            if (lane >= off) {
+                xs += ys;
+                xp += yp;
+            }
+        }
+        int os = xs - ls, op = xp - lp;
+        const bool first = chunk == 0;
+        int32_t *ob = offsets + (int64_t)bh * (C + 1);
+        int32_t *pb = poff + (int64_t)bh * (C + 1);
+        for (int c = l0; c < l1; ++c) {
+            const int n = run[c];
+            run[c] = os;
+            if (first) {
+                ob[c] = os;
+                pb[c] = op;
+            }
+            os += n;
+            op += (n + prow - 1) / prow;
+        }
+        // lane 63 ends on the totals (its run of labels may be empty)
+        if (first && lane == 63) {
+            ob[C] = os;
+            pb[C] = op;
+        }
+    }
+    __syncthreads();
+    for (int c0 = lane; c0 < C; c0 += 64 * kB) {
+        int v[kB];
+#pragma unroll
+        for (int u = 0; u < kB; ++u) v[u] = c0 + 64 * u < C ? bb[c0 + 64 * u] : 0;
+#pragma unroll
+        for (int u = 0; u < kB; ++u)
+            if (c0 + 64 * u < C) run[c0 + 64 * u] += v[u];
+    }
     __syncthreads();
     const int t0 = chunk * kSortChunk;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -802,7 +861,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 }
 
 struct ClusterWs {
-    size_t off_hist, off_planes, off_norms, off_aug, off_poff, off_partial, total;
+    size_t off_hist, off_tot, off_planes, off_norms, off_aug, off_poff, off_partial, total;
     int Cpad, maxp;
 };
 
@@ -815,6 +874,7 @@ ClusterWs cluster_ws(int B, int H, int N, int d, int C)
     w.maxp = (N + piece_rows(d) - 1) / piece_rows(d) + C;  // >= sum over groups of ceil(n_j / piece rows)
     size_t o = 0;
     w.off_hist = o; o += isg_align256(BH * nchunks * C * sizeof(int32_t));
+    w.off_tot = o; o += isg_align256(BH * C * sizeof(int32_t));
     w.off_planes = o; o += isg_align256(BH * 2 * w.Cpad * d * sizeof(uint16_t));
     w.off_norms = o; o += isg_align256(BH * w.Cpad * sizeof(float));
     w.off_aug = o; o += isg_align256(BH * w.Cpad * 16 * sizeof(uint16_t));
@@ -850,6 +910,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     const int nchunks = (N + kSortChunk - 1) / kSortChunk;
     const ClusterWs w = cluster_ws(B, H, N, D, C);
     int32_t *hist = (int32_t *)(ws + w.off_hist);
+    int32_t *tot = (int32_t *)(ws + w.off_tot);
     int32_t *poff = (int32_t *)(ws + w.off_poff);
     double *partial = (double *)(ws + w.off_partial);
     int bits = 1;
@@ -862,8 +923,9 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     for (int it = 0; it < iters; ++it) {
         launch_assign<T, D>(st, x, xs, B, H, N, C, cent, labels, ws, w);
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
-        scan_kernel<<<BH, 256, 0, st>>>(hist, nchunks, C, piece_rows(D), offsets, poff);
-        scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, N, C, nchunks, bits, perm);
+        scan_kernel<<<dim3((C + 63) / 64, BH), 256, 0, st>>>(hist, nchunks, C, tot);
+        scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, tot, N, C, nchunks, bits, piece_rows(D),
+                                                         perm, offsets, poff);
         // the last iteration's update also writes the permuted copy of x
         update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
                                                                     partial, it + 1 == iters ? x_perm : nullptr);
