@@ -238,8 +238,28 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
     const int chunk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
     const int32_t *bb = base + ((int64_t)bh * nchunks + chunk) * C;
     const int32_t *tb = tot + (int64_t)bh * C;
+    // Loads in issue order: the first batch of label counts and of the chunk's
+    // bases, then the chunk's labels, so that one wait covers the counts and the
+    // others stay in flight through the label scan.
     constexpr int kB = 8;
-    for (int c0 = lane; c0 < C; c0 += 64 * kB) {
+    int tv[kB], bv[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+        const int c = lane + 64 * u;
+        tv[u] = c < C ? tb[c] : 0;
+        bv[u] = c < C ? bb[c] : 0;
+    }
+    const int t0 = chunk * kSortChunk;
+    int labs[kSortChunk / 64];
+#pragma unroll
+    for (int step = 0; step < kSortChunk / 64; ++step) {
+        const int t = t0 + step * 64 + lane;
+        labs[step] = t < N ? labels[(int64_t)bh * N + t] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+        if (lane + 64 * u < C) run[lane + 64 * u] = tv[u];
+    for (int c0 = lane + 64 * kB; c0 < C; c0 += 64 * kB) {
         int v[kB];
 #pragma unroll
         for (int u = 0; u < kB; ++u) v[u] = c0 + 64 * u < C ? tb[c0 + 64 * u] : 0;
@@ -286,7 +306,10 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
         }
     }
     __syncthreads();
-    for (int c0 = lane; c0 < C; c0 += 64 * kB) {
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+        if (lane + 64 * u < C) run[lane + 64 * u] += bv[u];
+    for (int c0 = lane + 64 * kB; c0 < C; c0 += 64 * kB) {
         int v[kB];
 #pragma unroll
         for (int u = 0; u < kB; ++u) v[u] = c0 + 64 * u < C ? bb[c0 + 64 * u] : 0;
@@ -295,15 +318,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
             if (c0 + 64 * u < C) run[c0 + 64 * u] += v[u];
     }
     __syncthreads();
-    const int t0 = chunk * kSortChunk;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    // the chunk's labels, all loads in flight at once
-    int labs[kSortChunk / 64];
-#pragma unroll
-    for (int step = 0; step < kSortChunk / 64; ++step) {
-        const int t = t0 + step * 64 + lane;
-        labs[step] = t < N ? labels[(int64_t)bh * N + t] : 0;
-    }
 #pragma unroll
     for (int step = 0; step < kSortChunk / 64; ++step) {
         const int t = t0 + step * 64 + lane;
