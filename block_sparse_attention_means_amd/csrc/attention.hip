@@ -662,7 +662,7 @@ template <int D, int HALF, int J>
 __device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0, uint8_t *k1, uint8_t *v0,
                                          uint8_t *v1, int (*ring_row)[kTK], float (*ring_bias)[kTK],
                                          const uint16_t *kh, const uint16_t *vh, const bf16x8 *qf, f32x16 *oacc,
-                                         f32x16 *sacc, bf16x8 *pb, f32x16 &lacc, const bf16x8 &ones_a,
+                                         f32x16 *sacc, bf16x8 *pb, f32x4 &lacc, const bf16x8 &ones_a,
                                          const int *zrow, float m_ref, const int *vtr, float scale_log2,
                                          bool wave_active, int wq, int lane, int hl, int l32)
 {
@@ -723,10 +723,12 @@ __device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0
                     const int k2 = i & 1, s = i >> 1;
                     sacc[k2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(opnd[j % R], qf[s], sacc[k2], 0, 0, 0);
                 }
-                // row sums of the weights: a product with A = 1 in row 0, so row 0 of
-                // lacc (lanes 0-31) accumulates the sum over keys of each query
+                // row sums of the weights: the 16 keys x 32 queries of pb[s], read as the
+                // B operand of a 16x16x32 product, hold queries n and n + 16 in
+                // alternate 8-key blocks; an A with ones in those blocks for rows 0 and
+                // 1 sums both at half the cost of a 32x32x16 product
                 if ((j & 7) == 7)
-                    lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones_a, pb[j >> 3], lacc, 0, 0, 0);
+                    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones_a, pb[j >> 3], lacc, 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_setprio(0);
@@ -789,7 +791,7 @@ template <int D, int HALF>
 __device__ __forceinline__ void pp_chunks(int nchunks, const PPTile<D> &tt, uint8_t *k0, uint8_t *k1, uint8_t *v0,
                                           uint8_t *v1, int (*ring_row)[kTK], float (*ring_bias)[kTK],
                                           int *zrow, const uint16_t *kh, const uint16_t *vh, const bf16x8 *qf,
-                                          f32x16 *oacc, f32x16 &lacc, float m_ref, const int *vtr, float scale_log2,
+                                          f32x16 *oacc, f32x4 &lacc, float m_ref, const int *vtr, float scale_log2,
                                           bool wave_active, int wq, int lane, int hl, int l32)
 {
     constexpr int KB = kTK * D * 2;
@@ -824,10 +826,13 @@ __device__ __forceinline__ void pp_chunks(int nchunks, const PPTile<D> &tt, uint
         for (int e = 0; e < 8; ++e) pb[s][e] = (__bf16)0.0f;
     // the first product slot's K Q^T accumulator starts at tile 0's offsets
     load_offsets(sacc, ring_bias[0], hl);
-    // A operand of the row-sum product: row 0 (lanes 0 and 32) all ones
+    // A operand of the row-sum product (16x16x32: lane l holds row l % 16, k block
+    // l / 16): row 0 is one on k blocks 0 and 2 (query n of the 32x32x16 B layout),
+    // row 1 on blocks 1 and 3 (query n + 16)
     bf16x8 ones_a;
+    const bool one = (lane & 15) == ((lane >> 4) & 1);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ones_a[e] = (__bf16)(l32 == 0 ? 1.0f : 0.0f);
+    for (int e = 0; e < 8; ++e) ones_a[e] = (__bf16)(one ? 1.0f : 0.0f);
     for (int c = 0; c < nchunks; ++c) {
         pp_phase<D, HALF, 0>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
                              zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
@@ -926,9 +931,7 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.0f;
-    f32x16 lacc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lacc[r] = 0.0f;
+    f32x4 lacc = {0.0f, 0.0f, 0.0f, 0.0f};
     // each half names its own buffers, so the compiler sees which LDS object every
     // direct load writes and every product reads; both paths pass 4 * nchunks barriers
     if (half == 0)
@@ -939,7 +942,10 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
                         vtr, scale_log2, wave_active, wq, lane, hl, l32);
 
     if (!wave_active) return;
-    const float l_tot = lacc[0] + __shfl_xor(lacc[0], 32);  // row 0 lives in lanes 0-31
+    // rows 0 and 1 of the row-sum product live in lanes 0-15: the sums of queries
+    // 0-15 and 16-31
+    const float ls0 = __shfl(lacc[0], l32 & 15), ls1 = __shfl(lacc[1], l32 & 15);
+    const float l_tot = l32 < 16 ? ls0 : ls1;
     const int qrow_raw = tt.r0 + wq * 32 + l32;
     if (__any(qrow_raw < tt.r1 && !(l_tot >= 8.271806e-25f))) {  // 2^-80: hand the tile to the fallback
         if (lane == 0) redo[tt.lb] = 1;
