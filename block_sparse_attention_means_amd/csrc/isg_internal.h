@@ -58,56 +58,57 @@ __device__ __forceinline__ int xcd_logical_block(int p, int nblocks)
     return (p & 7) * (nblocks >> 3) + (p >> 3);
 }
 
-// Exclusive block scan over `n` ints held in shared memory `a` (in place), using
-// `tmp` (>= blockDim.x ints) as scratch.  Returns the total.  All threads call it.
-__device__ __forceinline__ int block_exclusive_scan_int(int *a, int n, int *tmp)
+// Inclusive prefix sum across the 64 lanes of a wave.
+template <typename V>
+__device__ __forceinline__ V wave_inclusive_scan(V x)
 {
-    const int T = blockDim.x, tid = threadIdx.x;
-    const int per = (n + T - 1) / T;
-    const int lo = tid * per, hi = min(n, lo + per);
-    int s = 0;
-    for (int k = lo; k < hi; ++k) s += a[k];
-    tmp[tid] = s;
-    __syncthreads();
-    for (int off = 1; off < T; off <<= 1) {
-        int v = tid >= off ? tmp[tid - off] : 0;
-        __syncthreads();
-        tmp[tid] += v;
-        __syncthreads();
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const V y = __shfl_up(x, off);
+        if (lane >= off) x += y;
     }
-    int run = tmp[tid] - s;
+    return x;
+}
+
+// Exclusive block scan over `n` values held in shared memory `a` (in place).
+// Thread t takes a contiguous run of ceil(n / blockDim.x) values; the runs' sums
+// are scanned within each wave by shuffles and across waves through `tmp`
+// (>= blockDim.x / 64 entries).  blockDim.x must be a multiple of 64.  Returns
+// the total.  All threads call it.
+template <typename V>
+__device__ __forceinline__ V block_exclusive_scan(V *a, int n, V *tmp)
+{
+    const int T = blockDim.x, tid = threadIdx.x, wave = tid >> 6, nw = T >> 6;
+    const int per = (n + T - 1) / T;
+    const int lo = min(n, tid * per), hi = min(n, lo + per);
+    V s = 0;
+    for (int k = lo; k < hi; ++k) s += a[k];
+    const V incl = wave_inclusive_scan(s);
+    if ((tid & 63) == 63) tmp[wave] = incl;
+    __syncthreads();
+    V base = 0, total = 0;
+    for (int w = 0; w < nw; ++w) {
+        const V t = tmp[w];
+        if (w < wave) base += t;
+        total += t;
+    }
+    V run = base + incl - s;
     for (int k = lo; k < hi; ++k) {
-        int v = a[k];
+        const V v = a[k];
         a[k] = run;
         run += v;
     }
-    int total = tmp[T - 1];
     __syncthreads();
     return total;
 }
 
+__device__ __forceinline__ int block_exclusive_scan_int(int *a, int n, int *tmp)
+{
+    return block_exclusive_scan<int>(a, n, tmp);
+}
+
 __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t *a, int n, uint64_t *tmp)
 {
-    const int T = blockDim.x, tid = threadIdx.x;
-    const int per = (n + T - 1) / T;
-    const int lo = tid * per, hi = min(n, lo + per);
-    uint64_t s = 0;
-    for (int k = lo; k < hi; ++k) s += a[k];
-    tmp[tid] = s;
-    __syncthreads();
-    for (int off = 1; off < T; off <<= 1) {
-        uint64_t v = tid >= off ? tmp[tid - off] : 0;
-        __syncthreads();
-        tmp[tid] += v;
-        __syncthreads();
-    }
-    uint64_t run = tmp[tid] - s;
-    for (int k = lo; k < hi; ++k) {
-        uint64_t v = a[k];
-        a[k] = run;
-        run += v;
-    }
-    uint64_t total = tmp[T - 1];
-    __syncthreads();
-    return total;
+    return block_exclusive_scan<uint64_t>(a, n, tmp);
 }

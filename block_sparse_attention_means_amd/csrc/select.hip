@@ -101,22 +101,59 @@ __device__ __forceinline__ uint64_t scale128(uint64_t hi, uint64_t lo, uint64_t 
     return a1 + (mid < a0 ? 1 : 0);
 }
 
+// Per-work-group arrays in dynamic LDS, each P2 long (Ck rounded up to a power of
+// two), plus block-scan and reduction scratch.
 struct SelShared {
-    int order[kMaxGroups];
-    int n[kMaxGroups];
-    float S[kMaxGroups];
-    float P[kMaxGroups];    // pi (top-p rule)
-    int votes[kMaxGroups];
-    int flag[kMaxGroups];   // 1 = exact
-    int buf[kMaxGroups];    // scan scratch (ints)
-    int tmp[kThreads];
-    uint64_t W[kMaxGroups];      // compacted skipped weights -> exclusive prefix
-    uint64_t tmp64[kThreads];
-    int sk_group[kMaxGroups];    // compacted skipped group ids (ascending)
-    uint32_t sk_u[kMaxGroups];
-    float red_f[kThreads];
-    int red_i[kThreads];
+    uint64_t *W;       // rank keys, then compacted skipped weights -> exclusive prefix
+    uint64_t *tmp64;
+    int *order;
+    int *n;
+    float *S;
+    float *P;          // pi (top-p rule), then 1/u per skipped group
+    int *votes;        // votes, then the log weight per skipped group
+    int *flag;         // 1 = exact
+    int *buf;          // scan scratch (ints)
+    int *tmp;
+    int *sk_group;     // compacted skipped group ids (ascending)
+    uint32_t *sk_u;
+    float *red_f;
+    int *red_i;
 };
+
+__host__ __device__ inline int sel_p2(int Ck)
+{
+    int P2 = 1;
+    while (P2 < Ck) P2 <<= 1;
+    return P2;
+}
+
+__host__ __device__ inline size_t sel_lds_bytes(int Ck)
+{
+    const size_t P2 = (size_t)sel_p2(Ck);
+    return P2 * 8 + kThreads * 8 + 9 * P2 * 4 + 3 * kThreads * 4;
+}
+
+__device__ inline SelShared sel_carve(uint8_t *base, int P2)
+{
+    SelShared sh;
+    uint8_t *p = base;
+    auto take = [&](size_t bytes) { uint8_t *r = p; p += bytes; return r; };
+    sh.W = reinterpret_cast<uint64_t *>(take((size_t)P2 * 8));
+    sh.tmp64 = reinterpret_cast<uint64_t *>(take(kThreads * 8));
+    sh.order = reinterpret_cast<int *>(take((size_t)P2 * 4));
+    sh.n = reinterpret_cast<int *>(take((size_t)P2 * 4));
+    sh.S = reinterpret_cast<float *>(take((size_t)P2 * 4));
+    sh.P = reinterpret_cast<float *>(take((size_t)P2 * 4));
+    sh.votes = reinterpret_cast<int *>(take((size_t)P2 * 4));
+    sh.flag = reinterpret_cast<int *>(take((size_t)P2 * 4));
+    sh.buf = reinterpret_cast<int *>(take((size_t)P2 * 4));
+    sh.sk_group = reinterpret_cast<int *>(take((size_t)P2 * 4));
+    sh.sk_u = reinterpret_cast<uint32_t *>(take((size_t)P2 * 4));
+    sh.tmp = reinterpret_cast<int *>(take(kThreads * 4));
+    sh.red_f = reinterpret_cast<float *>(take(kThreads * 4));
+    sh.red_i = reinterpret_cast<int *>(take(kThreads * 4));
+    return sh;
+}
 
 // Ranking of non-empty groups: (S desc, j asc); (votes desc, S desc, j asc) in
 // votes mode; (pi desc, j asc) under the top-p rule.  Empty groups sort last.
@@ -170,14 +207,14 @@ __global__ __launch_bounds__(kThreads) void select_sample_kernel(
     int32_t *exact_groups, int32_t *n_exact, int32_t *sample_idx, float *sample_bias, int32_t *n_sample)
 {
     const bool topp = pi != nullptr;
-    __shared__ SelShared sh;
+    extern __shared__ __attribute__((aligned(16))) uint8_t sel_lds[];
     const int tid = threadIdx.x;
     const int64_t gi = blockIdx.x;
     const int64_t bh = gi / Cq;
     const int i = (int)(gi % Cq), h = (int)(bh % H), b = (int)(bh / H);
     const int32_t *ko = k_offsets + bh * (Ck + 1);
-    int P2 = 1;
-    while (P2 < Ck) P2 <<= 1;
+    const int P2 = sel_p2(Ck);
+    const SelShared sh = sel_carve(sel_lds, P2);
     for (int j = tid; j < P2; j += kThreads) {
         sh.order[j] = j;
         if (j < Ck) {
@@ -399,7 +436,7 @@ extern "C" isg_status isg_select_sample(void *stream, const float *scores, const
     ProposalTable tbl;
     isg_proposal_table(tbl.v);
     hipStream_t st = (hipStream_t)stream;
-    select_sample_kernel<<<(unsigned)G, kThreads, 0, st>>>(scores, nullptr, 0.0, k_offsets, votes, H, Cq, Ck,
+    select_sample_kernel<<<(unsigned)G, kThreads, sel_lds_bytes(Ck), st>>>(scores, nullptr, 0.0, k_offsets, votes, H, Cq, Ck,
                                                            exact_keys, m, mode, seed, call_id, tbl, exact_groups,
                                                            n_exact, sample_idx, sample_bias, n_sample);
     return isg_check_launch("isg_select_sample");
@@ -428,7 +465,7 @@ extern "C" isg_status isg_select_sample_topp(void *stream, const float *scores, 
     ProposalTable tbl;
     isg_proposal_table(tbl.v);
     hipStream_t st = (hipStream_t)stream;
-    select_sample_kernel<<<(unsigned)G, kThreads, 0, st>>>(scores, pi, (double)top_p, k_offsets, nullptr, H, Cq,
+    select_sample_kernel<<<(unsigned)G, kThreads, sel_lds_bytes(Ck), st>>>(scores, pi, (double)top_p, k_offsets, nullptr, H, Cq,
                                                            Ck, 0, m, mode, seed, call_id, tbl, exact_groups,
                                                            n_exact, sample_idx, sample_bias, n_sample);
     return isg_check_launch("isg_select_sample_topp");
