@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
                                                      const int32_t *tot, int N, int C, int nchunks, int bits,
                                                      int prow, int32_t *perm, int32_t *offsets, int32_t *poff)
 {
-    __shared__ int run[kMaxC];
+    extern __shared__ int run[];  // C entries (dynamic, so small C lets more waves share a CU)
     const int chunk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
     const int32_t *bb = base + ((int64_t)bh * nchunks + chunk) * C;
     const int32_t *tb = tot + (int64_t)bh * C;
@@ -939,8 +939,8 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         launch_assign<T, D>(st, x, xs, B, H, N, C, cent, labels, ws, w);
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
         scan_kernel<<<dim3((C + 63) / 64, BH), 256, 0, st>>>(hist, nchunks, C, tot);
-        scatter_kernel<<<dim3(nchunks, BH), 64, 0, st>>>(labels, hist, tot, N, C, nchunks, bits, piece_rows(D),
-                                                         perm, offsets, poff);
+        scatter_kernel<<<dim3(nchunks, BH), 64, C * sizeof(int32_t), st>>>(labels, hist, tot, N, C, nchunks, bits,
+                                                                           piece_rows(D), perm, offsets, poff);
         // the last iteration's update also writes the permuted copy of x
         update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
                                                                     partial, it + 1 == iters ? x_perm : nullptr);
