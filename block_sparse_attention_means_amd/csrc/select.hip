@@ -22,52 +22,77 @@ constexpr int kMaxGroups = 1024;
 constexpr int kThreads = 256;
 
 // S_ij = fma-chain(cq_i . ck_j) * scale (fp32, k ascending); pi from S in fp64.
+// A work-group takes kQB query centroids of one head, so each key centroid's row
+// is read once for kQB chains; per row i the reductions are those of a one-row
+// work-group (thread t takes j = t, t + 256, ...), so the results do not depend
+// on kQB.
+constexpr int kQB = 4;
 __global__ __launch_bounds__(kThreads) void probs_kernel(const float *cq, const float *ck,
                                                          const int32_t *k_offsets, int Cq, int Ck, int d,
                                                          float scale, float *scores, float *pi)
 {
-    extern __shared__ float qs[];  // d floats
+    extern __shared__ float qs[];  // kQB rows of d floats
     __shared__ double red[kThreads];
     __shared__ float redf[kThreads];
-    const int64_t gi = blockIdx.x;  // bh*Cq + i
-    const int64_t bh = gi / Cq;
-    const float *qi = cq + gi * d;
-    for (int k = threadIdx.x; k < d; k += kThreads) qs[k] = qi[k];
+    const int nqb = (Cq + kQB - 1) / kQB;
+    const int64_t bh = blockIdx.x / nqb;
+    const int i0 = (int)(blockIdx.x % nqb) * kQB;
+    const int nq = min(kQB, Cq - i0);
+    const float *qi = cq + (bh * Cq + i0) * d;
+    for (int k = threadIdx.x; k < kQB * d; k += kThreads) qs[k] = k < nq * d ? qi[k] : 0.0f;
     __syncthreads();
     const int32_t *ko = k_offsets + bh * (Ck + 1);
-    float *S = scores + gi * Ck;
-    float lmax = -INFINITY;
+    float lmax[kQB];
+#pragma unroll
+    for (int r = 0; r < kQB; ++r) lmax[r] = -INFINITY;
     for (int j = threadIdx.x; j < Ck; j += kThreads) {
         const float *kj = ck + (bh * Ck + j) * d;
-        float acc = 0.0f;
-        for (int k = 0; k < d; ++k) acc = __fmaf_rn(qs[k], kj[k], acc);
-        const float s = __fmul_rn(acc, scale);
-        S[j] = s;
-        if (ko[j + 1] > ko[j]) lmax = fmaxf(lmax, s);
+        float acc[kQB];
+#pragma unroll
+        for (int r = 0; r < kQB; ++r) acc[r] = 0.0f;
+        for (int k = 0; k < d; ++k) {
+            const float kv = kj[k];
+#pragma unroll
+            for (int r = 0; r < kQB; ++r) acc[r] = __fmaf_rn(qs[r * d + k], kv, acc[r]);
+        }
+        const bool nonempty = ko[j + 1] > ko[j];
+#pragma unroll
+        for (int r = 0; r < kQB; ++r)
+            if (r < nq) {
+                const float s = __fmul_rn(acc[r], scale);
+                scores[(bh * Cq + i0 + r) * Ck + j] = s;
+                if (nonempty) lmax[r] = fmaxf(lmax[r], s);
+            }
     }
     if (!pi) return;
-    redf[threadIdx.x] = lmax;
-    __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (threadIdx.x < off) redf[threadIdx.x] = fmaxf(redf[threadIdx.x], redf[threadIdx.x + off]);
+#pragma unroll
+    for (int r = 0; r < kQB; ++r) {
+        if (r >= nq) break;  // uniform over the work-group
+        const int64_t gi = bh * Cq + i0 + r;
+        const float *S = scores + gi * Ck;
+        redf[threadIdx.x] = lmax[r];
         __syncthreads();
-    }
-    const double mx = (double)redf[0];
-    double part = 0.0;
-    for (int j = threadIdx.x; j < Ck; j += kThreads) {
-        const int nj = ko[j + 1] - ko[j];
-        if (nj > 0) part += (double)nj * exp((double)S[j] - mx);
-    }
-    red[threadIdx.x] = part;
-    __syncthreads();
-    for (int off = kThreads / 2; off > 0; off >>= 1) {
-        if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+        for (int off = kThreads / 2; off > 0; off >>= 1) {
+            if (threadIdx.x < off) redf[threadIdx.x] = fmaxf(redf[threadIdx.x], redf[threadIdx.x + off]);
+            __syncthreads();
+        }
+        const double mx = (double)redf[0];
+        double part = 0.0;
+        for (int j = threadIdx.x; j < Ck; j += kThreads) {
+            const int nj = ko[j + 1] - ko[j];
+            if (nj > 0) part += (double)nj * exp((double)S[j] - mx);
+        }
+        red[threadIdx.x] = part;
         __syncthreads();
-    }
-    const double tot = red[0];
-    for (int j = threadIdx.x; j < Ck; j += kThreads) {
-        const int nj = ko[j + 1] - ko[j];
-        pi[gi * Ck + j] = nj > 0 ? (float)((double)nj * exp((double)S[j] - mx) / tot) : 0.0f;
+        for (int off = kThreads / 2; off > 0; off >>= 1) {
+            if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+            __syncthreads();
+        }
+        const double tot = red[0];
+        for (int j = threadIdx.x; j < Ck; j += kThreads) {
+            const int nj = ko[j + 1] - ko[j];
+            pi[gi * Ck + j] = nj > 0 ? (float)((double)nj * exp((double)S[j] - mx) / tot) : 0.0f;
+        }
     }
 }
 
@@ -405,10 +430,10 @@ extern "C" isg_status isg_probs(void *stream, const float *cq, const float *ck, 
     ISG_REQUIRE(d >= 1 && d <= 1024, ISG_E_ARG, "isg_probs: d must be in [1, 1024]");
     ISG_REQUIRE(std::isfinite(scale), ISG_E_ARG, "isg_probs: scale must be finite");
     hipStream_t st = (hipStream_t)stream;
-    const int64_t G = (int64_t)B * H * Cq;
-    ISG_REQUIRE(G <= 0x7fffffff, ISG_E_ARG, "isg_probs: too many groups");
-    probs_kernel<<<(unsigned)G, kThreads, d * sizeof(float), st>>>(cq, ck, k_offsets, Cq, Ck, d, scale, scores,
-                                                                   pi);
+    const int64_t G = (int64_t)B * H * ((Cq + kQB - 1) / kQB);
+    ISG_REQUIRE((int64_t)B * H * Cq <= 0x7fffffff, ISG_E_ARG, "isg_probs: too many groups");
+    probs_kernel<<<(unsigned)G, kThreads, kQB * d * sizeof(float), st>>>(cq, ck, k_offsets, Cq, Ck, d, scale,
+                                                                         scores, pi);
     return isg_check_launch("isg_probs");
 }
 
