@@ -1108,8 +1108,9 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
                                     const int32_t *q_offsets, const int32_t *k_offsets,
                                     const int32_t *exact_groups, const int32_t *n_exact,
                                     const int32_t *sample_idx, const float *sample_bias,
-                                    const int32_t *n_sample, int m, float scale, void *o_p, float *lse_p,
-                                    void *workspace, size_t ws_bytes)
+                                    const int32_t *n_sample, int m, float scale,
+                                    const float *k_max_sqnorm, void *o_p, float *lse_p, void *workspace,
+                                    size_t ws_bytes)
 {
     ISG_REQUIRE(q_p && k_p && v_p && q_offsets && k_offsets && exact_groups && n_exact && n_sample && o_p,
                 ISG_E_ARG, "isg_attention: null pointer argument");
@@ -1144,6 +1145,9 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     int32_t *col_x = (int32_t *)(ws + Lq.off_x);
     float *col_bmax = (float *)(ws + Lq.off_bmax);
     int *kmax2 = (int *)(ws + Lq.off_kmax);
+    // the per-head largest squared key norm: the caller's (from isg_cluster of K),
+    // else the key-norm pass below fills the workspace copy
+    const int *kmx = k_max_sqnorm ? reinterpret_cast<const int *>(k_max_sqnorm) : kmax2;
     int *redo = (int *)(ws + Lq.off_redo);
     int4 *table = (int4 *)(ws + Lq.off_table);
     columns_kernel<<<(unsigned)G, 256, 0, st>>>(k_offsets, exact_groups, n_exact, sample_idx, sample_bias,
@@ -1154,13 +1158,13 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     if (dt == ISG_BF16) {
         const dim3 kgrid((unsigned)std::min((N + 255) / 256, 128), (unsigned)(B * H));
         if (d == 128) {
-            kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
+            if (!k_max_sqnorm) kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<128, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                  kmax2, scale_log2, o_p, lse_p, redo);
+                                  kmx, scale_log2, o_p, lse_p, redo);
         } else {
-            kmax_kernel<64><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
+            if (!k_max_sqnorm) kmax_kernel<64><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<64, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                 kmax2, scale_log2, o_p, lse_p, redo);
+                                 kmx, scale_log2, o_p, lse_p, redo);
         }
     } else {
         if (d == 128)

@@ -352,7 +352,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides xs, int H, int N, int C,
                                                            const int32_t *perm, const int32_t *offsets,
                                                            const int32_t *poff, int maxp, double *partial,
-                                                           T *x_perm)
+                                                           T *x_perm, float *pmax)
 {
     constexpr int TPR = D / 8;     // threads per row
     constexpr int RP = 256 / TPR;  // row slots
@@ -390,6 +390,31 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
         for (int i = 0; i < RPT; ++i)
             if (idx[i] >= 0) v[i].store(xp + (int64_t)(r0 + rs + i * RP) * D);
     }
+    // last k-means iteration, if asked: the largest squared norm of the piece's
+    // rows, in the key-norm pass's arithmetic (fp32 fma chain over a lane's 8
+    // elements, then a butterfly over the row's lanes), one value per piece (the
+    // final pass takes the head's maximum: no atomics on one shared line)
+    if (pmax) {
+        __shared__ float wmax[4];
+        float best = 0.0f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            float ss = 0.0f;
+            if (idx[i] >= 0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss = fmaf(v[i].get(e), v[i].get(e), ss);
+            }
+#pragma unroll
+            for (int off = TPR / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+            best = fmaxf(best, ss);
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+        if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
+        __syncthreads();
+        if (threadIdx.x == 0)
+            pmax[(int64_t)bh * maxp + q] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    }
     // fp64 sum of the slot's rows in sorted order
     double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -410,13 +435,25 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
 
 template <int D>
 __global__ __launch_bounds__(128) void update_final_kernel(int C, const int32_t *offsets, const int32_t *poff,
-                                                           int maxp, const double *partial, float *cent)
+                                                           int maxp, const double *partial, float *cent,
+                                                           const float *pmax, float *max_sqnorm)
 {
     const int j = blockIdx.x, bh = blockIdx.y;
+    const int32_t *pb = poff + (int64_t)bh * (C + 1);
+    if (pmax && j == 0) {
+        // the head's largest squared row norm: the maximum over its pieces
+        __shared__ float wmax[2];
+        float best = 0.0f;
+        for (int q = threadIdx.x; q < pb[C]; q += 128) best = fmaxf(best, pmax[(int64_t)bh * maxp + q]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) best = fmaxf(best, __shfl_xor(best, off));
+        if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = best;
+        __syncthreads();
+        if (threadIdx.x == 0) max_sqnorm[bh] = fmaxf(wmax[0], wmax[1]);
+    }
     const int32_t *ob = offsets + (int64_t)bh * (C + 1);
     const int n = ob[j + 1] - ob[j];
     if (n == 0) return;  // empty: keep the centroid
-    const int32_t *pb = poff + (int64_t)bh * (C + 1);
     for (int k = threadIdx.x; k < D; k += 128) {
         double sum = 0.0;
         for (int q = pb[j]; q < pb[j + 1]; ++q) sum += partial[((int64_t)bh * maxp + q) * D + k];
@@ -876,7 +913,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 }
 
 struct ClusterWs {
-    size_t off_hist, off_tot, off_planes, off_norms, off_aug, off_poff, off_partial, total;
+    size_t off_hist, off_tot, off_planes, off_norms, off_aug, off_poff, off_partial, off_pmax, total;
     int Cpad, maxp;
 };
 
@@ -895,6 +932,7 @@ ClusterWs cluster_ws(int B, int H, int N, int d, int C)
     w.off_aug = o; o += isg_align256(BH * w.Cpad * 16 * sizeof(uint16_t));
     w.off_poff = o; o += isg_align256(BH * (C + 1) * sizeof(int32_t));
     w.off_partial = o; o += isg_align256(BH * (size_t)w.maxp * d * sizeof(double));
+    w.off_pmax = o; o += isg_align256(BH * (size_t)w.maxp * sizeof(float));
     w.total = o;
     return w;
 }
@@ -919,7 +957,7 @@ void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, 
 template <typename T, int D>
 isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int N, int C, int iters,
                        int init_mode, const T *comp, float *cent, int32_t *labels, int32_t *perm,
-                       int32_t *offsets, T *x_perm, T *comp_perm, uint8_t *ws)
+                       int32_t *offsets, T *x_perm, T *comp_perm, float *max_sqnorm, uint8_t *ws)
 {
     const int BH = B * H;
     const int nchunks = (N + kSortChunk - 1) / kSortChunk;
@@ -928,6 +966,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     int32_t *tot = (int32_t *)(ws + w.off_tot);
     int32_t *poff = (int32_t *)(ws + w.off_poff);
     double *partial = (double *)(ws + w.off_partial);
+    float *pmax = (float *)(ws + w.off_pmax);
     int bits = 1;
     while ((1 << bits) < C) ++bits;
     if (init_mode == 0) {
@@ -936,6 +975,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         init_centroids_kernel<T><<<grid, 256, 0, st>>>(x, xs, H, N, C, D, cent, total);
     }
     for (int it = 0; it < iters; ++it) {
+        const bool last_norms = max_sqnorm && it + 1 == iters;
         launch_assign<T, D>(st, x, xs, B, H, N, C, cent, labels, ws, w);
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
         scan_kernel<<<dim3((C + 63) / 64, BH), 256, 0, st>>>(hist, nchunks, C, tot);
@@ -943,8 +983,10 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
                                                                            piece_rows(D), perm, offsets, poff);
         // the last iteration's update also writes the permuted copy of x
         update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
-                                                                    partial, it + 1 == iters ? x_perm : nullptr);
-        update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent);
+                                                                    partial, it + 1 == iters ? x_perm : nullptr,
+                                                                    last_norms ? pmax : nullptr);
+        update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent,
+                                                            last_norms ? pmax : nullptr, max_sqnorm);
     }
     if (comp_perm) {
         const int64_t total = (int64_t)BH * N * (D / 8);
@@ -957,18 +999,18 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
 template <typename T>
 isg_status dispatch_d(int d, hipStream_t st, const T *x, Strides xs, int B, int H, int N, int C,
                       int iters, int init_mode, const T *comp, float *cent, int32_t *labels,
-                      int32_t *perm, int32_t *offsets, T *x_perm, T *comp_perm, uint8_t *ws)
+                      int32_t *perm, int32_t *offsets, T *x_perm, T *comp_perm, float *max_sqnorm, uint8_t *ws)
 {
     switch (d) {
     case 16:
         return run_cluster<T, 16>(st, x, xs, B, H, N, C, iters, init_mode, comp, cent, labels, perm,
-                                  offsets, x_perm, comp_perm, ws);
+                                  offsets, x_perm, comp_perm, max_sqnorm, ws);
     case 64:
         return run_cluster<T, 64>(st, x, xs, B, H, N, C, iters, init_mode, comp, cent, labels, perm,
-                                  offsets, x_perm, comp_perm, ws);
+                                  offsets, x_perm, comp_perm, max_sqnorm, ws);
     case 128:
         return run_cluster<T, 128>(st, x, xs, B, H, N, C, iters, init_mode, comp, cent, labels, perm,
-                                   offsets, x_perm, comp_perm, ws);
+                                   offsets, x_perm, comp_perm, max_sqnorm, ws);
     default:
         return isg_fail(ISG_E_UNSUPPORTED, "isg_cluster: d=%d not built (16, 64, 128)", d);
     }
@@ -985,8 +1027,8 @@ extern "C" size_t isg_cluster_workspace_size(int B, int H, int N, int d, int C)
 extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
                                   int B, int H, int N, int d, int C, int iters, int init_mode,
                                   const void *companion, float *centroids, int32_t *labels, int32_t *perm,
-                                  int32_t *offsets, void *x_perm, void *companion_perm, void *workspace,
-                                  size_t ws_bytes)
+                                  int32_t *offsets, void *x_perm, void *companion_perm, float *max_sqnorm,
+                                  void *workspace, size_t ws_bytes)
 {
     ISG_REQUIRE(x && x_strides && centroids && labels && perm && offsets, ISG_E_ARG,
                 "isg_cluster: null pointer argument");
@@ -1019,8 +1061,8 @@ extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, con
     if (dt == ISG_F32)
         return dispatch_d<float>(d, st, (const float *)x, xs, B, H, N, C, iters, init_mode,
                                  (const float *)companion, centroids, labels, perm, offsets, (float *)x_perm,
-                                 (float *)companion_perm, ws);
+                                 (float *)companion_perm, max_sqnorm, ws);
     return dispatch_d<uint16_t>(d, st, (const uint16_t *)x, xs, B, H, N, C, iters, init_mode,
                                 (const uint16_t *)companion, centroids, labels, perm, offsets,
-                                (uint16_t *)x_perm, (uint16_t *)companion_perm, ws);
+                                (uint16_t *)x_perm, (uint16_t *)companion_perm, max_sqnorm, ws);
 }

@@ -48,14 +48,15 @@ def _declare(L):
     L.isg_proposal_table.argtypes = [_p]
     L.isg_cluster_workspace_size.argtypes = [_i] * 5
     L.isg_cluster_workspace_size.restype = _sz
-    L.isg_cluster.argtypes = [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _sz]
+    L.isg_cluster.argtypes = [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                              _sz]
     L.isg_probs.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]
     L.isg_select_sample.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _u64, _u64,
                                     _p, _p, _p, _p, _p]
     L.isg_attention_workspace_size.argtypes = [_i] * 5
     L.isg_attention_workspace_size.restype = _sz
     L.isg_attention.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
-                                _i, _f, _p, _p, _p, _sz]
+                                _i, _f, _p, _p, _p, _p, _sz]
     L.isg_unpermute.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p]
     L.isg_select_sample_topp.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _u64, _u64,
                                          _p, _p, _p, _p, _p]
@@ -117,8 +118,11 @@ def attention_workspace_size(B, H, N, Cq, Ck):
     return int(lib().isg_attention_workspace_size(B, H, N, Cq, Ck))
 
 
-def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, workspace=None, stream=None):
-    """k-means + stable permutation per head of x [B,H,N,d] (d contiguous, any other strides)."""
+def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, want_max_sqnorm=False,
+                workspace=None, stream=None):
+    """k-means + stable permutation per head of x [B,H,N,d] (d contiguous, any other strides).
+    With want_max_sqnorm, also the per-head largest squared row norm [B,H] (fp32), which
+    isg_attention takes as k_max_sqnorm when x is K."""
     _dev(x, "x")
     B, H, N, d = x.shape
     if x.stride(3) != 1:
@@ -136,14 +140,15 @@ def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, work
         if companion.shape != x.shape or companion.stride() != x.stride() or companion.dtype != x.dtype:
             raise IsgError("companion must match x in shape, strides and dtype")
         comp_perm = torch.empty((B, H, N, d), device=dev, dtype=x.dtype)
+    mx = torch.empty((B, H), device=dev, dtype=torch.float32) if want_max_sqnorm else None
     need = cluster_workspace_size(B, H, N, d, C_)
     ws = workspace if workspace is not None else torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
     st = lib().isg_cluster(_stream(stream), _ptr(x), _dtype(x), _i64x3(x.stride()[:3]), B, H, N, d, C_, iters,
                            0 if init is None else 1, _ptr(companion), _ptr(cent), _ptr(labels), _ptr(perm),
-                           _ptr(offsets), _ptr(x_perm), _ptr(comp_perm), _ptr(ws), ws.numel())
+                           _ptr(offsets), _ptr(x_perm), _ptr(comp_perm), _ptr(mx), _ptr(ws), ws.numel())
     _check(st, "isg_cluster")
     return dict(centroids=cent, labels=labels, perm=perm, offsets=offsets, x_perm=x_perm,
-                companion_perm=comp_perm)
+                companion_perm=comp_perm, max_sqnorm=mx)
 
 
 _side_streams = {}
@@ -161,7 +166,8 @@ def _side_stream(device):
 
 
 def cluster_qk(q, k, v, Cq, Ck, iters, *, ws_q=None, ws_k=None, stream=None):
-    """isg_cluster of Q and of K (companion V), Q's on a second stream beside K's.
+    """isg_cluster of Q and of K (companion V, and K's per-head largest squared norm
+    for isg_attention), Q's on a second stream beside K's.
 
     Both start after the work already queued on ``stream`` (default: the current
     stream), and ``stream`` waits for both before this returns.  The calls share
@@ -179,7 +185,7 @@ def cluster_qk(q, k, v, Cq, Ck, iters, *, ws_q=None, ws_k=None, stream=None):
     if ws_q is not None:
         ws_q.record_stream(side)
     with torch.cuda.stream(main):
-        ck = isg_cluster(k, Ck, iters, companion=v, workspace=ws_k, stream=main)
+        ck = isg_cluster(k, Ck, iters, companion=v, want_max_sqnorm=True, workspace=ws_k, stream=main)
     done = torch.cuda.Event()
     done.record(side)
     main.wait_event(done)
@@ -242,8 +248,8 @@ def isg_select_sample(scores, k_offsets, N, exact_keys, m, *, mode="importance",
     return out
 
 
-def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, want_lse=True, out=None, workspace=None,
-                  stream=None):
+def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, k_max_sqnorm=None, want_lse=True, out=None,
+                  workspace=None, stream=None):
     for n, t in (("q_p", q_p), ("k_p", k_p), ("v_p", v_p)):
         _dev(t, n)
         if not t.is_contiguous():
@@ -259,8 +265,8 @@ def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, want_lse=T
     st = lib().isg_attention(_stream(stream), _ptr(q_p), _ptr(k_p), _ptr(v_p), _dtype(q_p), B, H, N, d, Cq, Ck,
                              _ptr(q_offsets.contiguous()), _ptr(k_offsets.contiguous()),
                              _ptr(sel["exact_groups"]), _ptr(sel["n_exact"]), _ptr(sel["sample_idx"]),
-                             _ptr(sel["sample_bias"]), _ptr(sel["n_sample"]), int(m), float(scale), _ptr(o_p),
-                             _ptr(lse_p), _ptr(ws), ws.numel())
+                             _ptr(sel["sample_bias"]), _ptr(sel["n_sample"]), int(m), float(scale),
+                             _ptr(k_max_sqnorm), _ptr(o_p), _ptr(lse_p), _ptr(ws), ws.numel())
     _check(st, "isg_attention")
     return o_p, lse_p
 
@@ -299,7 +305,7 @@ def pq_codebooks(x, P, Cc, iters, *, stream=None):
         ws = torch.empty(max(cluster_workspace_size(P, H, N, ds, Cc), 1), device=dev, dtype=torch.uint8)
         st = lib().isg_cluster(_stream(stream), _ptr(x), _dtype(x), _i64x3((ds, x.stride(1), x.stride(2))), P, H, N,
                                ds, Cc, iters, 0, None, _ptr(cbs), _ptr(codes), _ptr(perm), _ptr(offsets), None,
-                               None, _ptr(ws), ws.numel())
+                               None, None, _ptr(ws), ws.numel())
         _check(st, "isg_cluster (subspaces)")
         return codes, cbs
     perm = torch.empty((B, H, N), device=dev, dtype=torch.int32)
@@ -309,7 +315,7 @@ def pq_codebooks(x, P, Cc, iters, *, stream=None):
         xs = x[..., s * ds:(s + 1) * ds]
         st = lib().isg_cluster(_stream(stream), _ptr(xs), _dtype(x), _i64x3(xs.stride()[:3]), B, H, N, ds, Cc,
                                iters, 0, None, _ptr(cbs[s]), _ptr(codes[s]), _ptr(perm), _ptr(offsets), None, None,
-                               _ptr(ws), ws.numel())
+                               None, _ptr(ws), ws.numel())
         _check(st, "isg_cluster (subspace)")
     return codes, cbs
 
@@ -372,7 +378,7 @@ def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0
         sel = isg_select_sample(scores, ck["offsets"], q.shape[2], exact_keys, m, mode=mode, seed=seed,
                                 call_id=call_id, votes=None if pqr is None else pqr["votes"], stream=stream)
     o_p, lse_p = isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
-                               sel, scale, stream=stream)
+                               sel, scale, k_max_sqnorm=ck["max_sqnorm"], stream=stream)
     o, lse = isg_unpermute(o_p, lse_p, cq["perm"], stream=stream)
     return dict(cq=cq, ck=ck, scores=scores, pi=pi, pq=pqr, sel=sel, o_p=o_p, lse_p=lse_p, o=o, lse=lse,
                 scale=scale)

@@ -100,12 +100,16 @@ void isg_proposal_table(uint32_t out[256]);
  * offsets     device int32 [B,H,C+1] (written): group j = rows [off[j], off[j+1]).
  * x_perm      device or NULL, dtype dt, contiguous [B,H,N,d] (written).
  * companion_perm  device or NULL (must be non-NULL iff companion is), [B,H,N,d].
+ * max_sqnorm  device fp32 [B,H] or NULL: per head, the largest squared row norm
+ *             of x (fp32 fma chain over each 8-element chunk, chunks of a row
+ *             added by a butterfly), computed from the rows the last round's
+ *             update reads; isg_attention accepts it as k_max_sqnorm.
  * workspace   device, >= isg_cluster_workspace_size(B,H,N,d,C) bytes. */
 size_t isg_cluster_workspace_size(int B, int H, int N, int d, int C);
 isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
                        int B, int H, int N, int d, int C, int iters, int init_mode,
                        const void *companion, float *centroids, int32_t *labels, int32_t *perm,
-                       int32_t *offsets, void *x_perm, void *companion_perm,
+                       int32_t *offsets, void *x_perm, void *companion_perm, float *max_sqnorm,
                        void *workspace, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------ */
@@ -192,8 +196,11 @@ isg_status isg_select_sample_topp(void *stream, const float *scores, const float
  * q_p, k_p, v_p device [B,H,N,d] in permuted order (from isg_cluster), dtype dt;
  * q_offsets [B,H,Cq+1], k_offsets [B,H,Ck+1] device int32; the list arguments
  * as written by isg_select_sample with the same m; d in {64, 128}; Cq, Ck in
- * [1, 1024]. o_p device dtype dt [B,H,N,d] (written, permuted order);
- * lse_p device fp32 [B,H,N] or NULL (natural log).
+ * [1, 1024]. k_max_sqnorm device fp32 [B,H] or NULL: the largest squared key
+ * norm per head, as isg_cluster of K writes it (max_sqnorm); bf16 calls use it
+ * for the fixed per-row reference and otherwise compute it with a pass over
+ * k_p (fp32 calls do not use it). o_p device dtype dt [B,H,N,d] (written,
+ * permuted order); lse_p device fp32 [B,H,N] or NULL (natural log).
  * workspace device, >= isg_attention_workspace_size(B,H,N,Cq,Ck) bytes. */
 size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck);
 isg_status isg_attention(void *stream, const void *q_p, const void *k_p, const void *v_p,
@@ -201,8 +208,8 @@ isg_status isg_attention(void *stream, const void *q_p, const void *k_p, const v
                          const int32_t *q_offsets, const int32_t *k_offsets,
                          const int32_t *exact_groups, const int32_t *n_exact,
                          const int32_t *sample_idx, const float *sample_bias,
-                         const int32_t *n_sample, int m, float scale, void *o_p, float *lse_p,
-                         void *workspace, size_t ws_bytes);
+                         const int32_t *n_sample, int m, float scale, const float *k_max_sqnorm,
+                         void *o_p, float *lse_p, void *workspace, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------ */
 /* isg_unpermute -- rows back to token order: o[perm_q[r]] = o_p[r] (and lse).

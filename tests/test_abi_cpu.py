@@ -50,11 +50,11 @@ def _i64x3(a, b, c):
 def _cluster(**kw):
     a = dict(stream=None, x=FAKE, dt=1, strides=_i64x3(8 * 64 * 128, 64 * 128, 128), B=1, H=8, N=64, d=128,
              C=8, iters=5, init=0, comp=None, cent=FAKE, lab=FAKE, perm=FAKE, off=FAKE, xp=FAKE, cp=None,
-             ws=FAKE, wsb=1 << 30)
+             mx=None, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return isg.lib().isg_cluster(a["stream"], a["x"], a["dt"], a["strides"], a["B"], a["H"], a["N"], a["d"],
                                  a["C"], a["iters"], a["init"], a["comp"], a["cent"], a["lab"], a["perm"],
-                                 a["off"], a["xp"], a["cp"], a["ws"], a["wsb"])
+                                 a["off"], a["xp"], a["cp"], a["mx"], a["ws"], a["wsb"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -121,11 +121,12 @@ def test_select_allows_empty_sample_arrays_when_m_is_zero():
 
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, B=1, H=1, N=256, d=128, Cq=4, Ck=8, qo=FAKE, ko=FAKE, eg=FAKE,
-             ne=FAKE, si=FAKE, sb=FAKE, ns=FAKE, m=16, scale=0.088, o=FAKE, lse=None, ws=FAKE, wsb=1 << 40)
+             ne=FAKE, si=FAKE, sb=FAKE, ns=FAKE, m=16, scale=0.088, kmx=None, o=FAKE, lse=None, ws=FAKE,
+             wsb=1 << 40)
     a.update(kw)
     return isg.lib().isg_attention(None, a["q"], a["k"], a["v"], a["dt"], a["B"], a["H"], a["N"], a["d"],
                                    a["Cq"], a["Ck"], a["qo"], a["ko"], a["eg"], a["ne"], a["si"], a["sb"],
-                                   a["ns"], a["m"], a["scale"], a["o"], a["lse"], a["ws"], a["wsb"])
+                                   a["ns"], a["m"], a["scale"], a["kmx"], a["o"], a["lse"], a["ws"], a["wsb"])
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -394,6 +394,32 @@ def test_pipeline_tiny_config_vs_oracle(orc):
     assert np.abs(npy(r["lse"]) - lse).max() <= 1e-4
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_norm_from_clustering_matches_attention_pass(d):
+    """K's per-head largest squared row norm, fused into the last k-means update,
+    against a plain fp32 reduction; and attention given it against attention
+    that runs its own key-norm pass: equal bit for bit (the same arithmetic)."""
+    H, N = 3, 3001
+    say(f"key norms H={H} N={N} d={d}")
+    q, k, v = _inputs(H, N, d, "bf16", seed=5)
+    qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
+    cq = isg.isg_cluster(qg, 7, 3)
+    ck = isg.isg_cluster(kg, 20, 3, companion=vg, want_max_sqnorm=True)
+    mx = ck["max_sqnorm"]
+    ref = (kg.float() ** 2).sum(-1).amax(-1)
+    rel = ((mx - ref).abs() / ref).max().item()
+    say(f"  max relative difference to the fp32 reduction {rel:.2e}")
+    assert rel <= 1e-5
+    scale = isg.default_scale(d)
+    S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
+    sel = isg.isg_select_sample(S, ck["offsets"], N, 300, 200)
+    args = (cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"], sel, scale)
+    o_a, l_a = isg.isg_attention(*args)
+    o_b, l_b = isg.isg_attention(*args, k_max_sqnorm=mx)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
+
+
 def _same_lists_and_samples(o, g):
     """Exact lists and counts equal; samples equal up to each group's n_sample
     (the entries past it are not written)."""
