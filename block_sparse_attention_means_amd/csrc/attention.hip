@@ -448,7 +448,8 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
     int N, int Cq, const int4 *__restrict__ table, int nblocks, const int32_t *__restrict__ col_row,
     const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
     const float *__restrict__ col_bmax, const int *__restrict__ kmax2, int64_t cap, float scale_log2,
-    uint16_t *__restrict__ o_p, float *__restrict__ lse_p, int *__restrict__ redo)
+    uint16_t *__restrict__ o_p, float *__restrict__ lse_p, const int32_t *__restrict__ perm_q,
+    int *__restrict__ redo)
 {
     constexpr int NDS = D / 16;          // 16-wide d steps of S^T = K Q^T
     constexpr int NDB = D / 32;          // 32-row d blocks of O^T
@@ -557,7 +558,9 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
             const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
             if (qrow_raw < r1) {
                 const float inv = 1.0f / l_tot[qb];
-                uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
+                // token order when a permutation is given (the un-permute step fused)
+                const int orow_i = perm_q ? perm_q[(int64_t)bh * N + qrow_raw] : qrow_raw;
+                uint16_t *orow = o_p + ((int64_t)bh * N + orow_i) * D;
     #pragma unroll
                 for (int db = 0; db < NDB; ++db)
     #pragma unroll
@@ -570,7 +573,7 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
                         *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
                     }
                 if (lse_p && hl == 0)
-                    lse_p[(int64_t)bh * N + qrow_raw] = (m_run[qb] + log2f(l_tot[qb])) * 0.6931471805599453f;
+                    lse_p[(int64_t)bh * N + orow_i] = (m_run[qb] + log2f(l_tot[qb])) * 0.6931471805599453f;
             }
         }
     };
@@ -852,7 +855,8 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     int Cq, const int4 *__restrict__ table, int nblocks, const int32_t *__restrict__ col_row,
     const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
     const float *__restrict__ col_bmax, const int *__restrict__ kmax2, int64_t cap, float scale_log2,
-    uint16_t *__restrict__ o_p, float *__restrict__ lse_p, int *__restrict__ redo)
+    uint16_t *__restrict__ o_p, float *__restrict__ lse_p, const int32_t *__restrict__ perm_q,
+    int *__restrict__ redo)
 {
     constexpr int NDS = D / 16;
     constexpr int NDB = D / 32;
@@ -953,7 +957,9 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     }
     if (qrow_raw < tt.r1) {
         const float inv = 1.0f / l_tot;
-        uint16_t *orow = o_p + ((int64_t)bh * N + qrow_raw) * D;
+        // token order when a permutation is given (the un-permute step fused)
+        const int orow_i = perm_q ? perm_q[(int64_t)bh * N + qrow_raw] : qrow_raw;
+        uint16_t *orow = o_p + ((int64_t)bh * N + orow_i) * D;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -965,7 +971,7 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
                                     ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 3] * inv) << 16);
                 *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
             }
-        if (lse_p && hl == 0) lse_p[(int64_t)bh * N + qrow_raw] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+        if (lse_p && hl == 0) lse_p[(int64_t)bh * N + orow_i] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
     }
 }
 
@@ -978,7 +984,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
                                                        const float *__restrict__ col_bias,
                                                        const int32_t *__restrict__ col_len, int64_t cap,
                                                        float scale_log2, float *__restrict__ o_p,
-                                                       float *__restrict__ lse_p)
+                                                       float *__restrict__ lse_p,
+                                                       const int32_t *__restrict__ perm_q)
 {
     constexpr int DQ = D / 4;
     constexpr int TKF = 32;
@@ -1035,9 +1042,10 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
     }
     if (qrow_raw < r1) {
         const float inv = 1.0f / l_run;
+        const int orow_i = perm_q ? perm_q[(int64_t)bh * N + qrow_raw] : qrow_raw;
 #pragma unroll
-        for (int e = 0; e < DQ; ++e) o_p[((int64_t)bh * N + qrow_raw) * D + part * DQ + e] = o[e] * inv;
-        if (lse_p && part == 0) lse_p[(int64_t)bh * N + qrow_raw] = (m_run + log2f(l_run)) * 0.6931471805599453f;
+        for (int e = 0; e < DQ; ++e) o_p[((int64_t)bh * N + orow_i) * D + part * DQ + e] = o[e] * inv;
+        if (lse_p && part == 0) lse_p[(int64_t)bh * N + orow_i] = (m_run + log2f(l_run)) * 0.6931471805599453f;
     }
 }
 
@@ -1077,20 +1085,20 @@ template <int D, int QB>
 void launch_bf16(hipStream_t st, const Layout &Lq, const void *q_p, const void *k_p, const void *v_p, int N, int Cq,
                  const int4 *table, const int32_t *col_row, const float *col_bias, const int32_t *col_len,
                  const int32_t *col_x, const float *col_bmax, const int *kmax2, float scale_log2, void *o_p,
-                 float *lse_p, int *redo)
+                 float *lse_p, const int32_t *perm_q, int *redo)
 {
     if constexpr (D == 128 && kUsePingPong) {
         const int npairs = (Lq.ntotal / 2 + 7) / 8 * 8;
         attn_pp_kernel<D><<<npairs, 64 * kPPWaves, 0, st>>>(
             (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo);
     } else
     attn_bf16_kernel<D, true, QB><<<Lq.ntotal, 256 / QB, 0, st>>>(
         (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo);
     attn_bf16_kernel<D, false, 1><<<std::min((Lq.ntotal + 63) / 64, kFallbackBlocks), 256, 0, st>>>(
         (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, redo);
+        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo);
 }
 
 }  // namespace
@@ -1109,8 +1117,8 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
                                     const int32_t *exact_groups, const int32_t *n_exact,
                                     const int32_t *sample_idx, const float *sample_bias,
                                     const int32_t *n_sample, int m, float scale,
-                                    const float *k_max_sqnorm, void *o_p, float *lse_p, void *workspace,
-                                    size_t ws_bytes)
+                                    const float *k_max_sqnorm, void *o_p, float *lse_p,
+                                    const int32_t *perm_q, void *workspace, size_t ws_bytes)
 {
     ISG_REQUIRE(q_p && k_p && v_p && q_offsets && k_offsets && exact_groups && n_exact && n_sample && o_p,
                 ISG_E_ARG, "isg_attention: null pointer argument");
@@ -1160,23 +1168,23 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
         if (d == 128) {
             if (!k_max_sqnorm) kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<128, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                  kmx, scale_log2, o_p, lse_p, redo);
+                                  kmx, scale_log2, o_p, lse_p, perm_q, redo);
         } else {
             if (!k_max_sqnorm) kmax_kernel<64><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<64, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                 kmx, scale_log2, o_p, lse_p, redo);
+                                 kmx, scale_log2, o_p, lse_p, perm_q, redo);
         }
     } else {
         if (d == 128)
             attn_f32_kernel<128><<<Lq.ntotal, 256, 0, st>>>((const float *)q_p, (const float *)k_p,
                                                            (const float *)v_p, N, Cq, table, Lq.ntotal, col_row,
                                                            col_bias, col_len, Lq.cap, scale_log2, (float *)o_p,
-                                                           lse_p);
+                                                           lse_p, perm_q);
         else
             attn_f32_kernel<64><<<Lq.ntotal, 256, 0, st>>>((const float *)q_p, (const float *)k_p,
                                                           (const float *)v_p, N, Cq, table, Lq.ntotal, col_row,
                                                           col_bias, col_len, Lq.cap, scale_log2, (float *)o_p,
-                                                          lse_p);
+                                                          lse_p, perm_q);
     }
     return isg_check_launch("isg_attention");
 }

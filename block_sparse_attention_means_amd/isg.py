@@ -56,7 +56,7 @@ def _declare(L):
     L.isg_attention_workspace_size.argtypes = [_i] * 5
     L.isg_attention_workspace_size.restype = _sz
     L.isg_attention.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
-                                _i, _f, _p, _p, _p, _p, _sz]
+                                _i, _f, _p, _p, _p, _p, _p, _sz]
     L.isg_unpermute.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p]
     L.isg_select_sample_topp.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _u64, _u64,
                                          _p, _p, _p, _p, _p]
@@ -248,8 +248,11 @@ def isg_select_sample(scores, k_offsets, N, exact_keys, m, *, mode="importance",
     return out
 
 
-def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, k_max_sqnorm=None, want_lse=True, out=None,
-                  workspace=None, stream=None):
+def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, k_max_sqnorm=None, perm_q=None,
+                  want_lse=True, out=None, workspace=None, stream=None):
+    """Attention over each query group's exact and sampled columns.  Rows come out
+    in the permuted order of q_p, or in token order when ``perm_q`` (the query
+    permutation from isg_cluster) is given, which fuses the un-permute step."""
     for n, t in (("q_p", q_p), ("k_p", k_p), ("v_p", v_p)):
         _dev(t, n)
         if not t.is_contiguous():
@@ -266,7 +269,8 @@ def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, k_max_sqno
                              _ptr(q_offsets.contiguous()), _ptr(k_offsets.contiguous()),
                              _ptr(sel["exact_groups"]), _ptr(sel["n_exact"]), _ptr(sel["sample_idx"]),
                              _ptr(sel["sample_bias"]), _ptr(sel["n_sample"]), int(m), float(scale),
-                             _ptr(k_max_sqnorm), _ptr(o_p), _ptr(lse_p), _ptr(ws), ws.numel())
+                             _ptr(k_max_sqnorm), _ptr(o_p), _ptr(lse_p),
+                             _ptr(None if perm_q is None else perm_q.contiguous()), _ptr(ws), ws.numel())
     _check(st, "isg_attention")
     return o_p, lse_p
 
@@ -352,11 +356,13 @@ def default_scale(d: int) -> float:
 
 
 def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0, call_id=0, scale=None,
-             pq=None, top_p=None, stream=None):
+             pq=None, top_p=None, fuse_unpermute=True, stream=None):
     """All steps on one batch: cluster Q and K (+V) side by side on two streams,
     probs, [PQ votes], select/sample, attention, unpermute.  ``pq=(P, Cc)`` is required by
     mode "votes"; ``top_p`` sizes the exact set by mass instead of
-    ``exact_keys``.  Returns every intermediate (all on the GPU)."""
+    ``exact_keys``.  With ``fuse_unpermute`` the attention writes its rows in token
+    order itself (o_p and lse_p are then None); otherwise isg_unpermute runs after
+    it.  Returns every intermediate (all on the GPU)."""
     d = q.shape[-1]
     scale = default_scale(d) if scale is None else scale
     cq, ck = cluster_qk(q, k, v, Cq, Ck, iters, stream=stream)
@@ -377,8 +383,12 @@ def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0
     else:
         sel = isg_select_sample(scores, ck["offsets"], q.shape[2], exact_keys, m, mode=mode, seed=seed,
                                 call_id=call_id, votes=None if pqr is None else pqr["votes"], stream=stream)
-    o_p, lse_p = isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
-                               sel, scale, k_max_sqnorm=ck["max_sqnorm"], stream=stream)
-    o, lse = isg_unpermute(o_p, lse_p, cq["perm"], stream=stream)
+    args = (cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"], sel, scale)
+    if fuse_unpermute:
+        o_p = lse_p = None
+        o, lse = isg_attention(*args, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], stream=stream)
+    else:
+        o_p, lse_p = isg_attention(*args, k_max_sqnorm=ck["max_sqnorm"], stream=stream)
+        o, lse = isg_unpermute(o_p, lse_p, cq["perm"], stream=stream)
     return dict(cq=cq, ck=ck, scores=scores, pi=pi, pq=pqr, sel=sel, o_p=o_p, lse_p=lse_p, o=o, lse=lse,
                 scale=scale)

@@ -199,8 +199,12 @@ isg_status isg_select_sample_topp(void *stream, const float *scores, const float
  * [1, 1024]. k_max_sqnorm device fp32 [B,H] or NULL: the largest squared key
  * norm per head, as isg_cluster of K writes it (max_sqnorm); bf16 calls use it
  * for the fixed per-row reference and otherwise compute it with a pass over
- * k_p (fp32 calls do not use it). o_p device dtype dt [B,H,N,d] (written,
- * permuted order); lse_p device fp32 [B,H,N] or NULL (natural log).
+ * k_p (fp32 calls do not use it). o_p device dtype dt [B,H,N,d] (written);
+ * lse_p device fp32 [B,H,N] or NULL (natural log).  perm_q device int32
+ * [B,H,N] or NULL: NULL writes row r of o_p and lse_p in the permuted order of
+ * q_p; given (the query permutation from isg_cluster), row r goes to
+ * o_p[perm_q[r]] and lse_p[perm_q[r]], i.e. token order, which is what
+ * isg_unpermute would produce from the permuted rows (the un-permute fused).
  * workspace device, >= isg_attention_workspace_size(B,H,N,Cq,Ck) bytes. */
 size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck);
 isg_status isg_attention(void *stream, const void *q_p, const void *k_p, const void *v_p,
@@ -209,7 +213,8 @@ isg_status isg_attention(void *stream, const void *q_p, const void *k_p, const v
                          const int32_t *exact_groups, const int32_t *n_exact,
                          const int32_t *sample_idx, const float *sample_bias,
                          const int32_t *n_sample, int m, float scale, const float *k_max_sqnorm,
-                         void *o_p, float *lse_p, void *workspace, size_t ws_bytes);
+                         void *o_p, float *lse_p, const int32_t *perm_q, void *workspace,
+                         size_t ws_bytes);
 
 /* ------------------------------------------------------------------------ */
 /* isg_unpermute -- rows back to token order: o[perm_q[r]] = o_p[r] (and lse).

@@ -121,12 +121,13 @@ def test_select_allows_empty_sample_arrays_when_m_is_zero():
 
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, B=1, H=1, N=256, d=128, Cq=4, Ck=8, qo=FAKE, ko=FAKE, eg=FAKE,
-             ne=FAKE, si=FAKE, sb=FAKE, ns=FAKE, m=16, scale=0.088, kmx=None, o=FAKE, lse=None, ws=FAKE,
-             wsb=1 << 40)
+             ne=FAKE, si=FAKE, sb=FAKE, ns=FAKE, m=16, scale=0.088, kmx=None, o=FAKE, lse=None, pq=None,
+             ws=FAKE, wsb=1 << 40)
     a.update(kw)
     return isg.lib().isg_attention(None, a["q"], a["k"], a["v"], a["dt"], a["B"], a["H"], a["N"], a["d"],
                                    a["Cq"], a["Ck"], a["qo"], a["ko"], a["eg"], a["ne"], a["si"], a["sb"],
-                                   a["ns"], a["m"], a["scale"], a["kmx"], a["o"], a["lse"], a["ws"], a["wsb"])
+                                   a["ns"], a["m"], a["scale"], a["kmx"], a["o"], a["lse"], a["pq"], a["ws"],
+                                   a["wsb"])
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -420,6 +420,22 @@ def test_key_norm_from_clustering_matches_attention_pass(d):
     assert torch.equal(o_a, o_b) and torch.equal(l_a, l_b)
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_attention_token_order_equals_unpermute(dtype, d):
+    """Attention given the query permutation writes rows in token order: equal bit
+    for bit to the permuted-order call followed by isg_unpermute (the paired-tile
+    kernel, the one-tile bf16 kernel and the fp32 kernel)."""
+    H, N = 2, 2500
+    say(f"token-order attention H={H} N={N} d={d} {dtype}")
+    q, k, v = _inputs(H, N, d, dtype, seed=9)
+    r = isg.pipeline(q.to(DEV), k.to(DEV), v.to(DEV), 9, 24, 3, 250, 150, seed=1, fuse_unpermute=False)
+    cq, ck = r["cq"], r["ck"]
+    o, lse = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
+                               r["sel"], r["scale"], k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, r["o"]) and torch.equal(lse, r["lse"])
+
+
 def _same_lists_and_samples(o, g):
     """Exact lists and counts equal; samples equal up to each group's n_sample
     (the entries past it are not written)."""
@@ -628,7 +644,9 @@ def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode
                                f32(sl(r["ck"]["companion_perm"])), qo_all[:, h:h + 1], ko_all[:, h:h + 1],
                                {kk: vv[:, h:h + 1] for kk, vv in selo.items()}, m, r["scale"],
                                group_mask=gm[:, h:h + 1])
-        og, lg = f32(r["o_p"][0, h]), npy(r["lse_p"][0, h])
+        # the step writes O and LSE in token order: row r of the permuted order is o[perm[r]]
+        ph = r["cq"]["perm"][0, h].long()
+        og, lg = f32(r["o"][0, h][ph]), npy(r["lse"][0, h][ph])
         for i in pick:
             rows = slice(qo_all[0, h, i], qo_all[0, h, i + 1])
             err = np.abs(og[rows] - oo[0, 0, rows]).max()
