@@ -260,17 +260,15 @@ def n_sweep(args, w, isg, make_workload, budget_keys, dev):
         ws_a = torch.empty(isg.attention_workspace_size(1, H, N, w["Cq"], w["Ck"]), device=dev, dtype=torch.uint8)
 
         def run():
-            cq = isg.isg_cluster(qg, w["Cq"], w["iters"])
-            ck = isg.isg_cluster(kg, w["Ck"], w["iters"], companion=vg)
+            cq, ck = isg.cluster_qk(qg, kg, vg, w["Cq"], w["Ck"], w["iters"], stream=stream)
             S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
             sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, seed=args.seed)
             a0 = torch.cuda.Event(enable_timing=True)
             a1 = torch.cuda.Event(enable_timing=True)
             a0.record(stream)
-            o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
-                                           ck["offsets"], sel, scale, workspace=ws_a)
+            isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"], sel,
+                              scale, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], workspace=ws_a)
             a1.record(stream)
-            isg.isg_unpermute(o_p, lse_p, cq["perm"])
             return cq, ck, sel, (a0, a1)
 
         run()
@@ -454,12 +452,12 @@ def main():
                                     sel2["n_sample"])
             for _ in range(2):
                 isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
-                                  sel2, scale, workspace=ws_a)
+                                  sel2, scale, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], workspace=ws_a)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(5):
                 isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
-                                  sel2, scale, workspace=ws_a)
+                                  sel2, scale, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], workspace=ws_a)
             b.record(stream)
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / 5
