@@ -85,10 +85,10 @@ void isg_proposal_table(uint32_t out[256]);
  *   perm = tokens stably sorted by the last labels; offsets = prefix of counts;
  *   x_perm[r] = x[perm[r]], companion_perm[r] = companion[perm[r]].
  * The labels are the assignment of the last round and the centroids are the
- * means of those groups.  The argmin is decided on fp32 distances (bf16 hi/lo
- * centroid planes on the matrix cores); whenever other kept candidates lie
- * within the fp32 error bound of the best, it is re-decided in fp64 among the
- * four best, or over all C when all four are that close.
+ * means of those groups.  For bf16 x the argmin is decided on fp32 distances
+ * (bf16 hi/lo centroid planes on the matrix cores); whenever other kept
+ * candidates lie within the fp32 error bound of the best, it is re-decided in
+ * fp64 among the four best, or over all C when all four are that close.
  *
  * x           device, dtype dt, element (b,h,t,k) at x[b*xs[0] + h*xs[1] + t*xs[2] + k]
  *             (xs = x_strides, in elements; k contiguous).  [B,N,H,d] and
