@@ -88,7 +88,8 @@ void isg_proposal_table(uint32_t out[256]);
  * means of those groups.  For bf16 x the argmin is decided on fp32 distances
  * (bf16 hi/lo centroid planes on the matrix cores); whenever other kept
  * candidates lie within the fp32 error bound of the best, it is re-decided in
- * fp64 among the four best, or over all C when all four are that close.
+ * fp64 among the four best, or over all C when all four are that close; fp32 x
+ * is assigned on fp64 distances throughout.
  *
  * x           device, dtype dt, element (b,h,t,k) at x[b*xs[0] + h*xs[1] + t*xs[2] + k]
  *             (xs = x_strides, in elements; k contiguous).  [B,N,H,d] and
