@@ -5,7 +5,7 @@ cluster Q, cluster K (+V), centroid scores and pi, exact set + shared sample,
 fused exact+sampled attention, un-permute.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--exact 0.08] [--sample 0.08] [--no-cpu-baseline] [--sweep]
+                  [--exact 0.08] [--sample 0.08] [--no-cpu-baseline] [--no-sweep]
 
 value = effective TFLOP/s of the step: algorithmic attention flops (4 d per
 computed (query, column) pair over the exact and sampled columns, padding
@@ -39,7 +39,11 @@ def parse():
     ap.add_argument("--mode", default=None, choices=["importance", "uniform", "votes"],
                     help="sampling mode (default: votes for a workload with product quantisation, else importance)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="also time the attention at every budget of the workload")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip timing the attention at every budget of the workload (on by default)")
+    ap.add_argument("--sweep", action="store_true", help=argparse.SUPPRESS)  # the default; kept for old commands
+    ap.add_argument("--serial-cluster", action="store_true",
+                    help="cluster Q, then K, on one stream (profiling aid: per-kernel durations do not overlap)")
     ap.add_argument("--top-p", type=float, default=None, metavar="P",
                     help="size the exact set by mass (groups by pi until the running pi reaches P) instead of --exact")
     ap.add_argument("--density-study", action="store_true",
@@ -121,6 +125,22 @@ def attention_flops(d, q_offsets, k_offsets, exact_groups, n_exact, n_sample):
     return float(4 * d * (nq * cols).sum()), float((nq * cols).sum())
 
 
+def query_tiles(q_offsets):
+    """128-row query tiles of one attention call (each query group in whole tiles)."""
+    import numpy as np
+    return int(((np.diff(q_offsets.cpu().numpy().astype(np.int64), axis=-1) + 127) // 128).sum())
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, q, k, v, E, m, seed, mode="importance", top_p=None):
     """The oracle as it stands on one head of the workload: every stage on the whole
     head except attention, which runs on a sample of query groups and is scaled to all
@@ -172,6 +192,7 @@ def cpu_baseline(w, q, k, v, E, m, seed, mode="importance", top_p=None):
     t_head = t_pre + t_att / frac + t_un
     flops_head = 4.0 * d * work.sum()
     return {"value": flops_head / t_head / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": (f"1 of {w['H']} heads of {w.get('name')}: clustering, scores, "
                        f"{'PQ votes, ' if mode == 'votes' else ''}selection and "
                        f"un-permute on the whole head ({t_pre + t_un:.1f} s); attention on the "
@@ -257,7 +278,8 @@ def n_sweep(args, w, isg, make_workload, budget_keys, dev):
         scale = isg.default_scale(w["d"])
         E, m = budget_keys(args.exact, N), budget_keys(args.sample, N)
         stream = torch.cuda.current_stream()
-        ws_a = torch.empty(isg.attention_workspace_size(1, H, N, w["Cq"], w["Ck"]), device=dev, dtype=torch.uint8)
+        ws_a = torch.empty(isg.attention_workspace_size(1, H, N, w["Cq"], w["Ck"], m), device=dev,
+                           dtype=torch.uint8)
 
         def run():
             cq, ck = isg.cluster_qk(qg, kg, vg, w["Cq"], w["Ck"], w["iters"], stream=stream)
@@ -336,7 +358,11 @@ def main():
     # Q's clustering runs on a second stream beside K's, each with its own workspace
     ws_q = torch.empty(isg.cluster_workspace_size(B, H, N, d, w["Cq"]), device=dev, dtype=torch.uint8)
     ws_k = torch.empty(isg.cluster_workspace_size(B, H, N, d, w["Ck"]), device=dev, dtype=torch.uint8)
-    ws_a = torch.empty(isg.attention_workspace_size(B, H, N, w["Cq"], w["Ck"]), device=dev, dtype=torch.uint8)
+    nfb = torch.zeros(1, device=dev, dtype=torch.int32)  # query tiles the rescaling fallback recomputed
+    # sized for the largest sample of the workload's budgets (the sweep reuses it)
+    m_max = max([m] + [budget_keys(ss, N) for (_, ss) in w.get("sweep", [])])
+    ws_a = torch.empty(isg.attention_workspace_size(B, H, N, w["Cq"], w["Ck"], m_max), device=dev,
+                       dtype=torch.uint8)
     # the attention writes O and LSE in token order itself (the un-permute step fused)
     stages = ["cluster_q_and_k", "probs"] + (["pq_codes", "pq_votes"] if mode == "votes" else []) + [
         "select_sample", "attention_and_unpermute"]
@@ -346,11 +372,16 @@ def main():
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
         if record:
             marks[0].record(stream)
-        cq, ck = isg.cluster_qk(qg, kg, vg, w["Cq"], w["Ck"], w["iters"], ws_q=ws_q, ws_k=ws_k, stream=stream)
+        if args.serial_cluster:
+            cq = isg.isg_cluster(qg, w["Cq"], w["iters"], workspace=ws_q, stream=stream)
+            ck = isg.isg_cluster(kg, w["Ck"], w["iters"], companion=vg, want_max_sqnorm=True, workspace=ws_k,
+                                 stream=stream)
+        else:
+            cq, ck = isg.cluster_qk(qg, kg, vg, w["Cq"], w["Ck"], w["iters"], ws_q=ws_q, ws_k=ws_k, stream=stream)
         if record:
             marks[1].record(stream)
-        S, pi = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale,
-                              want_pi=args.top_p is not None)
+        # pi is written in every step (a row of the path), although only top-p sizing reads it
+        S, pi = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=True)
         mi = 2
         if record:
             marks[mi].record(stream)
@@ -376,7 +407,7 @@ def main():
             marks[mi].record(stream)
         o, lse = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
                                    sel, scale, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"],
-                                   workspace=ws_a)
+                                   workspace=ws_a, n_fallback_tiles=nfb)
         mi += 1
         if record:
             marks[mi].record(stream)
@@ -430,6 +461,8 @@ def main():
                    "exact_keys": E, "m": m, "seed": args.seed, "mode": mode,
                    "pq": list(w["pq"]) if mode == "votes" else None, "top_p": args.top_p},
         "attention_ms": round(att_ms, 3),
+        "attention_fallback_tiles": int(nfb.item()),
+        "attention_query_tiles": query_tiles(cq["offsets"]),
         "attention_tflops": round(att_tflops, 2),
         "attention_tflop_per_call": round(flops / 1e12, 4),
         "stage_ms": {s: round(t, 3) for s, t in stage_ms.items()},
@@ -441,7 +474,8 @@ def main():
                      "kernel": ("isg_attention: attn_pp_kernel with its column-list and tile-table prep, writing O and "
                                 "LSE in token order (key norms come from K's clustering)")},
     }
-    if args.sweep:
+    if not args.no_sweep:
+        print("# budget sweep", file=sys.stderr, flush=True)
         sweep = {}
         for (es, ss) in w["sweep"]:
             E2, m2 = budget_keys(es, N), budget_keys(ss, N)
@@ -452,7 +486,8 @@ def main():
                                     sel2["n_sample"])
             for _ in range(2):
                 isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
-                                  sel2, scale, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], workspace=ws_a)
+                                  sel2, scale, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], workspace=ws_a,
+                                  n_fallback_tiles=nfb)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(5):
@@ -462,8 +497,10 @@ def main():
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / 5
             sweep[f"{int(es * 100)}+{int(ss * 100)}%"] = {"attention_ms": round(ms, 3),
+                                                           "tflop_per_call": round(f2 / 1e12, 4),
                                                            "tflops": round(f2 / ms / 1e9, 2),
-                                                           "frac_peak": round(f2 / ms / 1e9 / peak, 4)}
+                                                           "frac_peak": round(f2 / ms / 1e9 / peak, 4),
+                                                           "fallback_tiles": int(nfb.item())}
         result["attention_sweep"] = sweep
     if args.density_study:
         print("# density study", file=sys.stderr, flush=True)

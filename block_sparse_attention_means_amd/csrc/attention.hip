@@ -158,7 +158,8 @@ __global__ __launch_bounds__(256) void kmax_kernel(const uint16_t *k_p, int N, i
 }
 
 __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t *q_offsets, int BH, int Cq, int tq,
-                                                         int tph, int ntotal, int4 *table, int *redo, int *kmax2)
+                                                         int tph, int ntotal, int4 *table, int *redo, int *kmax2,
+                                                         int32_t *nflag)
 {
     __shared__ int cnt[kMaxGroups];
     __shared__ int tmp[256];
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(256) void tile_table_kernel(const int32_t *q_offset
     if (bh == BH - 1)
         for (int s = BH * tph + threadIdx.x; s < ntotal; s += 256) redo[s] = 0;
     if (threadIdx.x == 0) kmax2[bh] = 0;
+    if (nflag && bh == 0 && threadIdx.x == 0) *nflag = 0;  // tiles the fallback will recompute
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
     const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
     const float *__restrict__ col_bmax, const int *__restrict__ kmax2, int64_t cap, float scale_log2,
     uint16_t *__restrict__ o_p, float *__restrict__ lse_p, const int32_t *__restrict__ perm_q,
-    int *__restrict__ redo)
+    int *__restrict__ redo, int32_t *__restrict__ nflag)
 {
     constexpr int NDS = D / 16;          // 16-wide d steps of S^T = K Q^T
     constexpr int NDB = D / 32;          // 32-row d blocks of O^T
@@ -585,6 +587,7 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
         const int lane = threadIdx.x & 63;
         for (int base = blockIdx.x * 64; base < nblocks; base += gridDim.x * 64) {
             uint64_t mask = __ballot(base + lane < nblocks && redo[base + lane] != 0);
+            if (nflag && mask && threadIdx.x == 0) atomicAdd(nflag, (int32_t)__popcll(mask));
             while (mask) {
                 const int bit = __ffsll((unsigned long long)mask) - 1;
                 mask &= mask - 1;
@@ -1085,7 +1088,7 @@ template <int D, int QB>
 void launch_bf16(hipStream_t st, const Layout &Lq, const void *q_p, const void *k_p, const void *v_p, int N, int Cq,
                  const int4 *table, const int32_t *col_row, const float *col_bias, const int32_t *col_len,
                  const int32_t *col_x, const float *col_bmax, const int *kmax2, float scale_log2, void *o_p,
-                 float *lse_p, const int32_t *perm_q, int *redo)
+                 float *lse_p, const int32_t *perm_q, int *redo, int32_t *nflag)
 {
     if constexpr (D == 128 && kUsePingPong) {
         const int npairs = (Lq.ntotal / 2 + 7) / 8 * 8;
@@ -1095,20 +1098,22 @@ void launch_bf16(hipStream_t st, const Layout &Lq, const void *q_p, const void *
     } else
     attn_bf16_kernel<D, true, QB><<<Lq.ntotal, 256 / QB, 0, st>>>(
         (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo);
+        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
+        nullptr);
     attn_bf16_kernel<D, false, 1><<<std::min((Lq.ntotal + 63) / 64, kFallbackBlocks), 256, 0, st>>>(
         (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo);
+        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
+        nflag);
 }
 
 }  // namespace
 
-extern "C" size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck)
+extern "C" size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck, int m)
 {
     (void)Ck;
-    if (B < 1 || H < 1 || N < 1 || Cq < 1) return 0;
-    // the column map is sized for m = N (the largest sample a call may ask for)
-    return layout(B, H, N, Cq, N, kTQ32).total;
+    if (B < 1 || H < 1 || N < 1 || Cq < 1 || m < 0 || m > N) return 0;
+    // the column map holds up to N exact columns plus the m samples per query group
+    return layout(B, H, N, Cq, m, kTQ32).total;
 }
 
 extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k_p, const void *v_p,
@@ -1118,7 +1123,8 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
                                     const int32_t *sample_idx, const float *sample_bias,
                                     const int32_t *n_sample, int m, float scale,
                                     const float *k_max_sqnorm, void *o_p, float *lse_p,
-                                    const int32_t *perm_q, void *workspace, size_t ws_bytes)
+                                    const int32_t *perm_q, int32_t *n_fallback_tiles, void *workspace,
+                                    size_t ws_bytes)
 {
     ISG_REQUIRE(q_p && k_p && v_p && q_offsets && k_offsets && exact_groups && n_exact && n_sample && o_p,
                 ISG_E_ARG, "isg_attention: null pointer argument");
@@ -1134,13 +1140,15 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     ISG_REQUIRE(m >= 0 && m <= N, ISG_E_ARG, "isg_attention: need 0 <= m <= N");
     ISG_REQUIRE((int64_t)N * d * 4 <= 0x7fffffff, ISG_E_ARG,
                 "isg_attention: N*d too large for 32-bit row offsets (N=%d, d=%d)", N, d);
-    ISG_REQUIRE(std::isfinite(scale), ISG_E_ARG, "isg_attention: scale must be finite");
+    ISG_REQUIRE(std::isfinite(scale) && scale > 0.0f, ISG_E_ARG,
+                "isg_attention: scale must be finite and > 0 (the fixed per-row reference bounds the logits only "
+                "for a positive scale)");
     ISG_REQUIRE(((uintptr_t)q_p & 15) == 0 && ((uintptr_t)k_p & 15) == 0 && ((uintptr_t)v_p & 15) == 0 &&
                     ((uintptr_t)o_p & 15) == 0,
                 ISG_E_ARG, "isg_attention: q_p, k_p, v_p, o_p must be 16-byte aligned");
     const int tq = dt == ISG_BF16 ? kTQ : kTQ32;
     const Layout Lq = layout(B, H, N, Cq, m, tq);
-    const size_t need = isg_attention_workspace_size(B, H, N, Cq, Ck);
+    const size_t need = isg_attention_workspace_size(B, H, N, Cq, Ck, m);
     ISG_REQUIRE(workspace && ws_bytes >= need, ISG_E_WORKSPACE, "isg_attention: workspace %zu < %zu bytes",
                 workspace ? ws_bytes : (size_t)0, need);
     const int64_t G = (int64_t)B * H * Cq;
@@ -1161,18 +1169,19 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     columns_kernel<<<(unsigned)G, 256, 0, st>>>(k_offsets, exact_groups, n_exact, sample_idx, sample_bias,
                                                n_sample, Cq, Ck, m, scale, Lq.cap, col_row, col_bias, col_len, col_x,
                                                col_bmax);
-    tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table, redo, kmax2);
+    tile_table_kernel<<<B * H, 256, 0, st>>>(q_offsets, B * H, Cq, tq, Lq.tph, Lq.ntotal, table, redo, kmax2,
+                                             n_fallback_tiles);
     const float scale_log2 = (float)((double)scale * 1.4426950408889634);
     if (dt == ISG_BF16) {
         const dim3 kgrid((unsigned)std::min((N + 255) / 256, 128), (unsigned)(B * H));
         if (d == 128) {
             if (!k_max_sqnorm) kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<128, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                  kmx, scale_log2, o_p, lse_p, perm_q, redo);
+                                  kmx, scale_log2, o_p, lse_p, perm_q, redo, n_fallback_tiles);
         } else {
             if (!k_max_sqnorm) kmax_kernel<64><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<64, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                 kmx, scale_log2, o_p, lse_p, perm_q, redo);
+                                 kmx, scale_log2, o_p, lse_p, perm_q, redo, n_fallback_tiles);
         }
     } else {
         if (d == 128)

@@ -35,13 +35,28 @@ def common_flags():
             "-I", INCLUDE, "-I", HERE]
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer (device code is built as
+# usual): each flag goes to the host compilation only.
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
+SAN_DIR = os.path.join(BUILD, "sanitize")
+SAN_LIB = os.path.join(SAN_DIR, "libisg.so")
+
+
+def build(verbose: bool = False, jobs: int = 8, sanitize: bool = False) -> str:
+    """Build libisg.so in the package, or (sanitize=True) the host-sanitized build
+    _build/sanitize/libisg.so, which the sanitizer test loads through ISG_LIBRARY
+    with the compiler's AddressSanitizer runtime preloaded."""
+    bdir = SAN_DIR if sanitize else BUILD
+    lib_out = SAN_LIB if sanitize else LIB
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        cmd = [cc, "-c", os.path.join(HERE, src), "-o", obj] + common_flags() + EXTRA.get(src, [])
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
+        cmd = ([cc, "-c", os.path.join(HERE, src), "-o", obj] + common_flags() + EXTRA.get(src, []) +
+               (SAN_HOST if sanitize else []))
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,13 +70,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
 
     with ThreadPoolExecutor(max(1, min(jobs, len(SOURCES)))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib_out + ".tmp"
     cmd = [cc, "-shared", "--offload-arch=gfx950", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True, capture_output=not verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib_out)
+    return lib_out
 
 
 if __name__ == "__main__":

@@ -105,10 +105,11 @@ __global__ void init_centroids_kernel(const T *x, Strides xs, int H, int N, int 
 }
 
 // labels[t] = argmin_j |x_t - c_j|^2.  fp32 distances, each a sequential fused
-// sum of squared differences (relative error < (D + 2) 2^-24); whenever the two
-// best candidates are within 4e-5 relative of each other (more than twice that
-// bound) they are re-compared in fp64 with unfused operations in the order
-// k = 0..D-1, ties to the lower index.
+// sum of squared differences (relative error < (D + 2) 2^-24).  The fp32 argmin
+// stands unless the runner-up lies within 4e-5 relative of the best (more than
+// twice that bound); then every centroid is re-compared in fp64 with unfused
+// operations in the order k = 0..D-1, ties to the lower index (a third candidate
+// may be as close as the runner-up, so the rescan covers all of them).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void assign_kernel(const T *x, Strides xs, int H, int N, int C,
                                                      const float *cent, int32_t *labels)
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const T *x, Strides xs, int
     for (int k = 0; k < D; k += 8) load8(xr + k, xv + k);
     const float *ch = cent + (int64_t)bh * C * D;
     float best = INFINITY, second = INFINITY;
-    int bi = 0, si = 0;
+    int bi = 0;
     for (int c0 = 0; c0 < C; c0 += kAssignTile) {
         const int nc = min(kAssignTile, C - c0);
         __syncthreads();
@@ -138,23 +139,25 @@ __global__ __launch_bounds__(256) void assign_kernel(const T *x, Strides xs, int
             }
             const int j = c0 + jj;
             if (s < best) {
-                second = best; si = bi; best = s; bi = j;
+                second = best; best = s; bi = j;
             } else if (s < second) {
-                second = s; si = j;
+                second = s;
             }
         }
     }
     if (!valid) return;
     if (C > 1 && second - best <= 4e-5f * second) {
-        double d1 = 0.0, d2 = 0.0;
-        const float *c1 = ch + (int64_t)bi * D, *c2 = ch + (int64_t)si * D;
-        for (int k = 0; k < D; ++k) {
-            double a1 = __dsub_rn((double)xv[k], (double)c1[k]);
-            double a2 = __dsub_rn((double)xv[k], (double)c2[k]);
-            d1 = __dadd_rn(d1, __dmul_rn(a1, a1));
-            d2 = __dadd_rn(d2, __dmul_rn(a2, a2));
+        double bd = INFINITY;
+        for (int j = 0; j < C; ++j) {
+            const float *cj = ch + (int64_t)j * D;
+            double dj = 0.0;
+#pragma unroll
+            for (int k = 0; k < D; ++k) {
+                const double a = __dsub_rn((double)xv[k], (double)cj[k]);
+                dj = __dadd_rn(dj, __dmul_rn(a, a));
+            }
+            if (dj < bd) { bd = dj; bi = j; }
         }
-        if (d2 < d1 || (d2 == d1 && si < bi)) bi = si;
     }
     labels[(int64_t)bh * N + t] = bi;
 }
@@ -484,13 +487,16 @@ __global__ __launch_bounds__(256) void gather_kernel(const T *x, Strides xs, con
 // exact in bf16; each fp32 centroid, times -2 (exact), is split into bf16 planes
 // hi + lo (16 significant bits, residual <= 2^-16 |c|); padded rows have norm 1e30.
 // The norms enter the same accumulation through one more k step: |c|^2 and
-// |x|^2 + 1 are each split exactly into three bf16 parts (24 significant bits),
-// paired with ones, so the accumulator holds |x - c|^2 + 1 itself.  Per
+// |x|^2 + M are each split exactly into three bf16 parts (24 significant bits),
+// paired with ones, so the accumulator holds |x - c|^2 + M itself, M a per-token
+// margin above the screening error (so the accumulator stays positive).  Per
 // token the four best candidates are kept; whenever a rival lies within
 // tau = 1e-4 (|x|^2 + max_j |c_j|^2) -- several times the worst-case error of the
-// split and of fp32 accumulation -- the decision is re-taken in fp64 with the
-// same unfused arithmetic as the exact definition (the close candidates, or
-// every centroid when all kept candidates are close), ties to the lower index.
+// split and of fp32 accumulation -- the decision is re-taken on fp64 distances
+// (the close candidates, or every centroid when all kept candidates are close),
+// ties to the lower index.  Those fp64 distances are per-lane fused sums over a
+// few dims, then a fixed butterfly over 16 lanes: a different rounding order from
+// the plain sequential sum of the definition, which matters only at fp64 ties.
 constexpr int kCT = 32;  // centroids per MFMA tile
 
 // Exact split of an fp32 value into three bf16 parts, largest first.
@@ -753,24 +759,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
             }
         xn[tb] = ss + __shfl_xor(ss, 32);
     }
-    // keys hold |x|^2 + 1 + |c|^2 - 2<x,c> >= 1 (so they are positive normal floats)
     int ibits = 1;
     while ((1 << ibits) < Cpad) ++ibits;
     const uint32_t imask = (1u << ibits) - 1u, hi_mask = ~imask;
-    // B operand of the norm step: [1, 1, 1, (|x|^2 + 1) in three parts] in k = 0..7
-    // (lanes of the first half-wave), zero in k = 8..15
-    bf16x8 xaug[2];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-        const float xn1 = xn[tb] + 1.0f;
-        const uint16_t h = f32_to_bf16_bits(xn1);
-        const float r1 = xn1 - bf16_bits_to_f32(h);
-        const uint16_t m = f32_to_bf16_bits(r1);
-        const uint16_t l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
-        const uint16_t parts[8] = {0x3F80, 0x3F80, 0x3F80, h, m, l, 0, 0};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xaug[tb][e] = __builtin_bit_cast(__bf16, (uint16_t)(hl ? 0 : parts[e]));
-    }
     constexpr int TK = topk_of<D>();
     TopK<TK> top[2];
 #pragma unroll
@@ -783,6 +774,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const float cm = fmaxf(fmaxf(cm_part[0], cm_part[1]), fmaxf(cm_part[2], cm_part[3]));
+    // B operand of the norm step: [1, 1, 1, (|x|^2 + M) in three parts] in k = 0..7
+    // (lanes of the first half-wave), zero in k = 8..15.  The margin
+    // M = 1 + 1e-4 (|x|^2 + max|c|^2) is the same for every centroid of the token, so
+    // it leaves the ranking alone; it exceeds the worst-case screening error (the
+    // decision window below is built on the same bound), so every accumulator ends
+    // >= 1 even where |x - c|^2 is 0 and the norms are large: keys stay positive
+    // floats and order like their bits.
+    bf16x8 xaug[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const float xn1 = xn[tb] + fmaf(1e-4f, xn[tb] + cm, 1.0f);
+        const uint16_t h = f32_to_bf16_bits(xn1);
+        const float r1 = xn1 - bf16_bits_to_f32(h);
+        const uint16_t m = f32_to_bf16_bits(r1);
+        const uint16_t l = f32_to_bf16_bits(r1 - bf16_bits_to_f32(m));
+        const uint16_t parts[8] = {0x3F80, 0x3F80, 0x3F80, h, m, l, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xaug[tb][e] = __builtin_bit_cast(__bf16, (uint16_t)(hl ? 0 : parts[e]));
+    }
     for (int tile = 0; tile < ntiles; tile += 2) {
         // tile in tb0 while tile+1 loads into tb1, then the reverse
         if (tile + 1 < ntiles) planes_direct<D>(tb1, pb, ab, Cpad, tile + 1, wave, lane);
@@ -1016,19 +1026,11 @@ isg_status dispatch_d(int d, hipStream_t st, const T *x, Strides xs, int B, int 
     }
 }
 
-}  // namespace
-
-extern "C" size_t isg_cluster_workspace_size(int B, int H, int N, int d, int C)
-{
-    if (B < 1 || H < 1 || N < 1 || C < 1 || d < 1) return 0;
-    return cluster_ws(B, H, N, d, C).total;
-}
-
-extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
-                                  int B, int H, int N, int d, int C, int iters, int init_mode,
-                                  const void *companion, float *centroids, int32_t *labels, int32_t *perm,
-                                  int32_t *offsets, void *x_perm, void *companion_perm, float *max_sqnorm,
-                                  void *workspace, size_t ws_bytes)
+// Host-side checks of isg_cluster's arguments (everything but the workspace).
+isg_status check_cluster_args(const void *x, isg_dtype dt, const int64_t x_strides[3], int B, int H, int N,
+                              int d, int C, int iters, int init_mode, const void *companion,
+                              const float *centroids, const int32_t *labels, const int32_t *perm,
+                              const int32_t *offsets, const void *x_perm, const void *companion_perm)
 {
     ISG_REQUIRE(x && x_strides && centroids && labels && perm && offsets, ISG_E_ARG,
                 "isg_cluster: null pointer argument");
@@ -1052,12 +1054,15 @@ extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, con
     ISG_REQUIRE(((uintptr_t)x & 15) == 0 && ((uintptr_t)companion & 15) == 0 && ((uintptr_t)x_perm & 15) == 0 &&
                     ((uintptr_t)companion_perm & 15) == 0,
                 ISG_E_ARG, "isg_cluster: x / companion / outputs must be 16-byte aligned");
-    const size_t need = isg_cluster_workspace_size(B, H, N, d, C);
-    ISG_REQUIRE(workspace && ws_bytes >= need, ISG_E_WORKSPACE, "isg_cluster: workspace %zu < %zu bytes",
-                workspace ? ws_bytes : (size_t)0, need);
-    hipStream_t st = (hipStream_t)stream;
+    return ISG_OK;
+}
+
+isg_status run_checked(hipStream_t st, const void *x, isg_dtype dt, const int64_t x_strides[3], int B, int H,
+                       int N, int d, int C, int iters, int init_mode, const void *companion, float *centroids,
+                       int32_t *labels, int32_t *perm, int32_t *offsets, void *x_perm, void *companion_perm,
+                       float *max_sqnorm, uint8_t *ws)
+{
     Strides xs{x_strides[0], x_strides[1], x_strides[2]};
-    uint8_t *ws = (uint8_t *)workspace;
     if (dt == ISG_F32)
         return dispatch_d<float>(d, st, (const float *)x, xs, B, H, N, C, iters, init_mode,
                                  (const float *)companion, centroids, labels, perm, offsets, (float *)x_perm,
@@ -1065,4 +1070,28 @@ extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, con
     return dispatch_d<uint16_t>(d, st, (const uint16_t *)x, xs, B, H, N, C, iters, init_mode,
                                 (const uint16_t *)companion, centroids, labels, perm, offsets,
                                 (uint16_t *)x_perm, (uint16_t *)companion_perm, max_sqnorm, ws);
+}
+
+}  // namespace
+
+extern "C" size_t isg_cluster_workspace_size(int B, int H, int N, int d, int C)
+{
+    if (B < 1 || H < 1 || N < 1 || C < 1 || d < 1) return 0;
+    return cluster_ws(B, H, N, d, C).total;
+}
+
+extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
+                                  int B, int H, int N, int d, int C, int iters, int init_mode,
+                                  const void *companion, float *centroids, int32_t *labels, int32_t *perm,
+                                  int32_t *offsets, void *x_perm, void *companion_perm, float *max_sqnorm,
+                                  void *workspace, size_t ws_bytes)
+{
+    const isg_status a = check_cluster_args(x, dt, x_strides, B, H, N, d, C, iters, init_mode, companion,
+                                            centroids, labels, perm, offsets, x_perm, companion_perm);
+    if (a != ISG_OK) return a;
+    const size_t need = isg_cluster_workspace_size(B, H, N, d, C);
+    ISG_REQUIRE(workspace && ws_bytes >= need, ISG_E_WORKSPACE, "isg_cluster: workspace %zu < %zu bytes",
+                workspace ? ws_bytes : (size_t)0, need);
+    return run_checked((hipStream_t)stream, x, dt, x_strides, B, H, N, d, C, iters, init_mode, companion, centroids,
+                       labels, perm, offsets, x_perm, companion_perm, max_sqnorm, (uint8_t *)workspace);
 }

@@ -299,7 +299,7 @@ extern "C" isg_status isg_pq_votes(void *stream, const int32_t *q_codes, const f
     ISG_REQUIRE(Cq >= 1 && Cq <= kMaxGroups && Ck >= 1 && Ck <= kMaxGroups, ISG_E_ARG,
                 "isg_pq_votes: Cq, Ck must be in [1, %d]", kMaxGroups);
     ISG_REQUIRE(exact_keys >= 0, ISG_E_ARG, "isg_pq_votes: exact_keys must be >= 0");
-    ISG_REQUIRE(std::isfinite(scale), ISG_E_ARG, "isg_pq_votes: scale must be finite");
+    ISG_REQUIRE(std::isfinite(scale) && scale > 0.0f, ISG_E_ARG, "isg_pq_votes: scale must be finite and > 0");
     const int64_t BH = (int64_t)B * H;
     ISG_REQUIRE(BH <= 65535 && (int64_t)P * Cc <= 65535 && BH * Cq <= (1 << 30), ISG_E_ARG,
                 "isg_pq_votes: grid too large");

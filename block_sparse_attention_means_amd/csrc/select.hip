@@ -428,7 +428,7 @@ extern "C" isg_status isg_probs(void *stream, const float *cq, const float *ck, 
     ISG_REQUIRE(Cq >= 1 && Cq <= kMaxGroups && Ck >= 1 && Ck <= kMaxGroups, ISG_E_ARG,
                 "isg_probs: Cq, Ck must be in [1, %d] (got %d, %d)", kMaxGroups, Cq, Ck);
     ISG_REQUIRE(d >= 1 && d <= 1024, ISG_E_ARG, "isg_probs: d must be in [1, 1024]");
-    ISG_REQUIRE(std::isfinite(scale), ISG_E_ARG, "isg_probs: scale must be finite");
+    ISG_REQUIRE(std::isfinite(scale) && scale > 0.0f, ISG_E_ARG, "isg_probs: scale must be finite and > 0");
     hipStream_t st = (hipStream_t)stream;
     const int64_t G = (int64_t)B * H * ((Cq + kQB - 1) / kQB);
     ISG_REQUIRE((int64_t)B * H * Cq <= 0x7fffffff, ISG_E_ARG, "isg_probs: too many groups");

@@ -12,7 +12,8 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libisg.so")
+# ISG_LIBRARY names another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("ISG_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libisg.so")
 
 ISG_F32, ISG_BF16 = 0, 1
 MODES = {"importance": 0, "uniform": 1, "votes": 2}
@@ -53,10 +54,10 @@ def _declare(L):
     L.isg_probs.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]
     L.isg_select_sample.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _u64, _u64,
                                     _p, _p, _p, _p, _p]
-    L.isg_attention_workspace_size.argtypes = [_i] * 5
+    L.isg_attention_workspace_size.argtypes = [_i] * 6
     L.isg_attention_workspace_size.restype = _sz
     L.isg_attention.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
-                                _i, _f, _p, _p, _p, _p, _p, _sz]
+                                _i, _f, _p, _p, _p, _p, _p, _p, _sz]
     L.isg_unpermute.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p]
     L.isg_select_sample_topp.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _i, _i, _u64, _u64,
                                          _p, _p, _p, _p, _p]
@@ -114,8 +115,29 @@ def cluster_workspace_size(B, H, N, d, C_):
     return int(lib().isg_cluster_workspace_size(B, H, N, d, C_))
 
 
-def attention_workspace_size(B, H, N, Cq, Ck):
-    return int(lib().isg_attention_workspace_size(B, H, N, Cq, Ck))
+def attention_workspace_size(B, H, N, Cq, Ck, m):
+    return int(lib().isg_attention_workspace_size(B, H, N, Cq, Ck, m))
+
+
+
+def cluster_outputs(x, C_, *, companion=None, want_perm=True, want_max_sqnorm=False):
+    """Output tensors of one isg_cluster call on x [B,H,N,d] (allocated here, once)."""
+    B, H, N, d = x.shape
+    dev = x.device
+    labels = torch.empty((B, H, N), device=dev, dtype=torch.int32)
+    return dict(centroids=torch.empty((B, H, C_, d), device=dev, dtype=torch.float32), labels=labels,
+                perm=torch.empty_like(labels), offsets=torch.empty((B, H, C_ + 1), device=dev, dtype=torch.int32),
+                x_perm=torch.empty((B, H, N, d), device=dev, dtype=x.dtype) if want_perm else None,
+                companion_perm=(torch.empty((B, H, N, d), device=dev, dtype=x.dtype) if companion is not None
+                                else None),
+                max_sqnorm=torch.empty((B, H), device=dev, dtype=torch.float32) if want_max_sqnorm else None)
+
+
+def _check_companion(x, companion):
+    if companion is not None:
+        _dev(companion, "companion")
+        if companion.shape != x.shape or companion.stride() != x.stride() or companion.dtype != x.dtype:
+            raise IsgError("companion must match x in shape, strides and dtype")
 
 
 def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, want_max_sqnorm=False,
@@ -124,31 +146,21 @@ def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, want
     With want_max_sqnorm, also the per-head largest squared row norm [B,H] (fp32), which
     isg_attention takes as k_max_sqnorm when x is K."""
     _dev(x, "x")
-    B, H, N, d = x.shape
     if x.stride(3) != 1:
         raise IsgError("x must have a contiguous last dimension")
-    dev = x.device
-    cent = (init.to(device=dev, dtype=torch.float32).contiguous().clone() if init is not None
-            else torch.empty((B, H, C_, d), device=dev, dtype=torch.float32))
-    labels = torch.empty((B, H, N), device=dev, dtype=torch.int32)
-    perm = torch.empty_like(labels)
-    offsets = torch.empty((B, H, C_ + 1), device=dev, dtype=torch.int32)
-    x_perm = torch.empty((B, H, N, d), device=dev, dtype=x.dtype) if want_perm else None
-    comp_perm = None
-    if companion is not None:
-        _dev(companion, "companion")
-        if companion.shape != x.shape or companion.stride() != x.stride() or companion.dtype != x.dtype:
-            raise IsgError("companion must match x in shape, strides and dtype")
-        comp_perm = torch.empty((B, H, N, d), device=dev, dtype=x.dtype)
-    mx = torch.empty((B, H), device=dev, dtype=torch.float32) if want_max_sqnorm else None
+    _check_companion(x, companion)
+    B, H, N, d = x.shape
+    o = cluster_outputs(x, C_, companion=companion, want_perm=want_perm, want_max_sqnorm=want_max_sqnorm)
+    if init is not None:
+        o["centroids"].copy_(init.to(device=x.device, dtype=torch.float32))
     need = cluster_workspace_size(B, H, N, d, C_)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), device=x.device, dtype=torch.uint8)
     st = lib().isg_cluster(_stream(stream), _ptr(x), _dtype(x), _i64x3(x.stride()[:3]), B, H, N, d, C_, iters,
-                           0 if init is None else 1, _ptr(companion), _ptr(cent), _ptr(labels), _ptr(perm),
-                           _ptr(offsets), _ptr(x_perm), _ptr(comp_perm), _ptr(mx), _ptr(ws), ws.numel())
+                           0 if init is None else 1, _ptr(companion), _ptr(o["centroids"]), _ptr(o["labels"]),
+                           _ptr(o["perm"]), _ptr(o["offsets"]), _ptr(o["x_perm"]), _ptr(o["companion_perm"]),
+                           _ptr(o["max_sqnorm"]), _ptr(ws), ws.numel())
     _check(st, "isg_cluster")
-    return dict(centroids=cent, labels=labels, perm=perm, offsets=offsets, x_perm=x_perm,
-                companion_perm=comp_perm, max_sqnorm=mx)
+    return o
 
 
 _side_streams = {}
@@ -249,10 +261,12 @@ def isg_select_sample(scores, k_offsets, N, exact_keys, m, *, mode="importance",
 
 
 def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, k_max_sqnorm=None, perm_q=None,
-                  want_lse=True, out=None, workspace=None, stream=None):
+                  want_lse=True, out=None, workspace=None, n_fallback_tiles=None, stream=None):
     """Attention over each query group's exact and sampled columns.  Rows come out
     in the permuted order of q_p, or in token order when ``perm_q`` (the query
-    permutation from isg_cluster) is given, which fuses the un-permute step."""
+    permutation from isg_cluster) is given, which fuses the un-permute step.
+    ``n_fallback_tiles`` (a one-element int32 GPU tensor) receives the number of
+    query tiles the rescaling fallback recomputed."""
     for n, t in (("q_p", q_p), ("k_p", k_p), ("v_p", v_p)):
         _dev(t, n)
         if not t.is_contiguous():
@@ -262,15 +276,16 @@ def isg_attention(q_p, k_p, v_p, q_offsets, k_offsets, sel, scale, *, k_max_sqno
     Ck = k_offsets.shape[-1] - 1
     o_p = out if out is not None else torch.empty_like(q_p)
     lse_p = torch.empty((B, H, N), device=q_p.device, dtype=torch.float32) if want_lse else None
-    need = attention_workspace_size(B, H, N, Cq, Ck)
-    ws = workspace if workspace is not None else torch.empty(need, device=q_p.device, dtype=torch.uint8)
     m = sel["sample_idx"].shape[-1] if sel.get("m") is None else sel["m"]
+    need = attention_workspace_size(B, H, N, Cq, Ck, m)
+    ws = workspace if workspace is not None else torch.empty(need, device=q_p.device, dtype=torch.uint8)
     st = lib().isg_attention(_stream(stream), _ptr(q_p), _ptr(k_p), _ptr(v_p), _dtype(q_p), B, H, N, d, Cq, Ck,
                              _ptr(q_offsets.contiguous()), _ptr(k_offsets.contiguous()),
                              _ptr(sel["exact_groups"]), _ptr(sel["n_exact"]), _ptr(sel["sample_idx"]),
                              _ptr(sel["sample_bias"]), _ptr(sel["n_sample"]), int(m), float(scale),
                              _ptr(k_max_sqnorm), _ptr(o_p), _ptr(lse_p),
-                             _ptr(None if perm_q is None else perm_q.contiguous()), _ptr(ws), ws.numel())
+                             _ptr(None if perm_q is None else perm_q.contiguous()), _ptr(n_fallback_tiles),
+                             _ptr(ws), ws.numel())
     _check(st, "isg_attention")
     return o_p, lse_p
 
@@ -362,7 +377,8 @@ def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0
     mode "votes"; ``top_p`` sizes the exact set by mass instead of
     ``exact_keys``.  With ``fuse_unpermute`` the attention writes its rows in token
     order itself (o_p and lse_p are then None); otherwise isg_unpermute runs after
-    it.  Returns every intermediate (all on the GPU)."""
+    it.  Returns every intermediate (all on the GPU), and the number of query tiles
+    the attention's rescaling fallback recomputed (``n_fallback_tiles``)."""
     d = q.shape[-1]
     scale = default_scale(d) if scale is None else scale
     cq, ck = cluster_qk(q, k, v, Cq, Ck, iters, stream=stream)
@@ -384,11 +400,13 @@ def pipeline(q, k, v, Cq, Ck, iters, exact_keys, m, *, mode="importance", seed=0
         sel = isg_select_sample(scores, ck["offsets"], q.shape[2], exact_keys, m, mode=mode, seed=seed,
                                 call_id=call_id, votes=None if pqr is None else pqr["votes"], stream=stream)
     args = (cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"], sel, scale)
+    nfb = torch.zeros(1, device=q.device, dtype=torch.int32)
     if fuse_unpermute:
         o_p = lse_p = None
-        o, lse = isg_attention(*args, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], stream=stream)
+        o, lse = isg_attention(*args, k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], n_fallback_tiles=nfb,
+                               stream=stream)
     else:
-        o_p, lse_p = isg_attention(*args, k_max_sqnorm=ck["max_sqnorm"], stream=stream)
+        o_p, lse_p = isg_attention(*args, k_max_sqnorm=ck["max_sqnorm"], n_fallback_tiles=nfb, stream=stream)
         o, lse = isg_unpermute(o_p, lse_p, cq["perm"], stream=stream)
     return dict(cq=cq, ck=ck, scores=scores, pi=pi, pq=pqr, sel=sel, o_p=o_p, lse_p=lse_p, o=o, lse=lse,
-                scale=scale)
+                scale=scale, n_fallback_tiles=nfb)

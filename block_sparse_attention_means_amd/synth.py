@@ -18,6 +18,10 @@ are not available here; these mixtures stand in for them):
   draw from w (random 3-D locality bias);
 * q_t = q_scale * (mu_z + noise_std * eps), k_t = mu_z + noise_std * eps',
   v_t ~ N(0, I_d);
+* optionally (``norm_spread`` s > 0) every q_t and k_t is scaled by its own
+  log-normal factor exp(s * g), g ~ N(0, 1), drawn after everything above (so
+  the other draws are unchanged): a wide spread of |q| |k|, as with the
+  large-norm outlier tokens of real activations;
 * cast to the requested dtype (bf16 uses round-to-nearest-even).
 """
 from __future__ import annotations
@@ -30,7 +34,7 @@ import torch
 
 
 def _head(ss, N, d, n_centers, grid, locality, n_anchors, zipf, q_scale,
-          center_std, noise_std):
+          center_std, noise_std, norm_spread=0.0):
     rng = np.random.Generator(np.random.Philox(ss))
     mu = rng.standard_normal((n_centers, d)) * center_std
     if zipf:
@@ -55,6 +59,9 @@ def _head(ss, N, d, n_centers, grid, locality, n_anchors, zipf, q_scale,
     q = q_scale * (mu[z] + noise_std * rng.standard_normal((N, d)))
     k = mu[z] + noise_std * rng.standard_normal((N, d))
     v = rng.standard_normal((N, d))
+    if norm_spread:
+        q = q * np.exp(norm_spread * rng.standard_normal((N, 1)))
+        k = k * np.exp(norm_spread * rng.standard_normal((N, 1)))
     return (q.astype(np.float32), k.astype(np.float32), v.astype(np.float32),
             z.astype(np.int32))
 
@@ -63,7 +70,7 @@ def make_qkv(H: int, N: int, d: int, *, n_centers: int = 64, grid=None,
              locality: float = 0.75, n_anchors: int = 64, zipf=None,
              q_scale: float = 1.0, center_std: float = 1.0,
              noise_std: float = 0.3, seed: int = 0, dtype: str = "bf16",
-             B: int = 1, threads: int | None = None):
+             B: int = 1, threads: int | None = None, norm_spread: float = 0.0):
     """Return (q, k, v, comp) as CPU tensors of shape [B, H, N, d] (comp: [B, H, N]).
 
     ``dtype`` is "bf16" or "f32". Batch b uses seed ``seed + b``.
@@ -81,7 +88,7 @@ def make_qkv(H: int, N: int, d: int, *, n_centers: int = 64, grid=None,
     def run(job):
         b, h, ss = job
         qh, kh, vh, zh = _head(ss, N, d, n_centers, grid, locality, n_anchors,
-                               zipf, q_scale, center_std, noise_std)
+                               zipf, q_scale, center_std, noise_std, norm_spread)
         q[b, h] = torch.from_numpy(qh).to(tdt)
         k[b, h] = torch.from_numpy(kh).to(tdt)
         v[b, h] = torch.from_numpy(vh).to(tdt)
@@ -125,4 +132,4 @@ def make_workload(w: dict, *, seed: int = 0, threads: int | None = None, H=None,
     return make_qkv(H, N, w["d"], n_centers=w["n_centers"], grid=grid,
                     locality=w.get("locality", 0.75), zipf=w.get("zipf"),
                     q_scale=w.get("q_scale", 1.0), seed=seed, dtype=w["dtype"],
-                    B=w.get("B", 1), threads=threads)
+                    B=w.get("B", 1), threads=threads, norm_spread=w.get("norm_spread", 0.0))

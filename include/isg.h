@@ -56,7 +56,13 @@ typedef enum {
     ISG_E_HIP = 5           /* HIP runtime / launch error */
 } isg_status;
 
-typedef enum { ISG_F32 = 0, ISG_BF16 = 1 } isg_dtype;
+/* dtypes.  A caller may pass any int here (unknown values return ISG_E_DTYPE); the
+ * library is C++, where only a fixed underlying type makes every int a valid value. */
+#ifdef __cplusplus
+typedef enum isg_dtype_e : int { ISG_F32 = 0, ISG_BF16 = 1 } isg_dtype;
+#else
+typedef enum isg_dtype_e { ISG_F32 = 0, ISG_BF16 = 1 } isg_dtype;
+#endif
 
 typedef enum {
     ISG_SAMPLE_IMPORTANCE = 0,  /* proposal ~ n_j exp(S_ij) (quantised), the pages' main mode */
@@ -85,11 +91,15 @@ void isg_proposal_table(uint32_t out[256]);
  *   perm = tokens stably sorted by the last labels; offsets = prefix of counts;
  *   x_perm[r] = x[perm[r]], companion_perm[r] = companion[perm[r]].
  * The labels are the assignment of the last round and the centroids are the
- * means of those groups.  For bf16 x the argmin is decided on fp32 distances
- * (bf16 hi/lo centroid planes on the matrix cores); whenever other kept
- * candidates lie within the fp32 error bound of the best, it is re-decided in
- * fp64 among the four best, or over all C when all four are that close; fp32 x
- * is assigned on fp64 distances throughout.
+ * means of those groups.  For bf16 x the argmin is screened on fp32 distances
+ * (bf16 hi/lo centroid planes on the matrix cores) and the four best are kept;
+ * whenever other kept candidates lie within the screening error bound of the
+ * best, it is re-decided on fp64 distances among the four, or over all C when
+ * all four are that close.  For fp32 x the argmin is taken on fp32 distances
+ * (sequential fused sums) and stands unless the runner-up lies within 4e-5
+ * relative of the best; then every centroid is re-compared in fp64.  Either way
+ * a label differs from the fp64 argmin only at fp64-level ties (the re-decisions
+ * sum in another order than a plain sequential fp64 sum).
  *
  * x           device, dtype dt, element (b,h,t,k) at x[b*xs[0] + h*xs[1] + t*xs[2] + k]
  *             (xs = x_strides, in elements; k contiguous).  [B,N,H,d] and
@@ -125,7 +135,7 @@ isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t 
  *           with n_j = k_offsets[j+1] - k_offsets[j].
  * cq [B,H,Cq,d], ck [B,H,Ck,d] device fp32; k_offsets device int32 [B,H,Ck+1];
  * scores device fp32 [B,H,Cq,Ck] (written); pi device fp32 [B,H,Cq,Ck] or NULL.
- * Cq, Ck in [1, 1024]; d in [1, 1024]. */
+ * Cq, Ck in [1, 1024]; d in [1, 1024]; scale finite and > 0. */
 isg_status isg_probs(void *stream, const float *cq, const float *ck, const int32_t *k_offsets,
                      int B, int H, int Cq, int Ck, int d, float scale, float *scores, float *pi);
 
@@ -207,16 +217,25 @@ isg_status isg_select_sample_topp(void *stream, const float *scores, const float
  * q_p; given (the query permutation from isg_cluster), row r goes to
  * o_p[perm_q[r]] and lse_p[perm_q[r]], i.e. token order, which is what
  * isg_unpermute would produce from the permuted rows (the un-permute fused).
- * workspace device, >= isg_attention_workspace_size(B,H,N,Cq,Ck) bytes. */
-size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck);
+ * n_fallback_tiles device int32 scalar or NULL: bf16 calls write the number of
+ * 128-row query tiles whose weights fell so far below the fixed per-row
+ * reference (row sum < 2^-80) that a second kernel recomputed them with a
+ * running maximum (0 for fp32 calls, which always use a running maximum).
+ * scale is the softmax scale (1/sqrt(d) in the method): finite and > 0, since the
+ * fixed per-row reference of the bf16 kernels bounds the logits only for a
+ * positive scale; anything else returns ISG_E_ARG.
+ * workspace device, >= isg_attention_workspace_size(B,H,N,Cq,Ck,m) bytes (the
+ * column map holds each query group's exact rows, at most N, plus its m samples:
+ * about B*H*Cq*(N+m)*8 bytes).  Returns 0 for an invalid shape (m outside [0, N]). */
+size_t isg_attention_workspace_size(int B, int H, int N, int Cq, int Ck, int m);
 isg_status isg_attention(void *stream, const void *q_p, const void *k_p, const void *v_p,
                          isg_dtype dt, int B, int H, int N, int d, int Cq, int Ck,
                          const int32_t *q_offsets, const int32_t *k_offsets,
                          const int32_t *exact_groups, const int32_t *n_exact,
                          const int32_t *sample_idx, const float *sample_bias,
                          const int32_t *n_sample, int m, float scale, const float *k_max_sqnorm,
-                         void *o_p, float *lse_p, const int32_t *perm_q, void *workspace,
-                         size_t ws_bytes);
+                         void *o_p, float *lse_p, const int32_t *perm_q, int32_t *n_fallback_tiles,
+                         void *workspace, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------ */
 /* isg_unpermute -- rows back to token order: o[perm_q[r]] = o_p[r] (and lse).
@@ -255,7 +274,7 @@ isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, cons
  * tables  device fp32 [B,H,P,Cc,Ck] (written);
  * votes   device int32 [B,H,Cq,Ck] (written).
  * d <= 256, 1 <= P <= 16, P | d; Cc in [1, 4096]; Cq, Ck in [1, 1024];
- * exact_keys >= 0; codes must lie in [0, Cc) (not checked). */
+ * exact_keys >= 0; scale finite and > 0; codes must lie in [0, Cc) (not checked). */
 isg_status isg_pq_votes(void *stream, const int32_t *q_codes, const float *q_codebooks,
                         const int32_t *k_codes, const float *k_codebooks, const int32_t *perm_q,
                         const int32_t *q_offsets, const int32_t *perm_k, const int32_t *k_offsets,

@@ -18,11 +18,14 @@ _lib = None
 
 
 def lib():
+    """The compiled oracle; ISG_ORACLE_LIB names another build of the same source
+    (the sanitizer test's)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB):
+        path = os.environ.get("ISG_ORACLE_LIB") or LIB
+        if path == LIB and not os.path.exists(LIB):
             build()
-        _lib = C.CDLL(LIB)
+        _lib = C.CDLL(path)
         _declare(_lib)
     return _lib
 

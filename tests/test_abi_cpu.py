@@ -76,7 +76,8 @@ def _probs(**kw):
 
 
 @pytest.mark.parametrize("kw", [dict(cq=None), dict(s=None), dict(Cq=0), dict(Ck=2000), dict(d=0),
-                                dict(scale=float("inf")), dict(scale=float("nan"))])
+                                dict(scale=float("inf")), dict(scale=float("nan")), dict(scale=0.0),
+                                dict(scale=-0.125)])
 def test_probs_rejects(kw):
     assert _probs(**kw) == 1
 
@@ -122,17 +123,18 @@ def test_select_allows_empty_sample_arrays_when_m_is_zero():
 def _attn(**kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dt=1, B=1, H=1, N=256, d=128, Cq=4, Ck=8, qo=FAKE, ko=FAKE, eg=FAKE,
              ne=FAKE, si=FAKE, sb=FAKE, ns=FAKE, m=16, scale=0.088, kmx=None, o=FAKE, lse=None, pq=None,
-             ws=FAKE, wsb=1 << 40)
+             nfb=None, ws=FAKE, wsb=1 << 40)
     a.update(kw)
     return isg.lib().isg_attention(None, a["q"], a["k"], a["v"], a["dt"], a["B"], a["H"], a["N"], a["d"],
                                    a["Cq"], a["Ck"], a["qo"], a["ko"], a["eg"], a["ne"], a["si"], a["sb"],
-                                   a["ns"], a["m"], a["scale"], a["kmx"], a["o"], a["lse"], a["pq"], a["ws"],
-                                   a["wsb"])
+                                   a["ns"], a["m"], a["scale"], a["kmx"], a["o"], a["lse"], a["pq"], a["nfb"],
+                                   a["ws"], a["wsb"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(o=None), 1), (dict(si=None), 1), (dict(dt=5), 2), (dict(d=96), 3),
     (dict(d=16), 3), (dict(Cq=0), 1), (dict(Ck=4096), 1), (dict(m=257), 1), (dict(scale=float("nan")), 1),
+    (dict(scale=0.0), 1), (dict(scale=-0.088), 1), (dict(scale=float("-inf")), 1),
     (dict(ws=None), 4), (dict(wsb=100), 4), (dict(v=C.c_void_p(264)), 1), (dict(B=2, H=40000), 1),
 ])
 def test_attention_rejects(kw, status):
@@ -140,11 +142,28 @@ def test_attention_rejects(kw, status):
 
 
 def test_workspace_sizes_grow_with_shape():
-    a = isg.attention_workspace_size(1, 1, 1000, 8, 32)
-    b = isg.attention_workspace_size(1, 2, 1000, 8, 32)
+    a = isg.attention_workspace_size(1, 1, 1000, 8, 32, 100)
+    b = isg.attention_workspace_size(1, 2, 1000, 8, 32, 100)
     assert 0 < a < b
     assert isg.cluster_workspace_size(1, 1, 5000, 128, 100) > isg.cluster_workspace_size(1, 1, 500, 128, 100) > 0
-    assert isg.attention_workspace_size(0, 1, 10, 1, 1) == 0
+    assert isg.attention_workspace_size(0, 1, 10, 1, 1, 0) == 0
+    assert isg.attention_workspace_size(1, 1, 10, 1, 1, 11) == 0  # m > N
+    assert isg.attention_workspace_size(1, 1, 10, 1, 1, -1) == 0
+
+
+def test_attention_workspace_follows_m():
+    """The column map is sized for N exact rows plus the call's m samples per group:
+    at the 14B 720p shape and m = 6,048 that is about half of what m = N needs."""
+    H, N, Cq, Ck = 40, 75600, 100, 500
+    small = isg.attention_workspace_size(1, H, N, Cq, Ck, 6048)
+    full = isg.attention_workspace_size(1, H, N, Cq, Ck, N)
+    assert small < 0.6 * full
+    assert abs(small - H * Cq * (N + 6048) * 8) < 0.01 * small
+    # a workspace sized for a smaller m is refused by a call with a larger m
+    ws = isg.attention_workspace_size(1, 1, 256, 4, 8, 8)
+    assert ws < isg.attention_workspace_size(1, 1, 256, 4, 8, 128)
+    assert _attn(m=128, wsb=ws) == 4
+    assert _attn(m=8, wsb=ws, scale=0.0) == 1
 
 
 def _unperm(**kw):
@@ -174,7 +193,8 @@ def _pq(**kw):
 
 @pytest.mark.parametrize("kw", [dict(qc=None), dict(votes=None), dict(tab=None), dict(N=0), dict(d=512),
                                 dict(P=3), dict(P=32, d=256), dict(Cc=0), dict(Cc=5000), dict(Cq=0),
-                                dict(Ck=1025), dict(E=-1), dict(scale=float("inf"))])
+                                dict(Ck=1025), dict(E=-1), dict(scale=float("inf")), dict(scale=0.0),
+                                dict(scale=-1.0)])
 def test_pq_votes_rejects(kw):
     assert _pq(**kw) == 1
     assert len(isg.lib().isg_last_error()) > 0

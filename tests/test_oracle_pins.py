@@ -408,6 +408,22 @@ def test_every_skipped_token_weight_one_is_exact(orc):
     assert np.abs(lse[0, 0] - lse_ref).max() < 1e-12
 
 
+def seed_summary_z(x, target):
+    """z-score of the mean over seeds of a per-seed summary: each seed's estimates,
+    standardised per element by their spread over the seeds, averaged over the
+    elements.  Elements of one query group share a sample, so their per-element z
+    are correlated and their plain mean is not N(0, 1/#elements); the seeds are
+    independent, so this summary's z is N(0, 1) when the estimator is unbiased.
+    Elements with no spread (a fully enumerated skipped region) are left out."""
+    x = np.asarray(x, np.float64)
+    t = np.broadcast_to(np.asarray(target, np.float64), x.shape[1:]).reshape(-1)
+    x = x.reshape(x.shape[0], -1)
+    sd = x.std(0, ddof=1)
+    keep = sd > 1e-12 * np.maximum(np.abs(t), 1e-300)
+    T = ((x[:, keep] - t[keep]) / sd[keep]).mean(1)
+    return float(T.mean() / (T.std(ddof=1) / math.sqrt(x.shape[0])))
+
+
 def _unbiased_stats(orc, bias_tamper=None, seeds=1000, mode=0):
     q, k, v, cq, ck, S, scale = _clustered(orc, N=256, d=16, Cq=4, Ck=16, seed=2)
     q = q * 0.5   # softer attention so the skipped region carries real mass
@@ -434,18 +450,18 @@ def _unbiased_stats(orc, bias_tamper=None, seeds=1000, mode=0):
         se = x.std(0, ddof=1) / math.sqrt(x.shape[0])
         return (mu - target) / np.maximum(se, 1e-300)
 
-    return z(Dh, 1.0).ravel(), z(Nh, o_ref).ravel()
+    return (z(Dh, 1.0).ravel(), seed_summary_z(Dh, 1.0)), (z(Nh, o_ref).ravel(), seed_summary_z(Nh, o_ref))
 
 
 @pytest.mark.parametrize("mode", [0, 1])
 def test_unbiased_over_1000_seeds(orc, mode):
     """The mean over 1,000 seeds of the denominator (e^LSE) and numerator (O e^LSE)
     estimates converges to the dense ones: per-element z-scores, fraction |z| > 4 at
-    most 0.1 % and the mean z within 4/sqrt(#elements)."""
-    for zz in _unbiased_stats(orc, mode=mode):
+    most 0.1 %, and the seed-level summary's z within 4."""
+    for zz, zs in _unbiased_stats(orc, mode=mode):
+        print(f"mode {mode}: max |z| {np.abs(zz).max():.2f}, summary z {zs:.2f}")
         assert np.mean(np.abs(zz) > 4) <= 1e-3
-        # elements of one query group share a sample, so their z are correlated: loose bound
-        assert abs(zz.mean()) < 0.5
+        assert abs(zs) < 4
 
 
 def test_unbiased_negative_control(orc):
@@ -459,8 +475,9 @@ def test_unbiased_negative_control(orc):
             rows = sel["sample_idx"][0, 0, i, :ns]
             g = np.searchsorted(off, rows, side="right") - 1
             sel["sample_bias"][0, 0, i, :ns] -= np.log(n[g]).astype(np.float32)
-    zd, zn = _unbiased_stats(orc, bias_tamper=tamper, seeds=200)
+    (zd, zsd), (zn, zsn) = _unbiased_stats(orc, bias_tamper=tamper, seeds=200)
     assert np.mean(np.abs(zd) > 4) > 0.5
+    assert abs(zsd) > 10
 
 
 def test_unpermute_inverts_perm(orc):
@@ -558,40 +575,106 @@ def test_pq_exact_quantisation_reproduces_centroid_ranking(orc):
     assert np.array_equal(selv["exact_groups"], sel["exact_groups"])
 
 
-def test_pq_votes_brute_force(orc):
-    """Votes against a direct numpy evaluation of the same reading on a tiny head."""
-    q, k, cq, ck, P, Cc = _pq_case(orc, seed=4)
-    qc, qcb = orc.pq_codebooks(q, P, Cc, 5)
-    kc, kcb = orc.pq_codebooks(k, P, Cc, 5)
-    scale = 0.5
-    kbar = orc.pq_kbar(kc, kcb, ck["perm"], ck["offsets"])
-    tables = orc.pq_tables(qcb, kbar, scale)
-    E = 50
-    votes = orc.pq_votes(qc, tables, cq["perm"], cq["offsets"], ck["offsets"], E)
-    ds = q.shape[-1] // P
+def _pq_reference(q, k, cq, ck, P, kc, kcb, qc, qcb, scale):
+    """Direct fp64 numpy evaluation of the PQ reading: reconstructed keys and queries
+    (codewords per subspace), key-group means in fp64, per-query group scores."""
     ko = ck["offsets"][0, 0]
     n_k = np.diff(ko)
-    # direct: per-key reconstruction, group means, per-query scores from reconstructed q
     krec = np.concatenate([kcb[s, 0, 0][kc[s, 0, 0]] for s in range(P)], 1).astype(np.float64)
     qrec = np.concatenate([qcb[s, 0, 0][qc[s, 0, 0]] for s in range(P)], 1).astype(np.float64)
     kperm = krec[ck["perm"][0, 0]]
     gmean = np.stack([kperm[ko[j]:ko[j + 1]].mean(0) if n_k[j] else np.zeros(q.shape[-1]) for j in range(len(n_k))])
-    want = np.zeros_like(votes[0, 0])
+    return n_k, qrec, gmean, scale * (qrec @ gmean.T)
+
+
+def _walk(sc, n_k, E, stop_at_equal=False):
+    """The exact-set rule on one query's ranking (score desc, group asc): the groups
+    taken, and the smallest score gap between neighbours among the ranked groups the
+    walk looked at (the taken ones, the one that stopped it, and the next one)."""
+    order = sorted([j for j in range(len(n_k)) if n_k[j]], key=lambda j: (-sc[j], j))
+    taken, cum = [], 0
+    for p_, j in enumerate(order):
+        over = cum + n_k[j] >= E if stop_at_equal else cum + n_k[j] > E
+        if p_ > 0 and over:
+            break
+        cum += n_k[j]
+        taken.append(j)
+    look = order[:min(len(order), len(taken) + 2)]
+    gaps = [abs(sc[look[p]] - sc[look[p + 1]]) for p in range(len(look) - 1)]
+    return taken, (min(gaps) if gaps else np.inf)
+
+
+@pytest.mark.parametrize("seed,scale", [(4, 0.5), (8, 0.3), (13, 1.0)])
+def test_pq_votes_brute_force(orc, seed, scale):
+    """Votes against a direct fp64 numpy evaluation of the same reading on a tiny head.
+    Every query whose ranking has no two groups within 1e-5 up to where the budget walk
+    stops must vote exactly as the direct evaluation (the table path sums in fp32 in
+    another order, which can only swap groups closer than that); the remaining
+    near-tie queries are counted and bound the difference.  The budget sits exactly
+    at a cumulative group size of one query, so a >= for > slip in the rule changes
+    the votes (negative control on the reference)."""
+    q, k, cq, ck, P, Cc = _pq_case(orc, seed=seed)
+    qc, qcb = orc.pq_codebooks(q, P, Cc, 5)
+    kc, kcb = orc.pq_codebooks(k, P, Cc, 5)
+    kbar = orc.pq_kbar(kc, kcb, ck["perm"], ck["offsets"])
+    tables = orc.pq_tables(qcb, kbar, scale)
+    n_k, qrec, gmean, sc = _pq_reference(q, k, cq, ck, P, kc, kcb, qc, qcb, scale)
     qo = cq["offsets"][0, 0]
-    for i in range(len(qo) - 1):
+    t0 = cq["perm"][0, 0, 0]
+    order0 = sorted([j for j in range(len(n_k)) if n_k[j]], key=lambda j: (-sc[t0, j], j))
+    E = int(n_k[order0[0]] + n_k[order0[1]] + n_k[order0[2]])
+    votes = orc.pq_votes(qc, tables, cq["perm"], cq["offsets"], ck["offsets"], E)[0, 0]
+    Cq_, Ck_ = votes.shape
+    want = np.zeros((Cq_, Ck_), np.int64)
+    slip = np.zeros((Cq_, Ck_), np.int64)
+    near = np.zeros(Cq_, np.int64)
+    for i in range(Cq_):
         for r in range(qo[i], qo[i + 1]):
             t = cq["perm"][0, 0, r]
-            sc = scale * gmean @ qrec[t]
-            order = sorted([j for j in range(len(n_k)) if n_k[j]], key=lambda j: (-sc[j], j))
-            cum = 0
-            for p_, j in enumerate(order):
-                if p_ > 0 and cum + n_k[j] > E:
-                    break
-                cum += n_k[j]
-                want[i, j] += 1
-    # float rounding of the table path can reorder near-equal scores: demand near-total agreement
-    assert (votes[0, 0] == want).mean() > 0.97
-    assert np.all(votes[0, 0].sum(1) >= np.diff(qo))
+            taken, gap = _walk(sc[t], n_k, E)
+            for j in _walk(sc[t], n_k, E, stop_at_equal=True)[0]:
+                slip[i, j] += 1
+            if gap > 1e-5:
+                for j in taken:
+                    want[i, j] += 1
+            else:
+                near[i] += 1
+    print(f"PQ votes seed {seed}: {int(near.sum())} of {int(qo[-1])} queries have a near-tie in their ranking")
+    resid = votes.astype(np.int64) - want
+    for i in range(Cq_):
+        if near[i] == 0:
+            assert np.array_equal(resid[i], np.zeros(Ck_)), i
+        else:
+            assert (resid[i] >= 0).all() and (resid[i] <= near[i]).all(), i
+    assert near.sum() <= 0.05 * qo[-1]
+    assert np.all(votes.sum(1) >= np.diff(qo))
+    assert not np.array_equal(slip, votes)
+
+
+def test_pq_kbar_and_tables_against_numpy(orc):
+    """Kbar = fp64 mean of each key group's reconstructed sub-vectors (0 for an empty
+    group) and M_s[a][j] = scale <cw^q_{s,a}, Kbar_{j,s}>, both against direct numpy fp64
+    within 1e-6 relative (the oracle rounds to fp32; its tables are an fp32 fma chain)."""
+    q, k, cq, ck, P, Cc = _pq_case(orc, seed=6)
+    qc, qcb = orc.pq_codebooks(q, P, Cc, 5)
+    kc, kcb = orc.pq_codebooks(k, P, Cc, 5)
+    ko = ck["offsets"].copy()
+    ko[0, 0, 4] = ko[0, 0, 3]  # group 3 empty (its rows join group 4)
+    kbar = orc.pq_kbar(kc, kcb, ck["perm"], ko)
+    ck2 = dict(ck, offsets=ko)
+    scale = 0.37
+    n_k, _, gmean, _ = _pq_reference(q, k, cq, ck2, P, kc, kcb, qc, qcb, scale)
+    assert n_k[3] == 0 and np.all(kbar[0, 0, 3] == 0)
+    big = np.abs(gmean).max()
+    assert np.allclose(kbar[0, 0], gmean, rtol=1e-6, atol=1e-6 * big)
+    tables = orc.pq_tables(qcb, kbar, scale)
+    ds = q.shape[-1] // P
+    kb = kbar[0, 0].astype(np.float64).reshape(len(n_k), P, ds)
+    want = scale * np.einsum("sae,jse->saj", qcb[:, 0, 0].astype(np.float64), kb)
+    assert tables.shape[-3:] == want.shape
+    assert np.allclose(tables[0, 0], want, rtol=1e-6, atol=1e-6 * np.abs(want).max())
+    # a dropped subspace term or a transposed operand would be far off
+    assert not np.allclose(tables[0, 0][1:], want[:-1], rtol=1e-3)
 
 
 # ---------------------------------------------------------------- top-p exact-set sizing
