@@ -8,6 +8,7 @@
 // Per round: assign (labels) -> per-chunk histograms -> scan over chunks ->
 // label offsets + stable scatter (perm, offsets) -> segmented fp64 mean in sorted order
 // (centroids).  No float atomics: every output is deterministic.
+#include <mutex>
 #include <type_traits>
 
 #include "isg_internal.h"
@@ -1026,7 +1027,8 @@ isg_status dispatch_d(int d, hipStream_t st, const T *x, Strides xs, int B, int 
     }
 }
 
-// Host-side checks of isg_cluster's arguments (everything but the workspace).
+// Host-side checks shared by isg_cluster and isg_cluster_noalloc (everything but
+// the workspace).
 isg_status check_cluster_args(const void *x, isg_dtype dt, const int64_t x_strides[3], int B, int H, int N,
                               int d, int C, int iters, int init_mode, const void *companion,
                               const float *centroids, const int32_t *labels, const int32_t *perm,
@@ -1072,6 +1074,58 @@ isg_status run_checked(hipStream_t st, const void *x, isg_dtype dt, const int64_
                                 (uint16_t *)x_perm, (uint16_t *)companion_perm, max_sqnorm, ws);
 }
 
+// ---------------------------------------------------------------- scratch of isg_cluster_noalloc
+// A fixed device array takes the place of the caller's workspace.  Every GPU the
+// library runs on holds its own copy (allocated with the code object, kept until
+// the process ends).  In host code `scratch` names a host-side stand-in, not a
+// device address, so it is never passed to a kernel: its device address is looked
+// up once per device and only that pointer is used.  Every call on one GPU shares
+// the array; nothing in it has to start at zero (each round writes every word it
+// later reads), and calls that overlap on one GPU race.
+constexpr size_t kNoAllocScratchBytes = (size_t)ISG_CLUSTER_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch`, resolved on the first call
+// for that device with the device current.
+isg_status scratch_for_stream(hipStream_t st, uint8_t **out)
+{
+    int dev = 0;
+    if (st) {
+        hipDevice_t sd = 0;
+        const hipError_t e = hipStreamGetDevice(st, &sd);
+        if (e != hipSuccess) return isg_fail(ISG_E_HIP, "isg_cluster_noalloc: hipStreamGetDevice: %s",
+                                             hipGetErrorString(e));
+        dev = (int)sd;
+    } else {
+        const hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return isg_fail(ISG_E_HIP, "isg_cluster_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    }
+    ISG_REQUIRE(dev >= 0 && dev < kMaxDevices, ISG_E_UNSUPPORTED, "isg_cluster_noalloc: device %d >= %d", dev,
+                kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = 0;
+        hipError_t e = hipGetDevice(&cur);
+        if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+        void *p = nullptr;
+        if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess || !p)
+            return isg_fail(ISG_E_HIP, "isg_cluster_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                            hipGetErrorString(e));
+        g_scratch_ptr[dev] = (uint8_t *)p;
+    }
+    *out = g_scratch_ptr[dev];
+    return ISG_OK;
+}
+
 }  // namespace
 
 extern "C" size_t isg_cluster_workspace_size(int B, int H, int N, int d, int C)
@@ -1094,4 +1148,26 @@ extern "C" isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, con
                 workspace ? ws_bytes : (size_t)0, need);
     return run_checked((hipStream_t)stream, x, dt, x_strides, B, H, N, d, C, iters, init_mode, companion, centroids,
                        labels, perm, offsets, x_perm, companion_perm, max_sqnorm, (uint8_t *)workspace);
+}
+
+extern "C" isg_status isg_cluster_noalloc(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
+                                          int B, int H, int N, int d, int C, int iters, int init_mode,
+                                          const void *companion, float *centroids, int32_t *labels,
+                                          int32_t *perm, int32_t *offsets, void *x_perm, void *companion_perm,
+                                          float *max_sqnorm)
+{
+    const isg_status a = check_cluster_args(x, dt, x_strides, B, H, N, d, C, iters, init_mode, companion,
+                                            centroids, labels, perm, offsets, x_perm, companion_perm);
+    if (a != ISG_OK) return a;
+    const size_t need = isg_cluster_workspace_size(B, H, N, d, C);
+    ISG_REQUIRE(need <= kNoAllocScratchBytes, ISG_E_WORKSPACE,
+                "isg_cluster_noalloc: this shape needs %zu bytes of scratch, more than the %zu-byte static array "
+                "(split the heads over several calls, or use isg_cluster with a workspace)",
+                need, kNoAllocScratchBytes);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t *ws = nullptr;
+    const isg_status s = scratch_for_stream(st, &ws);
+    if (s != ISG_OK) return s;
+    return run_checked(st, x, dt, x_strides, B, H, N, d, C, iters, init_mode, companion, centroids, labels, perm,
+                       offsets, x_perm, companion_perm, max_sqnorm, ws);
 }

@@ -19,7 +19,7 @@ ISG_F32, ISG_BF16 = 0, 1
 MODES = {"importance": 0, "uniform": 1, "votes": 2}
 EXPORTS = ["isg_last_error", "isg_version", "isg_proposal_table", "isg_cluster_workspace_size",
            "isg_cluster", "isg_probs", "isg_select_sample", "isg_attention_workspace_size",
-           "isg_attention", "isg_unpermute", "isg_pq_votes", "isg_select_sample_topp"]
+           "isg_attention", "isg_unpermute", "isg_pq_votes", "isg_select_sample_topp", "isg_cluster_noalloc"]
 
 _lib = None
 
@@ -51,6 +51,7 @@ def _declare(L):
     L.isg_cluster_workspace_size.restype = _sz
     L.isg_cluster.argtypes = [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                               _sz]
+    L.isg_cluster_noalloc.argtypes = [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
     L.isg_probs.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _p]
     L.isg_select_sample.argtypes = [_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _u64, _u64,
                                     _p, _p, _p, _p, _p]
@@ -64,7 +65,7 @@ def _declare(L):
     L.isg_pq_votes.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                _p, _p, _p]
     for name in ["isg_cluster", "isg_probs", "isg_select_sample", "isg_attention", "isg_unpermute",
-                 "isg_pq_votes", "isg_select_sample_topp"]:
+                 "isg_pq_votes", "isg_select_sample_topp", "isg_cluster_noalloc"]:
         getattr(L, name).restype = _i
 
 
@@ -119,6 +120,8 @@ def attention_workspace_size(B, H, N, Cq, Ck, m):
     return int(lib().isg_attention_workspace_size(B, H, N, Cq, Ck, m))
 
 
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ISG_CLUSTER_NOALLOC_SCRATCH_BYTES
+
 
 def cluster_outputs(x, C_, *, companion=None, want_perm=True, want_max_sqnorm=False):
     """Output tensors of one isg_cluster call on x [B,H,N,d] (allocated here, once)."""
@@ -161,6 +164,27 @@ def isg_cluster(x, C_, iters, *, init=None, companion=None, want_perm=True, want
                            _ptr(o["max_sqnorm"]), _ptr(ws), ws.numel())
     _check(st, "isg_cluster")
     return o
+
+
+def isg_cluster_noalloc(x, C_, iters, out, *, init_given=False, companion=None, stream=None):
+    """isg_cluster through isg_cluster_noalloc: no workspace (the library's static
+    scratch) and no allocation here either -- every output goes into ``out``, a dict
+    as returned by cluster_outputs (x_perm, companion_perm and max_sqnorm may be
+    None).  With ``init_given`` the call starts from out["centroids"] as they are."""
+    _dev(x, "x")
+    if x.stride(3) != 1:
+        raise IsgError("x must have a contiguous last dimension")
+    _check_companion(x, companion)
+    if (companion is None) != (out.get("companion_perm") is None):
+        raise IsgError("out['companion_perm'] must be given exactly when companion is")
+    B, H, N, d = x.shape
+    st = lib().isg_cluster_noalloc(_stream(stream), _ptr(x), _dtype(x), _i64x3(x.stride()[:3]), B, H, N, d, C_,
+                                   iters, 1 if init_given else 0, _ptr(companion), _ptr(out["centroids"]),
+                                   _ptr(out["labels"]), _ptr(out["perm"]), _ptr(out["offsets"]),
+                                   _ptr(out.get("x_perm")), _ptr(out.get("companion_perm")),
+                                   _ptr(out.get("max_sqnorm")))
+    _check(st, "isg_cluster_noalloc")
+    return out
 
 
 _side_streams = {}

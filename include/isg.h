@@ -125,6 +125,29 @@ isg_status isg_cluster(void *stream, const void *x, isg_dtype dt, const int64_t 
                        void *workspace, size_t ws_bytes);
 
 /* ------------------------------------------------------------------------ */
+/* isg_cluster_noalloc -- isg_cluster without a workspace and without allocating.
+ * For callers that cannot allocate device memory during a call: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, computation and results as isg_cluster (bit for bit), minus the
+ * workspace: its scratch is a static device array of
+ * ISG_CLUSTER_NOALLOC_SCRATCH_BYTES (64 MiB), one copy per GPU, allocated with
+ * the library's code object and held until the process ends.  A shape whose
+ * isg_cluster_workspace_size() exceeds that returns ISG_E_WORKSPACE before
+ * anything is enqueued (every 720p shape of this library's workloads fits: K of
+ * 40 heads x 75,600 tokens at C = 500 needs about 50 MB; split the heads over
+ * several calls otherwise).  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); the first call on a device resolves that device's
+ * copy of the array (hipGetSymbolAddress, with the device current) and keeps the
+ * address.  The stream's device decides which copy is used (NULL: the current
+ * device).  Calls on one GPU share the array: calls that may overlap on one GPU
+ * (two streams, or two host threads) race and must be ordered by the caller. */
+#define ISG_CLUSTER_NOALLOC_SCRATCH_BYTES (64u << 20)
+isg_status isg_cluster_noalloc(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3],
+                               int B, int H, int N, int d, int C, int iters, int init_mode,
+                               const void *companion, float *centroids, int32_t *labels, int32_t *perm,
+                               int32_t *offsets, void *x_perm, void *companion_perm, float *max_sqnorm);
+
+/* ------------------------------------------------------------------------ */
 /* isg_probs -- centroid scores and pi.
  * Pages: InstaGen, thelatestinai.com page, Figure 3(b) (centroid scores give
  * each key group a probability pi of being used by each query group); Paper

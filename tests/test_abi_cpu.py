@@ -68,6 +68,37 @@ def test_cluster_rejects(kw, status):
     assert len(isg.lib().isg_last_error()) > 0
 
 
+def _cluster_noalloc(**kw):
+    a = dict(stream=None, x=FAKE, dt=1, strides=_i64x3(8 * 64 * 128, 64 * 128, 128), B=1, H=8, N=64, d=128,
+             C=8, iters=5, init=0, comp=None, cent=FAKE, lab=FAKE, perm=FAKE, off=FAKE, xp=FAKE, cp=None,
+             mx=None)
+    a.update(kw)
+    return isg.lib().isg_cluster_noalloc(a["stream"], a["x"], a["dt"], a["strides"], a["B"], a["H"], a["N"],
+                                         a["d"], a["C"], a["iters"], a["init"], a["comp"], a["cent"], a["lab"],
+                                         a["perm"], a["off"], a["xp"], a["cp"], a["mx"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(perm=None), 1), (dict(B=0), 1), (dict(dt=3), 2), (dict(d=96), 3), (dict(C=65), 1),
+    (dict(comp=FAKE), 1), (dict(x=C.c_void_p(258)), 1),
+    # more scratch than the static array holds: K clustering of 40 heads at 84 latent frames
+    (dict(H=40, N=302400, C=500, strides=_i64x3(40 * 302400 * 128, 302400 * 128, 128)), 4),
+])
+def test_cluster_noalloc_rejects(kw, status):
+    """Host checks of the no-allocation variant, including a shape beyond its scratch."""
+    assert _cluster_noalloc(**kw) == status
+    assert len(isg.lib().isg_last_error()) > 0
+
+
+def test_noalloc_scratch_covers_the_720p_workloads():
+    from block_sparse_attention_means_amd.workloads import WORKLOADS
+    for name in ("wan1.3b_480p", "wan1.3b_720p", "wan14b_720p", "wan14b_720p_stress_pq"):
+        w = WORKLOADS[name]
+        for C_ in (w["Cq"], w["Ck"]):
+            assert isg.cluster_workspace_size(1, w["H"], w["N"], w["d"], C_) <= isg.NOALLOC_SCRATCH_BYTES, name
+    assert isg.cluster_workspace_size(1, 40, 302400, 128, 500) > isg.NOALLOC_SCRATCH_BYTES
+
+
 def _probs(**kw):
     a = dict(cq=FAKE, ck=FAKE, ko=FAKE, B=1, H=1, Cq=4, Ck=8, d=64, scale=0.125, s=FAKE, pi=None)
     a.update(kw)
