@@ -40,6 +40,9 @@ constexpr int kTQ = 128;         // query rows per bf16 work-group
 constexpr int kTQ32 = 64;        // query rows per fp32 work-group
 constexpr int kMaxGroups = 1024;
 constexpr float kLog2e = 1.4426950408889634f;
+// The fixed per-row reference sits this far (log2 units) below the
+// Cauchy-Schwarz bound of the row's logits: weights are at most 2^64.
+constexpr float kRefShift = 64.0f;
 // 32-row query blocks per wave in the fast bf16 kernel.  Two blocks per wave
 // halve the LDS fragment traffic per product but leave one wave per SIMD, whose
 // single instruction stream serialises LDS latency, exponentials and products;
@@ -438,10 +441,15 @@ __device__ __forceinline__ void tile_step(int t, int T, int X, const uint8_t *kc
 // waves per SIMD.
 //
 // FIXED = true (the fast kernel): every row uses the fixed reference
-//   m_ref = scale log2(e) |q| max|k| + max(offsets, 0) >= every logit of the row
-// (Cauchy-Schwarz), so weights exp2(l - m_ref) never exceed 1 and O, l need no
-// rescaling.  If a row's weight sum ends below 2^-80 (its logits all far below
-// the bound), weights may have underflowed: the tile is flagged in `redo`.
+//   m_ref = scale log2(e) |q| max|k| + max(offsets, 0) - kRefShift,
+// where the first terms bound every logit of the row (Cauchy-Schwarz), so
+// weights exp2(l - m_ref) never exceed 2^kRefShift and O, l need no rescaling.
+// The shift only has to keep sums of such weights (times values) inside the
+// fp32 range; lowering the reference lets rows whose logits sit far below the
+// bound (a wide spread of |q| |k|) keep normal weights.  If a row's weight sum
+// ends below 2^-80 (its logits more than ~80 + kRefShift below the bound),
+// weights may have underflowed, and if a sum or an output is not finite (values
+// beyond ~2^40), something overflowed: either way the tile is flagged in `redo`.
 // FIXED = false (the fallback): running maximum with rescaling; it processes
 // only the flagged tiles.
 template <int D, bool FIXED, int QB>
@@ -503,7 +511,7 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
             if (FIXED) {
                 qss += __shfl_xor(qss, 32);
                 const float kmx = sqrtf(__int_as_float(kmax2[bh]));
-                m_run[qb] = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, col_bmax[gi]) + 1e-6f;
+                m_run[qb] = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, col_bmax[gi]) + 1e-6f - kRefShift;
             }
         }
 
@@ -549,7 +557,13 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
         for (int qb = 0; qb < QB; ++qb) {
             l_tot[qb] = l_run[qb] + __shfl_xor(l_run[qb], 32);
             const int qrow_raw = r0 + wave * WROWS + qb * 32 + l32;
-            low = low || (qrow_raw < r1 && !(l_tot[qb] >= 8.271806e-25f));  // 2^-80
+            // 2^-80: weights may have underflowed; not finite: something overflowed
+            bool bad = !(l_tot[qb] >= 8.271806e-25f) || !(l_tot[qb] < INFINITY);
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bad = bad || !(fabsf(oacc[qb][db][r]) < INFINITY);
+            low = low || (qrow_raw < r1 && bad);
         }
         if (FIXED && __any(low)) {
             if (lane == 0) redo[lb] = 1;
@@ -611,6 +625,14 @@ __global__ __launch_bounds__(256 / QB) __attribute__((amdgpu_waves_per_eu(3 - QB
 // current slot.  Weights as in attn_bf16_kernel<D, true, 1> (fixed reference);
 // the row sums come from an extra product instead of VALU additions.
 constexpr int kPPWaves = 8;
+// The paired-tile kernel lowers each row's fixed reference to at most this far
+// (log2 units) above the largest logit of the row's first column tile.  With the
+// bound kRefShift above it, a row's reference is min(bound - kRefShift, first
+// tile's maximum + kAnchor): the largest weight is then >= 2^-kAnchor (no
+// underflow), and weights exceed 2^kRefShift only where a later logit beats the
+// first tile's maximum by more than kAnchor + kRefShift, far beyond realistic
+// data (the non-finite check catches an actual overflow).
+constexpr float kAnchor = 72.0f;
 constexpr bool kUsePingPong = true;
 constexpr int kPPAhead = 4;  // products whose operands are in flight ahead of use
 constexpr int kPPRing = 8;   // column-index ring: tiles u .. u+4 are live in weight slot u
@@ -663,13 +685,15 @@ __device__ __forceinline__ void load_offsets(f32x16 *sacc, const float *bias, in
 }
 
 // One phase of one half.  SLOT parity and buffer parities are compile-time
-// functions of (J, HALF); the tile index is runtime.
-template <int D, int HALF, int J>
+// functions of (J, HALF); the tile index is runtime.  m_ref is the row's fixed
+// reference, lowered once to the first tile's largest logit + kAnchor, or (RUN,
+// the rescaling pass over flagged tiles) the row's running maximum.
+template <int D, bool RUN, int HALF, int J>
 __device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0, uint8_t *k1, uint8_t *v0,
                                          uint8_t *v1, int (*ring_row)[kTK], float (*ring_bias)[kTK],
                                          const uint16_t *kh, const uint16_t *vh, const bf16x8 *qf, f32x16 *oacc,
                                          f32x16 *sacc, bf16x8 *pb, f32x4 &lacc, const bf16x8 &ones_a,
-                                         const int *zrow, float m_ref, const int *vtr, float scale_log2,
+                                         const int *zrow, float &m_ref, const int *vtr, float scale_log2,
                                          bool wave_active, int wq, int lane, int hl, int l32)
 {
     constexpr int NDS = D / 16;
@@ -770,6 +794,40 @@ __device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0
             tile_issue<D, 4, false>(UP == 0 ? k0 : k1, reinterpret_cast<const uint8_t *>(kh), kr, wq, lane);
             tile_issue<D, 4, true>(UP == 0 ? v1 : v0, reinterpret_cast<const uint8_t *>(vh), vr, wq, lane);
             if (wave_active) {
+                if constexpr (RUN) {
+                    // the largest logit of tile u in this lane's query (the lane holds
+                    // half of the 64 keys, lane l ^ 32 the other half); the maximum is
+                    // raised lazily, only when the tile exceeds it by more than 8, so
+                    // weights stay below 2^8 and O and the row sums (which hold the
+                    // tiles before u) are rescaled rarely
+                    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+                    if (__any(mx > m_ref + 8.0f)) {
+                        const float m_new = fmaxf(m_ref, mx);
+                        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 before the first tile
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                        // row sums: lane l < 16 holds queries l (element 0) and l + 16 (element 1)
+                        const float a16 = __shfl(alpha, (lane & 15) + 16);
+                        lacc[0] *= alpha;
+                        lacc[1] *= a16;
+                        m_ref = m_new;
+                    }
+                } else if (u == 0) {
+                    // anchor: the first tile's largest logit of this lane's query (the
+                    // lane holds half of the 64 keys, lane l ^ 32 the other half) bounds
+                    // the row's maximum from below, so a reference at most kAnchor above
+                    // it keeps the largest weight >= 2^-kAnchor (no underflow)
+                    float mx = fmaxf(sacc[0][0], sacc[1][0]);
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    m_ref = fminf(m_ref, fmaf(mx, scale_log2, kAnchor));
+                }
                 // logits in log2 units: (score + offset) * scale * log2 e
                 const float mneg = -m_ref;
 #pragma unroll
@@ -793,11 +851,11 @@ __device__ __forceinline__ void pp_phase(int c, const PPTile<D> &tt, uint8_t *k0
     }
 }
 
-template <int D, int HALF>
+template <int D, bool RUN, int HALF>
 __device__ __forceinline__ void pp_chunks(int nchunks, const PPTile<D> &tt, uint8_t *k0, uint8_t *k1, uint8_t *v0,
                                           uint8_t *v1, int (*ring_row)[kTK], float (*ring_bias)[kTK],
                                           int *zrow, const uint16_t *kh, const uint16_t *vh, const bf16x8 *qf,
-                                          f32x16 *oacc, f32x4 &lacc, float m_ref, const int *vtr, float scale_log2,
+                                          f32x16 *oacc, f32x4 &lacc, float &m_ref, const int *vtr, float scale_log2,
                                           bool wave_active, int wq, int lane, int hl, int l32)
 {
     constexpr int KB = kTK * D * 2;
@@ -840,26 +898,30 @@ __device__ __forceinline__ void pp_chunks(int nchunks, const PPTile<D> &tt, uint
 #pragma unroll
     for (int e = 0; e < 8; ++e) ones_a[e] = (__bf16)(one ? 1.0f : 0.0f);
     for (int c = 0; c < nchunks; ++c) {
-        pp_phase<D, HALF, 0>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+        pp_phase<D, RUN, HALF, 0>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
                              zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
-        pp_phase<D, HALF, 1>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+        pp_phase<D, RUN, HALF, 1>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
                              zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
-        pp_phase<D, HALF, 2>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+        pp_phase<D, RUN, HALF, 2>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
                              zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
-        pp_phase<D, HALF, 3>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
+        pp_phase<D, RUN, HALF, 3>(c, tt, k0, k1, v0, v1, ring_row, ring_bias, kh, vh, qf, oacc, sacc, pb, lacc, ones_a,
                              zrow, m_ref, vtr, scale_log2, wave_active, wq, lane, hl, l32);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the last (unused) direct loads have landed
 }
 
-template <int D>
+// RUN = false: the fast pass over every tile pair of the table (fixed, anchored
+// reference; tiles whose sums leave the fp32 range are flagged in `redo`).
+// RUN = true: the rescaling pass, over the flagged tiles only (flist holds their
+// ids in ascending order, *nflag their number), with a running maximum per row.
+template <int D, bool RUN>
 __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_pp_kernel(
     const uint16_t *__restrict__ q_p, const uint16_t *__restrict__ k_p, const uint16_t *__restrict__ v_p, int N,
     int Cq, const int4 *__restrict__ table, int nblocks, const int32_t *__restrict__ col_row,
     const float *__restrict__ col_bias, const int32_t *__restrict__ col_len, const int32_t *__restrict__ col_x,
     const float *__restrict__ col_bmax, const int *__restrict__ kmax2, int64_t cap, float scale_log2,
     uint16_t *__restrict__ o_p, float *__restrict__ lse_p, const int32_t *__restrict__ perm_q,
-    int *__restrict__ redo)
+    int *__restrict__ redo, const int *__restrict__ flist, const int *__restrict__ nflag)
 {
     constexpr int NDS = D / 16;
     constexpr int NDB = D / 32;
@@ -883,9 +945,12 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     // both halves' tiles (every wave reads both, so the phase count is uniform)
     int Th[2];
     int4 teh[2];
+    const int nlist = RUN ? *nflag : nblocks;
+    if (2 * lp >= nlist) return;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int tile = 2 * lp + h;
+        const int pos = 2 * lp + h;
+        const int tile = pos < nlist ? (RUN ? flist[pos] : pos) : nblocks;
         teh[h] = tile < nblocks ? table[tile] : make_int4(-1, 0, 0, 0);
         Th[h] = teh[h].x >= 0 ? (col_len[(int64_t)teh[h].w * Cq + teh[h].x] + kTK - 1) / kTK : 0;
     }
@@ -902,32 +967,37 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     tt.r0 = te.y;
     tt.r1 = te.z;
     tt.bh = bh;
-    tt.lb = 2 * lp + half;
+    tt.lb = RUN ? 0 : 2 * lp + half;  // the flag slot (the fast pass only)
     const int64_t gi = (int64_t)bh * Cq + i;
     tt.crow = col_row + gi * cap;
     tt.cbias = col_bias + gi * cap;
     const uint16_t *kh = k_p + (int64_t)bh * N * D;
     const uint16_t *vh = v_p + (int64_t)bh * N * D;
 
-    // Q^T fragments of this wave's 32 rows and the fixed reference
-    // a tile with an empty column list does no products and is flagged below
-    // (zero row sums), as in the single-tile kernel
+    // Q^T fragments of this wave's 32 rows and the row's reference: fixed (lowered
+    // to the first tile's maximum + kAnchor in the first weight slot), or the
+    // running maximum (RUN; -inf before the first tile).  A tile with an empty
+    // column list does no products and is flagged below (zero row sums), as in
+    // the single-tile kernel
     const bool wave_active = te.x >= 0 && tt.r0 + wq * 32 < tt.r1;
     bf16x8 qf[NDS];
-    float m_ref = 0.0f;
+    float m_ref = -INFINITY;
     {
         const int qrow = tt.active ? min(tt.r0 + wq * 32 + l32, tt.r1 - 1) : 0;
         const uint16_t *qsrc = q_p + ((int64_t)bh * N + qrow) * D + hl * 8;
-        float qss = 0.0f;
 #pragma unroll
-        for (int s = 0; s < NDS; ++s) {
-            qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+        for (int s = 0; s < NDS; ++s) qf[s] = *reinterpret_cast<const bf16x8 *>(qsrc + s * 16);
+        if constexpr (!RUN) {
+            float qss = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[s][e], (float)qf[s][e], qss);
+            for (int s = 0; s < NDS; ++s)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qss = fmaf((float)qf[s][e], (float)qf[s][e], qss);
+            qss += __shfl_xor(qss, 32);
+            const float kmx = sqrtf(__int_as_float(kmax2[bh]));
+            m_ref = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, tt.active ? col_bmax[gi] : 0.0f) + 1e-6f -
+                    kRefShift;
         }
-        qss += __shfl_xor(qss, 32);
-        const float kmx = sqrtf(__int_as_float(kmax2[bh]));
-        m_ref = fmaf(scale_log2 * sqrtf(qss) * kmx, 1.0f + 1e-5f, tt.active ? col_bmax[gi] : 0.0f) + 1e-6f;
     }
     int vtr[NDB];
 #pragma unroll
@@ -942,10 +1012,10 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     // each half names its own buffers, so the compiler sees which LDS object every
     // direct load writes and every product reads; both paths pass 4 * nchunks barriers
     if (half == 0)
-        pp_chunks<D, 0>(nchunks, tt, ka0, ka1, va0, va1, ring_row[0], ring_bias[0], zrow, kh, vh, qf, oacc, lacc, m_ref,
+        pp_chunks<D, RUN, 0>(nchunks, tt, ka0, ka1, va0, va1, ring_row[0], ring_bias[0], zrow, kh, vh, qf, oacc, lacc, m_ref,
                         vtr, scale_log2, wave_active, wq, lane, hl, l32);
     else
-        pp_chunks<D, 1>(nchunks, tt, kb0, kb1, vb0, vb1, ring_row[1], ring_bias[1], zrow, kh, vh, qf, oacc, lacc, m_ref,
+        pp_chunks<D, RUN, 1>(nchunks, tt, kb0, kb1, vb0, vb1, ring_row[1], ring_bias[1], zrow, kh, vh, qf, oacc, lacc, m_ref,
                         vtr, scale_log2, wave_active, wq, lane, hl, l32);
 
     if (!wave_active) return;
@@ -954,7 +1024,14 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     const float ls0 = __shfl(lacc[0], l32 & 15), ls1 = __shfl(lacc[1], l32 & 15);
     const float l_tot = l32 < 16 ? ls0 : ls1;
     const int qrow_raw = tt.r0 + wq * 32 + l32;
-    if (__any(qrow_raw < tt.r1 && !(l_tot >= 8.271806e-25f))) {  // 2^-80: hand the tile to the fallback
+    // 2^-80: weights may have underflowed; not finite: something overflowed.  Either
+    // hands the tile to the fallback.
+    bool bad = !(l_tot >= 8.271806e-25f) || !(l_tot < INFINITY);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bad = bad || !(fabsf(oacc[db][r]) < INFINITY);
+    if (!RUN && __any(qrow_raw < tt.r1 && bad)) {
         if (lane == 0) redo[tt.lb] = 1;
         return;
     }
@@ -1052,11 +1129,45 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
     }
 }
 
+// The flagged tiles' logical ids in ascending order (flist) and their number
+// (*nlist, and *nflag when given).  One work-group of 1024 threads walks the flags
+// in chunks of 1024: a ballot per wave, the waves' counts in order.
+__global__ __launch_bounds__(1024) void list_flags_kernel(const int *redo, int ntotal, int *flist, int *nlist,
+                                                          int32_t *nflag)
+{
+    __shared__ int wcount[16];
+    __shared__ int base;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) base = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < ntotal; c0 += 1024) {
+        const int t = c0 + threadIdx.x;
+        const bool f = t < ntotal && redo[t] != 0;
+        const uint64_t m = __ballot(f);
+        if (lane == 0) wcount[wave] = __popcll(m);
+        __syncthreads();
+        int before = base;
+        for (int w = 0; w < wave; ++w) before += wcount[w];
+        if (f) flist[before + __popcll(m & ((1ull << lane) - 1ull))] = t;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int add = 0;
+            for (int w = 0; w < 16; ++w) add += wcount[w];
+            base += add;
+        }
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        *nlist = base;
+        if (nflag) *nflag = base;
+    }
+}
+
 struct Layout {
     int64_t cap;       // columns per group in the column map
     int tph;           // tile slots per head
     int ntotal;        // launched blocks (multiple of 8)
-    size_t off_row, off_bias, off_len, off_x, off_bmax, off_kmax, off_redo, off_table, total;
+    size_t off_row, off_bias, off_len, off_x, off_bmax, off_kmax, off_redo, off_table, off_flist, off_nlist, total;
 };
 
 Layout layout(int B, int H, int N, int Cq, int m, int tq)
@@ -1076,6 +1187,8 @@ Layout layout(int B, int H, int N, int Cq, int m, int tq)
     L.off_kmax = o; o += isg_align256((size_t)B * H * sizeof(int));
     L.off_redo = o; o += isg_align256((size_t)L.ntotal * sizeof(int));
     L.off_table = o; o += isg_align256((size_t)L.ntotal * sizeof(int4));
+    L.off_flist = o; o += isg_align256((size_t)L.ntotal * sizeof(int));
+    L.off_nlist = o; o += isg_align256(sizeof(int));
     L.total = o;
     return L;
 }
@@ -1088,22 +1201,34 @@ template <int D, int QB>
 void launch_bf16(hipStream_t st, const Layout &Lq, const void *q_p, const void *k_p, const void *v_p, int N, int Cq,
                  const int4 *table, const int32_t *col_row, const float *col_bias, const int32_t *col_len,
                  const int32_t *col_x, const float *col_bmax, const int *kmax2, float scale_log2, void *o_p,
-                 float *lse_p, const int32_t *perm_q, int *redo, int32_t *nflag)
+                 float *lse_p, const int32_t *perm_q, int *redo, int *flist, int *nlist, int32_t *nflag)
 {
     if constexpr (D == 128 && kUsePingPong) {
+        // fast pass over every tile pair, then the flagged tiles (listed in
+        // ascending order) again with a running maximum, two per work-group like
+        // the fast pass; work-groups past the list's end exit at once
         const int npairs = (Lq.ntotal / 2 + 7) / 8 * 8;
-        attn_pp_kernel<D><<<npairs, 64 * kPPWaves, 0, st>>>(
+        attn_pp_kernel<D, false><<<npairs, 64 * kPPWaves, 0, st>>>(
             (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo);
-    } else
-    attn_bf16_kernel<D, true, QB><<<Lq.ntotal, 256 / QB, 0, st>>>(
-        (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
-        nullptr);
-    attn_bf16_kernel<D, false, 1><<<std::min((Lq.ntotal + 63) / 64, kFallbackBlocks), 256, 0, st>>>(
-        (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
-        col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
-        nflag);
+            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
+            nullptr, nullptr);
+        list_flags_kernel<<<1, 1024, 0, st>>>(redo, Lq.ntotal, flist, nlist, nflag);
+        attn_pp_kernel<D, true><<<npairs, 64 * kPPWaves, 0, st>>>(
+            (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
+            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
+            flist, nlist);
+    } else {
+        (void)flist;
+        (void)nlist;
+        attn_bf16_kernel<D, true, QB><<<Lq.ntotal, 256 / QB, 0, st>>>(
+            (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
+            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
+            nullptr);
+        attn_bf16_kernel<D, false, 1><<<std::min((Lq.ntotal + 63) / 64, kFallbackBlocks), 256, 0, st>>>(
+            (const uint16_t *)q_p, (const uint16_t *)k_p, (const uint16_t *)v_p, N, Cq, table, Lq.ntotal, col_row,
+            col_bias, col_len, col_x, col_bmax, kmax2, Lq.cap, scale_log2, (uint16_t *)o_p, lse_p, perm_q, redo,
+            nflag);
+    }
 }
 
 }  // namespace
@@ -1165,6 +1290,8 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
     // else the key-norm pass below fills the workspace copy
     const int *kmx = k_max_sqnorm ? reinterpret_cast<const int *>(k_max_sqnorm) : kmax2;
     int *redo = (int *)(ws + Lq.off_redo);
+    int *flist = (int *)(ws + Lq.off_flist);
+    int *nlist = (int *)(ws + Lq.off_nlist);
     int4 *table = (int4 *)(ws + Lq.off_table);
     columns_kernel<<<(unsigned)G, 256, 0, st>>>(k_offsets, exact_groups, n_exact, sample_idx, sample_bias,
                                                n_sample, Cq, Ck, m, scale, Lq.cap, col_row, col_bias, col_len, col_x,
@@ -1177,11 +1304,11 @@ extern "C" isg_status isg_attention(void *stream, const void *q_p, const void *k
         if (d == 128) {
             if (!k_max_sqnorm) kmax_kernel<128><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<128, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                  kmx, scale_log2, o_p, lse_p, perm_q, redo, n_fallback_tiles);
+                                  kmx, scale_log2, o_p, lse_p, perm_q, redo, flist, nlist, n_fallback_tiles);
         } else {
             if (!k_max_sqnorm) kmax_kernel<64><<<kgrid, 256, 0, st>>>((const uint16_t *)k_p, N, kmax2);
             launch_bf16<64, kQB>(st, Lq, q_p, k_p, v_p, N, Cq, table, col_row, col_bias, col_len, col_x, col_bmax,
-                                 kmx, scale_log2, o_p, lse_p, perm_q, redo, n_fallback_tiles);
+                                 kmx, scale_log2, o_p, lse_p, perm_q, redo, flist, nlist, n_fallback_tiles);
         }
     } else {
         if (d == 128)

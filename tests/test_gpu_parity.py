@@ -284,11 +284,14 @@ def test_attention_short_column_lists(orc, H, N, Cq, Ck, E, m):
     assert err <= 2e-2 and lerr <= LSE_TOL_BF16
 
 
-def test_attention_extreme_logit_range_falls_back(orc):
-    """Queries and keys anti-aligned with large norms: the Cauchy-Schwarz reference
-    of the fast kernel sits ~2000 log2 units above every logit, all its weights
-    underflow, and the tile must be recomputed by the rescaling kernel."""
-    H, N, d, Cq, Ck = 1, 2048, 128, 8, 32
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_extreme_logit_range_falls_back(orc, d):
+    """Queries and keys anti-aligned with large norms: the Cauchy-Schwarz bound sits
+    thousands of log2 units above every logit.  The one-tile kernel (d = 64) keeps
+    its fixed reference there, every weight underflows and each tile is recomputed
+    by the rescaling kernel; the paired-tile kernel (d = 128) anchors its reference
+    to the first tile's largest logit and needs no fallback.  Both outputs match."""
+    H, N, Cq, Ck = 1, 2048, 8, 32
     g = torch.Generator().manual_seed(5)
     u = torch.randn(d, generator=g)
     u = u / u.norm()
@@ -301,26 +304,32 @@ def test_attention_extreme_logit_range_falls_back(orc):
     ck = isg.isg_cluster(kg, Ck, 5, companion=vg)
     S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
     sel = isg.isg_select_sample(S, ck["offsets"], N, 300, 300, seed=1)
+    nfb = torch.zeros(1, device=DEV, dtype=torch.int32)
     o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
-                                   ck["offsets"], sel, scale)
+                                   ck["offsets"], sel, scale, n_fallback_tiles=nfb)
     torch.cuda.synchronize()
     selo = {kk: npy(vv) for kk, vv in sel.items() if kk != "m"}
     oo, lo = orc.attention(f32(cq["x_perm"]), f32(ck["x_perm"]), f32(ck["companion_perm"]), npy(cq["offsets"]),
                            npy(ck["offsets"]), selo, 300, scale)
     assert np.isfinite(f32(o_p)).all()
     err = np.abs(f32(o_p) - oo).max()
-    say(f"  extreme range: max|O-O_oracle| {err:.3e}, LSE range {lo.min():.1f}..{lo.max():.1f}")
+    n_fb = int(nfb.item())
+    say(f"  extreme range d={d}: max|O-O_oracle| {err:.3e}, LSE range {lo.min():.1f}..{lo.max():.1f}, "
+        f"{n_fb} tiles through the fallback")
+    assert (n_fb > 0) if d == 64 else (n_fb == 0)
     assert err <= 2e-2
     assert lo.max() < -1000  # the case really is extreme
     # |LSE| ~ 3500 here: fp32 logits carry ~1e-7 relative error on top of the bf16 bar
     assert np.abs(npy(lse_p) - lo).max() <= LSE_TOL_BF16 + 1e-6 * np.abs(lo).max()
 
 
-def test_attention_fallback_mixed_heads_many_tiles(orc):
-    """One extreme head (every tile flagged) among three ordinary ones, with more
-    query tiles than the fallback has work-groups: the rescaling pass walks the
-    flagged tiles with a persistent grid and leaves the others alone."""
-    H, N, d, Cq, Ck = 4, 16384, 128, 8, 32
+@pytest.mark.parametrize("d", [64, 128])
+def test_attention_fallback_mixed_heads_many_tiles(orc, d):
+    """One extreme head among three ordinary ones, with more query tiles than the
+    fallback has work-groups.  d = 64: every tile of the extreme head is flagged and
+    the rescaling pass walks them with a persistent grid, leaving the others alone;
+    d = 128: the anchored reference handles the extreme head directly."""
+    H, N, Cq, Ck = 4, 16384, 8, 32
     g = torch.Generator().manual_seed(11)
     q, k, v = _inputs(H, N, d, "bf16", seed=13)
     u = torch.randn(d, generator=g)
@@ -333,9 +342,14 @@ def test_attention_fallback_mixed_heads_many_tiles(orc):
     ck = isg.isg_cluster(kg, Ck, 5, companion=vg)
     S, _ = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=False)
     sel = isg.isg_select_sample(S, ck["offsets"], N, 300, 300, seed=2)
+    nfb = torch.zeros(1, device=DEV, dtype=torch.int32)
     o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"],
-                                   ck["offsets"], sel, scale)
+                                   ck["offsets"], sel, scale, n_fallback_tiles=nfb)
     torch.cuda.synchronize()
+    n_fb = int(nfb.item())
+    n_tiles = int(((np.diff(npy(cq["offsets"]), axis=-1) + 127) // 128)[0, 2].sum())
+    say(f"  d={d}: {n_fb} tiles through the fallback ({n_tiles} query tiles in the extreme head)")
+    assert (n_fb == n_tiles) if d == 64 else (n_fb == 0)
     selo = {kk: npy(vv) for kk, vv in sel.items() if kk != "m"}
     oo, lo = orc.attention(f32(cq["x_perm"]), f32(ck["x_perm"]), f32(ck["companion_perm"]), npy(cq["offsets"]),
                            npy(ck["offsets"]), selo, 300, scale)
@@ -675,7 +689,7 @@ def _lse_report(tag, lg, lo):
 
 
 def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode="importance", max_rows=None,
-                     all_groups_head=None, expect_fallback=False):
+                     all_groups_head=None, expect_fallback=None):
     w = WORKLOADS[name]
     N, d, Cq, Ck = w["N"], w["d"], w["Cq"], w["Ck"]
     say(f"full size {name}: inputs")
@@ -691,8 +705,8 @@ def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode
     n_fb = int(r["n_fallback_tiles"].item())
     say(f"  {n_fb} of {n_tiles} query tiles went to the rescaling fallback")
     assert 0 <= n_fb <= n_tiles
-    if expect_fallback:
-        assert n_fb > 0
+    if expect_fallback is not None:
+        assert (n_fb > 0) == expect_fallback
     # k-means of Q and of K: the last round against the oracle on sampled tokens
     say(f"full size {name}: k-means of Q and K, last round against the oracle")
     _last_round_near_ties(orc, qg, q, Cq, w["iters"], r["cq"], heads, seed=1)
@@ -783,10 +797,20 @@ def test_full_size_14b_720p_sweep(orc, share):
 
 
 def test_full_size_14b_720p_wide_norms(orc):
-    """Token norms spread log-normally (|q| |k| over a wide range): a share of the
-    query tiles falls far below the fixed reference and is recomputed by the
-    rescaling fallback; the output stays within the bar on every checked group."""
-    _full_size_check(orc, "wan14b_720p_wide_norms", 0.08, 0.08, heads=[0, 20, 39], groups_per_head=6,
+    """Token norms spread log-normally (|q| |k| over a wide range), so many rows sit
+    far below the Cauchy-Schwarz bound (29 % of the query tiles needed the
+    rescaling fallback with the bound as the reference): the reference anchored to
+    the first tile's maximum keeps every tile on the fast path, and the output stays
+    within the bar on every checked group."""
+    _full_size_check(orc, "wan14b_720p_wide_norms", 0.08, 0.08, heads=[0, 20, 39], groups_per_head=6)
+
+
+def test_full_size_14b_720p_wider_norms_rescaling_pass(orc):
+    """A log-normal norm spread of 0.6: some rows' logits run so far past the first
+    tile's that their sums would overflow around the anchored reference; those
+    tiles are flagged and recomputed by the running-maximum pass, and every checked
+    group stays within the bar."""
+    _full_size_check(orc, "wan14b_720p_wider_norms", 0.08, 0.08, heads=[0, 20, 39], groups_per_head=6,
                      expect_fallback=True)
 
 
