@@ -54,6 +54,9 @@ def parse():
                     help="also time the step and the attention at N = 75600 x 1, 2, 4, 8 (more latent frames)")
     ap.add_argument("--attention-only", type=int, default=0, metavar="K",
                     help="profiling aid: after one full step, run only K attention calls and exit")
+    ap.add_argument("--unpermute-calls", type=int, default=0, metavar="K",
+                    help="profiling aid: after the timed steps, run K isg_unpermute calls on the step's permuted-order "
+                         "attention output (the step itself fuses the un-permute into the attention)")
     ap.add_argument("--copy-calibration", type=float, default=0.0, metavar="GIB",
                     help="profiling aid: copy a GIB-sized buffer 3 times (a plain copy of known size) and exit")
     return ap.parse_args()
@@ -502,6 +505,12 @@ def main():
                                                            "frac_peak": round(f2 / ms / 1e9 / peak, 4),
                                                            "fallback_tiles": int(nfb.item())}
         result["attention_sweep"] = sweep
+    if args.unpermute_calls:
+        o_p, lse_p = isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"],
+                                       sel, scale, k_max_sqnorm=ck["max_sqnorm"], workspace=ws_a)
+        for _ in range(args.unpermute_calls):
+            isg.isg_unpermute(o_p, lse_p, cq["perm"])
+        torch.cuda.synchronize()
     if args.density_study:
         print("# density study", file=sys.stderr, flush=True)
         result["density_study"] = density_study(args, w, isg, make_workload, WORKLOADS, budget_keys, dev)

@@ -236,7 +236,8 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, i
 // ballots over the label bits.
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, const int32_t *base,
                                                      const int32_t *tot, int N, int C, int nchunks, int bits,
-                                                     int prow, int32_t *perm, int32_t *offsets, int32_t *poff)
+                                                     int prow, int maxp, int32_t *perm, int32_t *offsets,
+                                                     int32_t *poff, int4 *ptab)
 {
     extern __shared__ int run[];  // C entries (dynamic, so small C lets more waves share a CU)
     const int chunk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
@@ -293,12 +294,15 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
         const bool first = chunk == 0;
         int32_t *ob = offsets + (int64_t)bh * (C + 1);
         int32_t *pb = poff + (int64_t)bh * (C + 1);
+        int4 *pt = ptab + (int64_t)bh * maxp;
         for (int c = l0; c < l1; ++c) {
             const int n = run[c];
             run[c] = os;
             if (first) {
                 ob[c] = os;
                 pb[c] = op;
+                // piece table: group and row range of each of the group's pieces
+                for (int k = 0; k < n; k += prow) pt[op + k / prow] = make_int4(c, os + k, os + min(n, k + prow), 0);
             }
             os += n;
             op += (n + prow - 1) / prow;
@@ -354,8 +358,8 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
 // to fp32 (an empty group keeps its centroid).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides xs, int H, int N, int C,
-                                                           const int32_t *perm, const int32_t *offsets,
-                                                           const int32_t *poff, int maxp, double *partial,
+                                                           const int32_t *perm, const int32_t *poff,
+                                                           const int4 *ptab, int maxp, double *partial,
                                                            T *x_perm, float *pmax)
 {
     constexpr int TPR = D / 8;     // threads per row
@@ -363,17 +367,13 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
     constexpr int PR = piece_rows(D);
     constexpr int RPT = PR / RP;   // rows per slot: all indices, then all rows, in flight at once
     __shared__ double red[RP][D];
-    __shared__ int grp;
     const int q = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
-    const int32_t *pb = poff + (int64_t)bh * (C + 1);
-    if (q >= pb[C]) return;
-    // group of piece q: the one j with poff[j] <= q < poff[j + 1] (one parallel pass)
-    for (int jj = threadIdx.x; jj < C; jj += 256)
-        if (pb[jj] <= q && q < pb[jj + 1]) grp = jj;
-    __syncthreads();
-    const int j = grp;
-    const int32_t *ob = offsets + (int64_t)bh * (C + 1);
-    const int r0 = ob[j] + (q - pb[j]) * PR, r1 = min(ob[j + 1], r0 + PR);
+    // the piece's row range comes from the table the scatter wrote (entries past
+    // the head's piece count are stale and not read)
+    const int npieces = poff[(int64_t)bh * (C + 1) + C];
+    const int4 pt = ptab[(int64_t)bh * maxp + q];
+    if (q >= npieces) return;
+    const int r0 = pt.y, r1 = pt.z;
     const int rs = threadIdx.x / TPR, ck = threadIdx.x % TPR;
     const T *xb = x + b * xs.b + h * xs.h + ck * 8;
     const int32_t *pm = perm + (int64_t)bh * N;
@@ -924,7 +924,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 }
 
 struct ClusterWs {
-    size_t off_hist, off_tot, off_planes, off_norms, off_aug, off_poff, off_partial, off_pmax, total;
+    size_t off_hist, off_tot, off_planes, off_norms, off_aug, off_poff, off_ptab, off_partial, off_pmax, total;
     int Cpad, maxp;
 };
 
@@ -942,6 +942,7 @@ ClusterWs cluster_ws(int B, int H, int N, int d, int C)
     w.off_norms = o; o += isg_align256(BH * w.Cpad * sizeof(float));
     w.off_aug = o; o += isg_align256(BH * w.Cpad * 16 * sizeof(uint16_t));
     w.off_poff = o; o += isg_align256(BH * (C + 1) * sizeof(int32_t));
+    w.off_ptab = o; o += isg_align256(BH * (size_t)w.maxp * sizeof(int4));
     w.off_partial = o; o += isg_align256(BH * (size_t)w.maxp * d * sizeof(double));
     w.off_pmax = o; o += isg_align256(BH * (size_t)w.maxp * sizeof(float));
     w.total = o;
@@ -976,6 +977,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     int32_t *hist = (int32_t *)(ws + w.off_hist);
     int32_t *tot = (int32_t *)(ws + w.off_tot);
     int32_t *poff = (int32_t *)(ws + w.off_poff);
+    int4 *ptab = (int4 *)(ws + w.off_ptab);
     double *partial = (double *)(ws + w.off_partial);
     float *pmax = (float *)(ws + w.off_pmax);
     int bits = 1;
@@ -991,9 +993,10 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
         scan_kernel<<<dim3((C + 63) / 64, BH), 256, 0, st>>>(hist, nchunks, C, tot);
         scatter_kernel<<<dim3(nchunks, BH), 64, C * sizeof(int32_t), st>>>(labels, hist, tot, N, C, nchunks, bits,
-                                                                           piece_rows(D), perm, offsets, poff);
+                                                                           piece_rows(D), w.maxp, perm, offsets,
+                                                                           poff, ptab);
         // the last iteration's update also writes the permuted copy of x
-        update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, offsets, poff, w.maxp,
+        update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, poff, ptab, w.maxp,
                                                                     partial, it + 1 == iters ? x_perm : nullptr,
                                                                     last_norms ? pmax : nullptr);
         update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent,
