@@ -941,12 +941,14 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
     const int tid = threadIdx.x, lane = tid & 63, hl = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = wave >> 2, wq = wave & 3;
+    // one tile pair per work-group: pairs of the table (fast pass) or of the list
+    // of flagged tiles (rescaling pass; work-groups past its end exit at once)
     const int lp = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int nlist = RUN ? *nflag : nblocks;
+    if (2 * lp >= nlist) return;
     // both halves' tiles (every wave reads both, so the phase count is uniform)
     int Th[2];
     int4 teh[2];
-    const int nlist = RUN ? *nflag : nblocks;
-    if (2 * lp >= nlist) return;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int pos = 2 * lp + h;
@@ -1018,40 +1020,39 @@ __global__ __launch_bounds__(64 * kPPWaves) __attribute__((amdgpu_waves_per_eu(2
         pp_chunks<D, RUN, 1>(nchunks, tt, kb0, kb1, vb0, vb1, ring_row[1], ring_bias[1], zrow, kh, vh, qf, oacc, lacc, m_ref,
                         vtr, scale_log2, wave_active, wq, lane, hl, l32);
 
-    if (!wave_active) return;
-    // rows 0 and 1 of the row-sum product live in lanes 0-15: the sums of queries
-    // 0-15 and 16-31
-    const float ls0 = __shfl(lacc[0], l32 & 15), ls1 = __shfl(lacc[1], l32 & 15);
-    const float l_tot = l32 < 16 ? ls0 : ls1;
-    const int qrow_raw = tt.r0 + wq * 32 + l32;
-    // 2^-80: weights may have underflowed; not finite: something overflowed.  Either
-    // hands the tile to the fallback.
-    bool bad = !(l_tot >= 8.271806e-25f) || !(l_tot < INFINITY);
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) bad = bad || !(fabsf(oacc[db][r]) < INFINITY);
-    if (!RUN && __any(qrow_raw < tt.r1 && bad)) {
-        if (lane == 0) redo[tt.lb] = 1;
-        return;
-    }
-    if (qrow_raw < tt.r1) {
-        const float inv = 1.0f / l_tot;
-        // token order when a permutation is given (the un-permute step fused)
-        const int orow_i = perm_q ? perm_q[(int64_t)bh * N + qrow_raw] : qrow_raw;
-        uint16_t *orow = o_p + ((int64_t)bh * N + orow_i) * D;
+    if (wave_active) {
+        // rows 0 and 1 of the row-sum product live in lanes 0-15: the sums of queries
+        // 0-15 and 16-31
+        const float ls0 = __shfl(lacc[0], l32 & 15), ls1 = __shfl(lacc[1], l32 & 15);
+        const float l_tot = l32 < 16 ? ls0 : ls1;
+        const int qrow_raw = tt.r0 + wq * 32 + l32;
+        // 2^-80: weights may have underflowed; not finite: something overflowed.
+        // Either hands the tile to the rescaling pass.
+        bool bad = !(l_tot >= 8.271806e-25f) || !(l_tot < INFINITY);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = db * 32 + g * 8 + hl * 4;
-                const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g] * inv) |
-                                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 1] * inv) << 16);
-                const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 2] * inv) |
-                                    ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 3] * inv) << 16);
-                *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
-            }
-        if (lse_p && hl == 0) lse_p[(int64_t)bh * N + orow_i] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+            for (int r = 0; r < 16; ++r) bad = bad || !(fabsf(oacc[db][r]) < INFINITY);
+        if (!RUN && __any(qrow_raw < tt.r1 && bad)) {
+            if (lane == 0) redo[tt.lb] = 1;
+        } else if (qrow_raw < tt.r1) {
+            const float inv = 1.0f / l_tot;
+            // token order when a permutation is given (the un-permute step fused)
+            const int orow_i = perm_q ? perm_q[(int64_t)bh * N + qrow_raw] : qrow_raw;
+            uint16_t *orow = o_p + ((int64_t)bh * N + orow_i) * D;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = db * 32 + g * 8 + hl * 4;
+                    const uint32_t lo = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g] * inv) |
+                                        ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 1] * inv) << 16);
+                    const uint32_t hi = (uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 2] * inv) |
+                                        ((uint32_t)f32_to_bf16_bits(oacc[db][4 * g + 3] * inv) << 16);
+                    *reinterpret_cast<u32x2 *>(orow + d0) = u32x2{lo, hi};
+                }
+            if (lse_p && hl == 0) lse_p[(int64_t)bh * N + orow_i] = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+        }
     }
 }
 
@@ -1130,32 +1131,42 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(const float *__restrict__
 }
 
 // The flagged tiles' logical ids in ascending order (flist) and their number
-// (*nlist, and *nflag when given).  One work-group of 1024 threads walks the flags
-// in chunks of 1024: a ballot per wave, the waves' counts in order.
+// (*nlist, and *nflag when given).  One work-group of 1024 threads: each thread
+// counts the flags of 32 consecutive tiles, a block scan of the counts gives
+// every thread its first list position, and the ids follow in order (chunks of
+// 32768 tiles).
+constexpr int kListPer = 32;
+
 __global__ __launch_bounds__(1024) void list_flags_kernel(const int *redo, int ntotal, int *flist, int *nlist,
                                                           int32_t *nflag)
 {
-    __shared__ int wcount[16];
-    __shared__ int base;
+    __shared__ int wtot[16];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (threadIdx.x == 0) base = 0;
-    __syncthreads();
-    for (int c0 = 0; c0 < ntotal; c0 += 1024) {
-        const int t = c0 + threadIdx.x;
-        const bool f = t < ntotal && redo[t] != 0;
-        const uint64_t m = __ballot(f);
-        if (lane == 0) wcount[wave] = __popcll(m);
+    int base = 0;
+    for (int c0 = 0; c0 < ntotal; c0 += 1024 * kListPer) {
+        const int t0 = c0 + threadIdx.x * kListPer;
+        uint32_t bits = 0;
+#pragma unroll
+        for (int u = 0; u < kListPer; ++u)
+            if (t0 + u < ntotal && redo[t0 + u] != 0) bits |= 1u << u;
+        const int cnt = __popc(bits);
+        const int incl = wave_inclusive_scan(cnt);
+        if (lane == 63) wtot[wave] = incl;
         __syncthreads();
-        int before = base;
-        for (int w = 0; w < wave; ++w) before += wcount[w];
-        if (f) flist[before + __popcll(m & ((1ull << lane) - 1ull))] = t;
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            int add = 0;
-            for (int w = 0; w < 16; ++w) add += wcount[w];
-            base += add;
+        int before = base, add = 0;
+        for (int w = 0; w < 16; ++w) {
+            const int v = wtot[w];
+            if (w < wave) before += v;
+            add += v;
         }
-        __syncthreads();
+        int pos = before + incl - cnt;
+        while (bits) {
+            const int u = __ffs(bits) - 1;
+            bits &= bits - 1;
+            flist[pos++] = t0 + u;
+        }
+        base += add;
+        __syncthreads();  // wtot is rewritten by the next chunk
     }
     if (threadIdx.x == 0) {
         *nlist = base;

@@ -363,6 +363,52 @@ def test_attention_fallback_mixed_heads_many_tiles(orc, d):
     assert lerr[0, 2].max() <= LSE_TOL_BF16 + 1e-6 * np.abs(lo[0, 2]).max()
 
 
+@pytest.mark.parametrize("H", [1, 3])
+def test_attention_rescaling_pass_after_anchor(orc, H):
+    """Hand-built lists (d = 128): key group 0 is anti-aligned with every query and
+    comes first in the column list, key group 1 is aligned with large norms, so
+    the logits of the second tile exceed the first tile's by thousands of log2
+    units.  The anchored reference overflows there, every tile is flagged, and the
+    listed tiles are recomputed by the paired-tile kernel with a running maximum
+    (an odd number of tiles per head leaves one pair half-empty)."""
+    N, d, nq = 640, 128, 384
+    g = torch.Generator().manual_seed(23)
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    q = (40.0 * u + 0.3 * torch.randn(1, H, N, d, generator=g)).to(torch.bfloat16)
+    k = 0.3 * torch.randn(1, H, N, d, generator=g)
+    k[:, :, :64] += -40.0 * u
+    k[:, :, 64:128] += 60.0 * u
+    k = k.to(torch.bfloat16)
+    v = torch.randn(1, H, N, d, generator=g).to(torch.bfloat16)
+    # query groups: [0, nq) and [nq, N); key groups: [0, 64), [64, 128), [128, N)
+    qo = torch.tensor([0, nq, N], dtype=torch.int32).repeat(1, H, 1)
+    ko = torch.tensor([0, 64, 128, N], dtype=torch.int32).repeat(1, H, 1)
+    eg = torch.full((1, H, 2, 3), -1, dtype=torch.int32)
+    eg[..., 0], eg[..., 1] = 0, 1
+    sel = dict(exact_groups=eg, n_exact=torch.full((1, H, 2), 2, dtype=torch.int32),
+               sample_idx=torch.zeros((1, H, 2, 1), dtype=torch.int32),
+               sample_bias=torch.zeros((1, H, 2, 1), dtype=torch.float32),
+               n_sample=torch.zeros((1, H, 2), dtype=torch.int32), m=0)
+    scale = isg.default_scale(d)
+    dev = {kk: (vv.to(DEV) if torch.is_tensor(vv) else vv) for kk, vv in sel.items()}
+    nfb = torch.zeros(1, device=DEV, dtype=torch.int32)
+    o_p, lse_p = isg.isg_attention(q.to(DEV), k.to(DEV), v.to(DEV), qo.to(DEV), ko.to(DEV), dev, scale,
+                                   n_fallback_tiles=nfb)
+    torch.cuda.synchronize()
+    n_tiles = H * ((nq + 127) // 128 + (N - nq + 127) // 128)
+    oo, lo = orc.attention(f32(q), f32(k), f32(v), npy(qo), npy(ko), {kk: npy(vv) if torch.is_tensor(vv) else vv
+                                                                      for kk, vv in sel.items() if kk != "m"},
+                           0, scale)
+    err = np.abs(f32(o_p) - oo).max()
+    lerr = np.abs(npy(lse_p) - lo).max()
+    say(f"  H={H}: {int(nfb.item())} of {n_tiles} tiles through the rescaling pass; max|O-O_oracle| {err:.3e}, "
+        f"max|LSE-LSE_oracle| {lerr:.3e}, LSE {lo.min():.0f}..{lo.max():.0f}")
+    assert int(nfb.item()) == n_tiles
+    assert np.isfinite(f32(o_p)).all()
+    assert err <= 2e-2 and lerr <= LSE_TOL_BF16 + 1e-6 * np.abs(lo).max()
+
+
 def test_attention_high_entropy_zipf(orc):
     """Near-uniform attention (Q scaled by 0.2) with Zipf cluster sizes."""
     *_, o_p, lse_p, oo, lo = _attn_case(orc, 2, 4096, 128, "bf16", 16, 64, 300, 300, q_scale=0.2, zipf=1.2)
