@@ -359,15 +359,20 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
 template <typename T, int D>
 __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides xs, int H, int N, int C,
                                                            const int32_t *perm, const int32_t *poff,
-                                                           const int4 *ptab, int maxp, double *partial,
-                                                           T *x_perm, float *pmax)
+                                                           const int4 *ptab, int maxp, int64_t nblocks,
+                                                           double *partial, T *x_perm, float *pmax)
 {
     constexpr int TPR = D / 8;     // threads per row
     constexpr int RP = 256 / TPR;  // row slots
     constexpr int PR = piece_rows(D);
     constexpr int RPT = PR / RP;   // rows per slot: all indices, then all rows, in flight at once
     __shared__ double red[RP][D];
-    const int q = blockIdx.x, bh = blockIdx.y, b = bh / H, h = bh % H;
+    // XCD-aware order: each XCD (launch id mod 8) walks a contiguous range of
+    // (head, piece) pairs, so the heads it works on at a time are few and their
+    // rows, read at random positions, stay in that XCD's L2
+    const int64_t lb = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (lb >= nblocks) return;
+    const int q = (int)(lb % maxp), bh = (int)(lb / maxp), b = bh / H, h = bh % H;
     // the piece's row range comes from the table the scatter wrote (entries past
     // the head's piece count are stale and not read)
     const int npieces = poff[(int64_t)bh * (C + 1) + C];
@@ -675,7 +680,7 @@ __device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, 
 // (token, centroid) key goes into the token's top four.  The key's index bits
 // hold the centroid's row in the tile without the half-wave's offset of 4 rows;
 // the caller adds it once per token.
-template <int D>
+template <int D, bool BYTEKEY>
 __device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, int C, const bf16x8 (*xf)[D / 16],
                                             const bf16x8 *xaug, uint32_t hi_mask, TopK<topk_of<D>()> *top, int hl,
                                             int l32)
@@ -696,17 +701,23 @@ __device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, int C,
             acc[tb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xf[tb][s], acc[tb], 0, 0, 0);
         }
     }
+    const uint32_t jb = (uint32_t)(tile * kCT);  // wave-uniform
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const uint32_t j = (uint32_t)(tile * kCT + (r >> 2) * 8 + (r & 3));  // wave-uniform
+        const uint32_t j = jb + (r >> 2) * 8 + (r & 3);
         // rows j and j + 4 both padding (norm 1e30, never kept): skip (a scalar branch)
         if (j >= (uint32_t)C) continue;
+        // indices below 256: the key is the distance's upper three bytes and the
+        // index byte (one byte permute); else the distance with its low bits
+        // replaced by the index
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb) top_insert(top[tb], (__float_as_uint(acc[tb][r]) & hi_mask) | j);
+        for (int tb = 0; tb < 2; ++tb)
+            top_insert(top[tb], BYTEKEY ? __builtin_amdgcn_perm(__float_as_uint(acc[tb][r]), j, 0x07060500u)
+                                        : ((__float_as_uint(acc[tb][r]) & hi_mask) | j));
     }
 }
 
-template <int D>
+template <int D, bool BYTEKEY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void assign_mfma_kernel(
     const uint16_t *__restrict__ x, Strides xs, int H, int N, int C, int Cpad, const uint16_t *__restrict__ planes,
     const float *__restrict__ norms, const uint16_t *__restrict__ aug, const float *__restrict__ cent,
@@ -762,7 +773,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     }
     int ibits = 1;
     while ((1 << ibits) < Cpad) ++ibits;
-    const uint32_t imask = (1u << ibits) - 1u, hi_mask = ~imask;
+    if (BYTEKEY) ibits = 8;  // Cpad <= 256: the index is the key's low byte
+    const uint32_t imask = (1u << ibits) - 1u;
+    // the key's mask lives in a vector register: with the index a scalar, the key
+    // is then one v_and_or_b32 (a VOP3 reads at most one scalar operand)
+    uint32_t hi_mask;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(hi_mask) : "s"(~imask));
     constexpr int TK = topk_of<D>();
     TopK<TK> top[2];
 #pragma unroll
@@ -797,12 +813,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
     for (int tile = 0; tile < ntiles; tile += 2) {
         // tile in tb0 while tile+1 loads into tb1, then the reverse
         if (tile + 1 < ntiles) planes_direct<D>(tb1, pb, ab, Cpad, tile + 1, wave, lane);
-        assign_tile<D>(tb0, tile, C, xf, xaug, hi_mask, top, hl, l32);
+        assign_tile<D, BYTEKEY>(tb0, tile, C, xf, xaug, hi_mask, top, hl, l32);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tile + 1 >= ntiles) break;
         if (tile + 2 < ntiles) planes_direct<D>(tb0, pb, ab, Cpad, tile + 2, wave, lane);
-        assign_tile<D>(tb1, tile + 1, C, xf, xaug, hi_mask, top, hl, l32);
+        assign_tile<D, BYTEKEY>(tb1, tile + 1, C, xf, xaug, hi_mask, top, hl, l32);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
     }
@@ -959,10 +975,38 @@ void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, 
         float *norms = (float *)(ws + w.off_norms);
         uint16_t *aug = (uint16_t *)(ws + w.off_aug);
         centroid_planes_kernel<D><<<dim3(w.Cpad / 4, BH), 256, 0, st>>>(cent, C, w.Cpad, planes, norms, aug);
-        assign_mfma_kernel<D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, w.Cpad, planes, norms,
-                                                                         aug, cent, labels);
+        const dim3 grid((N + 255) / 256, BH);
+        if (w.Cpad <= 256)
+            assign_mfma_kernel<D, true><<<grid, 256, 0, st>>>(x, xs, H, N, C, w.Cpad, planes, norms, aug, cent,
+                                                              labels);
+        else
+            assign_mfma_kernel<D, false><<<grid, 256, 0, st>>>(x, xs, H, N, C, w.Cpad, planes, norms, aug, cent,
+                                                               labels);
     } else {
         assign_kernel<T, D><<<dim3((N + 255) / 256, BH), 256, 0, st>>>(x, xs, H, N, C, cent, labels);
+    }
+}
+
+// Subspace-major copy for product quantisation: x[b][h][t][s*ds + e] ->
+// out[s][b][h][t][e].  A work-group moves 64 tokens: it reads their rows whole
+// (coalesced) and writes P runs of 64*ds contiguous elements, so each subspace's
+// k-means then reads dense ds-element rows instead of ds-element pieces of longer
+// rows (a 32-byte piece costs a 128-byte line fetch).
+template <typename T>
+__global__ __launch_bounds__(256) void pq_split_kernel(const T *x, Strides xs, int B, int H, int N, int d, int ds,
+                                                       T *out)
+{
+    const int cpr = d / 8;  // 8-element chunks per row
+    const int bh = blockIdx.y, b = bh / H, h = bh % H;
+    const int t0 = blockIdx.x * 64;
+    const int nt = min(64, N - t0);
+    const int64_t plane = (int64_t)B * H * N * ds;
+    for (int q = threadIdx.x; q < nt * cpr; q += 256) {
+        const int tt = q / cpr, c = q % cpr;
+        const int s = (c * 8) / ds, e0 = (c * 8) % ds;
+        const T *src = x + b * xs.b + h * xs.h + (int64_t)(t0 + tt) * xs.t + c * 8;
+        T *dst = out + s * plane + ((int64_t)bh * N + t0 + tt) * ds + e0;
+        copy8(dst, src);
     }
 }
 
@@ -982,6 +1026,8 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     float *pmax = (float *)(ws + w.off_pmax);
     int bits = 1;
     while ((1 << bits) < C) ++bits;
+    const int64_t upd_n = (int64_t)w.maxp * BH;         // (piece, head) work-groups
+    const unsigned upd_blocks = (unsigned)((upd_n + 7) & ~(int64_t)7);
     if (init_mode == 0) {
         const int64_t total = (int64_t)BH * C * D;
         const int grid = (int)std::min<int64_t>((total + 255) / 256, 65536);
@@ -996,9 +1042,9 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
                                                                            piece_rows(D), w.maxp, perm, offsets,
                                                                            poff, ptab);
         // the last iteration's update also writes the permuted copy of x
-        update_piece_kernel<T, D><<<dim3(w.maxp, BH), 256, 0, st>>>(x, xs, H, N, C, perm, poff, ptab, w.maxp,
-                                                                    partial, it + 1 == iters ? x_perm : nullptr,
-                                                                    last_norms ? pmax : nullptr);
+        update_piece_kernel<T, D><<<upd_blocks, 256, 0, st>>>(x, xs, H, N, C, perm, poff, ptab, w.maxp, upd_n,
+                                                              partial, it + 1 == iters ? x_perm : nullptr,
+                                                              last_norms ? pmax : nullptr);
         update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent,
                                                             last_norms ? pmax : nullptr, max_sqnorm);
     }
@@ -1173,4 +1219,77 @@ extern "C" isg_status isg_cluster_noalloc(void *stream, const void *x, isg_dtype
     if (s != ISG_OK) return s;
     return run_checked(st, x, dt, x_strides, B, H, N, d, C, iters, init_mode, companion, centroids, labels, perm,
                        offsets, x_perm, companion_perm, max_sqnorm, ws);
+}
+
+// ---------------------------------------------------------------- product-quantisation codebooks
+namespace {
+
+struct PqWs {
+    size_t off_copy, off_perm, off_offsets, off_cluster, total;
+};
+
+PqWs pq_ws(isg_dtype dt, int B, int H, int N, int d, int P, int Cc)
+{
+    const int ds = d / P;
+    const size_t esz = dt == ISG_F32 ? sizeof(float) : sizeof(uint16_t);
+    const size_t rows = (size_t)P * B * H * N;
+    PqWs w;
+    size_t o = 0;
+    w.off_copy = o; o += isg_align256(rows * ds * esz);
+    w.off_perm = o; o += isg_align256(rows * sizeof(int32_t));
+    w.off_offsets = o; o += isg_align256((size_t)P * B * H * (Cc + 1) * sizeof(int32_t));
+    w.off_cluster = o; o += cluster_ws(P * B, H, N, ds, Cc).total;
+    w.total = o;
+    return w;
+}
+
+}  // namespace
+
+extern "C" size_t isg_pq_codebooks_workspace_size(isg_dtype dt, int B, int H, int N, int d, int P, int Cc)
+{
+    if (B < 1 || H < 1 || N < 1 || d < 1 || P < 1 || Cc < 1 || d % P != 0 || (dt != ISG_F32 && dt != ISG_BF16))
+        return 0;
+    return pq_ws(dt, B, H, N, d, P, Cc).total;
+}
+
+extern "C" isg_status isg_pq_codebooks(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3], int B,
+                                       int H, int N, int d, int P, int Cc, int iters, int32_t *codes,
+                                       float *codebooks, void *workspace, size_t ws_bytes)
+{
+    ISG_REQUIRE(x && x_strides && codes && codebooks, ISG_E_ARG, "isg_pq_codebooks: null pointer argument");
+    ISG_REQUIRE(B >= 1 && H >= 1 && N >= 1, ISG_E_ARG, "isg_pq_codebooks: B, H, N must be >= 1 (got %d, %d, %d)", B,
+                H, N);
+    ISG_REQUIRE(dt == ISG_F32 || dt == ISG_BF16, ISG_E_DTYPE, "isg_pq_codebooks: dtype %d", (int)dt);
+    ISG_REQUIRE(P >= 1 && d >= 1 && d % P == 0, ISG_E_ARG, "isg_pq_codebooks: need P >= 1 and P | d (got d=%d P=%d)",
+                d, P);
+    const int ds = d / P;
+    ISG_REQUIRE(ds == 16 || ds == 64 || ds == 128, ISG_E_UNSUPPORTED,
+                "isg_pq_codebooks: subspace dimension d/P = %d not built (16, 64, 128)", ds);
+    ISG_REQUIRE((int64_t)P * B * H <= 65535, ISG_E_ARG, "isg_pq_codebooks: P*B*H must be <= 65535 (got %lld)",
+                (long long)P * B * H);
+    ISG_REQUIRE(Cc >= 1 && Cc <= N && Cc <= kMaxC, ISG_E_ARG,
+                "isg_pq_codebooks: need 1 <= Cc <= min(N, %d), got Cc=%d N=%d", kMaxC, Cc, N);
+    ISG_REQUIRE(iters >= 1, ISG_E_ARG, "isg_pq_codebooks: iters must be >= 1 (got %d)", iters);
+    for (int k = 0; k < 3; ++k)
+        ISG_REQUIRE(x_strides[k] >= 0 && x_strides[k] % 8 == 0, ISG_E_ARG,
+                    "isg_pq_codebooks: x_strides must be non-negative multiples of 8 elements");
+    ISG_REQUIRE(x_strides[2] >= d, ISG_E_ARG, "isg_pq_codebooks: token stride %lld < d", (long long)x_strides[2]);
+    ISG_REQUIRE(((uintptr_t)x & 15) == 0, ISG_E_ARG, "isg_pq_codebooks: x must be 16-byte aligned");
+    const PqWs w = pq_ws(dt, B, H, N, d, P, Cc);
+    ISG_REQUIRE(workspace && ws_bytes >= w.total, ISG_E_WORKSPACE, "isg_pq_codebooks: workspace %zu < %zu bytes",
+                workspace ? ws_bytes : (size_t)0, w.total);
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t *ws = (uint8_t *)workspace;
+    const Strides xs{x_strides[0], x_strides[1], x_strides[2]};
+    const dim3 grid((N + 63) / 64, B * H);
+    if (dt == ISG_F32)
+        pq_split_kernel<float><<<grid, 256, 0, st>>>((const float *)x, xs, B, H, N, d, ds, (float *)(ws + w.off_copy));
+    else
+        pq_split_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t *)x, xs, B, H, N, d, ds,
+                                                        (uint16_t *)(ws + w.off_copy));
+    // subspace s of batch b is batch s*B + b of one clustering call on the dense copy
+    const int64_t cs[3] = {(int64_t)H * N * ds, (int64_t)N * ds, ds};
+    return run_checked(st, ws + w.off_copy, dt, cs, P * B, H, N, ds, Cc, iters, 0, nullptr, codebooks, codes,
+                       (int32_t *)(ws + w.off_perm), (int32_t *)(ws + w.off_offsets), nullptr, nullptr, nullptr,
+                       ws + w.off_cluster);
 }

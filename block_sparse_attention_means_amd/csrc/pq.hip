@@ -18,6 +18,7 @@
 // u* are then taken in ascending j while the running count stays <= E (the first
 // group of the ranking always).  u* is found by bisection over the 32-bit key
 // space with one wave-wide sum per step.
+#include <algorithm>
 #include <cmath>
 
 #include "isg_internal.h"
@@ -125,34 +126,80 @@ __device__ __forceinline__ int wave_sum(int v)
            __builtin_amdgcn_readlane(v, 47) + __builtin_amdgcn_readlane(v, 63);
 }
 
-// One wave per query; lane owns key groups j = k*64 + lane, k < KPL.  The 8
-// waves of a block share a query group, and logical blocks are laid out so that
-// one XCD works on consecutive query groups of the same head: an XCD then holds
-// about one head's groups at a time, so the head's tables (P*Cc*Ck fp32, 4 MB at
-// 8 x 256 x 500) stay in its L2.
+// Work split: a work-group takes kVoteChunk consecutive queries of one head in
+// the permuted (query-group) order, kVoteChunk / kVoteWaves per wave, so every
+// work-group does the same work however unequal the query groups are.  A wave
+// keeps its votes per lane (lane owns key groups j = k*64 + lane, k < KPL) for
+// the query group it is in and adds them to votes[i][j] with integer atomics
+// when its queries move to the next group and at its end (integer sums: the
+// result does not depend on the order).  Logical blocks are laid out so that one
+// XCD works on consecutive chunks of the same head: an XCD then holds about one
+// head at a time, so the head's tables (P*Cc*Ck fp32, 4 MB at 8 x 256 x 500)
+// stay in its L2.
 constexpr int kVoteWaves = 8;
+constexpr int kVoteQPW = 16;  // queries per wave
+constexpr int kVoteChunk = kVoteWaves * kVoteQPW;
 constexpr int kPBatch = 8;  // subspaces whose table rows are in flight together
+
+__device__ __forceinline__ float key_to_float(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ uint32_t wave_min(uint32_t v)
+{
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    return min(min((uint32_t)__builtin_amdgcn_readlane(v, 15), (uint32_t)__builtin_amdgcn_readlane(v, 31)),
+               min((uint32_t)__builtin_amdgcn_readlane(v, 47), (uint32_t)__builtin_amdgcn_readlane(v, 63)));
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));
+    return max(max((uint32_t)__builtin_amdgcn_readlane(v, 15), (uint32_t)__builtin_amdgcn_readlane(v, 31)),
+               max((uint32_t)__builtin_amdgcn_readlane(v, 47), (uint32_t)__builtin_amdgcn_readlane(v, 63)));
+}
+
+constexpr int kCountBits = 20;  // sizes below 2^20, counts up to 1024: sums stay below 2^31
+constexpr int kCountMask = (1 << kCountBits) - 1;
+constexpr int kFloatSteps = 6;
+
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *p, int64_t n)
+{
+    for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) p[e] = 0;
+}
+
+template <int KPL>
+__device__ __forceinline__ void flush_votes(int32_t *row, int Ck, int lane, int (&vk)[KPL])
+{
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+        if (vk[k] != 0 && k * 64 + lane < Ck) atomicAdd(row + k * 64 + lane, vk[k]);
+        vk[k] = 0;
+    }
+}
 
 template <int KPL>
 __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t *q_codes, const float *tables,
                                                        const int32_t *perm_q, const int32_t *q_offsets,
                                                        const int32_t *k_offsets, int B, int H, int N, int P,
-                                                       int Cc, int Cq, int Ck, int exact_keys, int nblocks,
-                                                       int32_t *votes)
+                                                       int Cc, int Cq, int Ck, int exact_keys, int chunks,
+                                                       int nblocks, int32_t *votes)
 {
-    __shared__ int cnt[KPL * 64];
     __shared__ int nsz[KPL * 64];
-    const int nb8 = gridDim.x;
-    const int lb = xcd_logical_block(blockIdx.x, nb8);
+    const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= nblocks) return;
-    const int i = lb % Cq, bh = lb / Cq, b = bh / H, h = bh % H;
+    const int bh = lb / chunks, b = bh / H, h = bh % H;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int32_t *ko = k_offsets + (int64_t)bh * (Ck + 1);
-    for (int j = tid; j < KPL * 64; j += 64 * kVoteWaves) {
-        cnt[j] = 0;
-        nsz[j] = j < Ck ? ko[j + 1] - ko[j] : 0;
-    }
+    for (int j = tid; j < KPL * 64; j += 64 * kVoteWaves) nsz[j] = j < Ck ? ko[j + 1] - ko[j] : 0;
     __syncthreads();
     int nk[KPL], vk[KPL];
     int part = 0;
@@ -163,26 +210,64 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
         part += nk[k];
     }
     const int total = wave_sum(part);
+    // packed per-group term of the bisection sums: size in the low kCountBits
+    // bits, one count per non-empty group above them (needs total < 2^kCountBits)
+    const bool packed = total < (1 << kCountBits);
+    int nkp[KPL];
+    int gpart = 0;
+#pragma unroll
+    for (int k = 0; k < KPL; ++k) {
+        nkp[k] = nk[k] + (packed && nk[k] > 0 ? (1 << kCountBits) : 0);
+        gpart += nk[k] > 0;
+    }
+    const int groups = wave_sum(gpart);
     const int E = exact_keys;
     const int32_t *qo = q_offsets + (int64_t)bh * (Cq + 1);
     const float *tb = tables + (int64_t)bh * P * Cc * Ck;
-    const int r_end = qo[i + 1];
-    if (total <= E) {  // every non-empty group fits every query's budget
-        for (int r = qo[i] + wave; r < r_end; r += kVoteWaves)
-#pragma unroll
-            for (int k = 0; k < KPL; ++k) vk[k] += nk[k] > 0;
+    int32_t *vb = votes + (int64_t)bh * Cq * Ck;
+    // this wave's queries: rows [r, r_stop) of the permuted order
+    int r = (lb % chunks) * kVoteChunk + wave * kVoteQPW;
+    const int r_stop = min(N, r + kVoteQPW);
+    if (r >= r_stop) return;
+    // query group of row r: the largest i with qo[i] <= r (groups may be empty)
+    int i = 0;
+    {
+        int lo = 0, hi = Cq;  // qo[lo] <= r < qo[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (qo[mid] <= r) lo = mid; else hi = mid;
+        }
+        i = lo;
     }
+    int g_end = qo[i + 1];
     const int32_t *qcode = q_codes + ((int64_t)b * H + h) * N;  // + s*B*H*N + t
     const int64_t sstride = (int64_t)B * H * N;
+    if (total <= E) {  // every non-empty group fits every query's budget
+        for (; r < r_stop; ++r) {
+            while (r >= g_end) {
+                flush_votes<KPL>(vb + (int64_t)i * Ck, Ck, lane, vk);
+                ++i;
+                g_end = qo[i + 1];
+            }
+#pragma unroll
+            for (int k = 0; k < KPL; ++k) vk[k] += nk[k] > 0;
+        }
+        flush_votes<KPL>(vb + (int64_t)i * Ck, Ck, lane, vk);
+        return;
+    }
     // codes of the next query are fetched while the current one runs its bisection
     int codes[kPBatch];
-    int r = qo[i] + wave;
-    if (total > E && r < r_end) {
+    {
         const int t = perm_q[(int64_t)bh * N + r];
 #pragma unroll
         for (int s = 0; s < kPBatch; ++s) codes[s] = s < P ? qcode[s * sstride + t] : 0;
     }
-    for (; total > E && r < r_end; r += kVoteWaves) {
+    for (; r < r_stop; ++r) {
+        while (r >= g_end) {
+            flush_votes<KPL>(vb + (int64_t)i * Ck, Ck, lane, vk);
+            ++i;
+            g_end = qo[i + 1];
+        }
         // this query's table rows, all issued before any is added (rows of the
         // first kPBatch subspaces; further subspaces in batches of kPBatch)
         float sc[KPL];
@@ -210,29 +295,62 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
                         if (k * 64 + lane < Ck) sc[k] = __fadd_rn(sc[k], rv[s][k]);
                 }
         }
-        if (r + kVoteWaves < r_end) {
-            const int tn = perm_q[(int64_t)bh * N + r + kVoteWaves];
+        if (r + 1 < r_stop) {
+            const int tn = perm_q[(int64_t)bh * N + r + 1];
 #pragma unroll
             for (int s = 0; s < kPBatch; ++s) codes[s] = s < P ? qcode[s * sstride + tn] : 0;
         }
         uint32_t ok[KPL];
 #pragma unroll
         for (int k = 0; k < KPL; ++k) ok[k] = orderable(sc[k]);
-        // bisection: lo keeps C(lo) > E, hi keeps C(hi) <= E (C(2^32) = 0)
-        uint32_t lo = 0;
-        uint64_t hi = 1ull << 32;
+        // Bisection: lo keeps C(lo) > E, hi keeps C(hi) <= E.  It starts on the
+        // keys' own range [min, max + 1) of the non-empty groups (C(min) = total >
+        // E, C(max + 1) = 0).  The first kFloatSteps steps halve the score
+        // interval, later ones the key interval, so at most kFloatSteps + 32 steps
+        // are taken (any point strictly inside the interval is a correct step).
+        // With packed counts (total < 2^20) each step also counts the groups at or
+        // above mid, so it stops as soon as one group is left in [lo, hi): that
+        // group's key is the largest u with C(u) > E, exactly where the full
+        // bisection would end.
+        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+        for (int k = 0; k < KPL; ++k)
+            if (nk[k] > 0) {
+                kmin = min(kmin, ok[k]);
+                kmax = max(kmax, ok[k]);
+            }
+        uint32_t lo = wave_min(kmin);
+        uint64_t hi = (uint64_t)wave_max(kmax) + 1u;
         int above = 0;  // C(hi)
-        for (int it = 0; it < 32; ++it) {
-            const uint32_t mid = lo + (uint32_t)((hi - lo) >> 1);
+        int g_lo = groups, g_hi = 0;  // groups with key >= lo, >= hi
+        for (int it = 0; hi - lo > 1 && (!packed || g_lo - g_hi > 1); ++it) {
+            uint32_t mid = lo + (uint32_t)((hi - lo) >> 1);
+            if (it < kFloatSteps) {
+                const float a = key_to_float(lo), b = key_to_float((uint32_t)(hi - 1));
+                const uint32_t fm = __builtin_amdgcn_readfirstlane(orderable(0.5f * a + 0.5f * b));
+                if (fm > lo && (uint64_t)fm < hi) mid = fm;
+            }
             int p = 0;
 #pragma unroll
-            for (int k = 0; k < KPL; ++k) p += ok[k] >= mid ? nk[k] : 0;
-            const int c = wave_sum(p);
+            for (int k = 0; k < KPL; ++k) p += ok[k] >= mid ? nkp[k] : 0;
+            const int sum = wave_sum(p);
+            const int c = packed ? (sum & kCountMask) : sum;
+            const int g = packed ? (sum >> kCountBits) : 0;
             if (c > E) {
                 lo = mid;
+                g_lo = g;
             } else {
                 hi = mid;
                 above = c;
+                g_hi = g;
+            }
+        }
+        if (hi - lo > 1) {
+            // one non-empty group left in [lo, hi): lo moves up to its key
+#pragma unroll
+            for (int k = KPL - 1; k >= 0; --k) {
+                const uint64_t m = __ballot(nk[k] > 0 && ok[k] >= lo && (uint64_t)ok[k] < hi);
+                if (m) lo = __builtin_amdgcn_readlane(ok[k], __builtin_ctzll(m));
             }
         }
         uint64_t take[KPL], tie[KPL];
@@ -263,11 +381,7 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
 #pragma unroll
         for (int k = 0; k < KPL; ++k) vk[k] += (int)((take[k] >> lane) & 1ull);
     }
-#pragma unroll
-    for (int k = 0; k < KPL; ++k)
-        if (vk[k]) atomicAdd(&cnt[k * 64 + lane], vk[k]);
-    __syncthreads();
-    for (int j = tid; j < Ck; j += 64 * kVoteWaves) votes[((int64_t)bh * Cq + i) * Ck + j] = cnt[j];
+    flush_votes<KPL>(vb + (int64_t)i * Ck, Ck, lane, vk);
 }
 
 template <int KPL>
@@ -275,10 +389,13 @@ void launch_votes(hipStream_t st, const int32_t *q_codes, const float *tables, c
                   const int32_t *q_offsets, const int32_t *k_offsets, int B, int H, int N, int P, int Cc, int Cq,
                   int Ck, int E, int32_t *votes)
 {
-    const int nblocks = B * H * Cq;
+    const int64_t nv = (int64_t)B * H * Cq * Ck;
+    zero_i32_kernel<<<(unsigned)std::min<int64_t>((nv + 255) / 256, 4096), 256, 0, st>>>(votes, nv);
+    const int chunks = (N + kVoteChunk - 1) / kVoteChunk;
+    const int nblocks = B * H * chunks;
     const int nb8 = (nblocks + 7) & ~7;
-    pq_votes_kernel<KPL><<<nb8, 64 * kVoteWaves, 0, st>>>(q_codes, tables, perm_q, q_offsets, k_offsets, B, H, N, P, Cc, Cq,
-                                              Ck, E, nblocks, votes);
+    pq_votes_kernel<KPL><<<nb8, 64 * kVoteWaves, 0, st>>>(q_codes, tables, perm_q, q_offsets, k_offsets, B, H, N, P,
+                                                          Cc, Cq, Ck, E, chunks, nblocks, votes);
 }
 
 }  // namespace

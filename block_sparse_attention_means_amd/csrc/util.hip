@@ -25,7 +25,7 @@ isg_status isg_check_launch(const char *what)
 
 extern "C" const char *isg_last_error(void) { return g_err; }
 
-extern "C" int isg_version(void) { return 3; }
+extern "C" int isg_version(void) { return 4; }
 
 // Importance weights live on a grid of ratio 2^(-1/256): entry k is 2^31 scaled
 // down by k grid steps, rounded to the nearest integer.

@@ -19,7 +19,8 @@ ISG_F32, ISG_BF16 = 0, 1
 MODES = {"importance": 0, "uniform": 1, "votes": 2}
 EXPORTS = ["isg_last_error", "isg_version", "isg_proposal_table", "isg_cluster_workspace_size",
            "isg_cluster", "isg_probs", "isg_select_sample", "isg_attention_workspace_size",
-           "isg_attention", "isg_unpermute", "isg_pq_votes", "isg_select_sample_topp", "isg_cluster_noalloc"]
+           "isg_attention", "isg_unpermute", "isg_pq_votes", "isg_select_sample_topp", "isg_cluster_noalloc",
+           "isg_pq_codebooks_workspace_size", "isg_pq_codebooks"]
 
 _lib = None
 
@@ -64,8 +65,11 @@ def _declare(L):
                                          _p, _p, _p, _p, _p]
     L.isg_pq_votes.argtypes = [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _i, _f,
                                _p, _p, _p]
+    L.isg_pq_codebooks_workspace_size.argtypes = [_i] * 7
+    L.isg_pq_codebooks_workspace_size.restype = _sz
+    L.isg_pq_codebooks.argtypes = [_p, _p, _i, _p, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz]
     for name in ["isg_cluster", "isg_probs", "isg_select_sample", "isg_attention", "isg_unpermute",
-                 "isg_pq_votes", "isg_select_sample_topp", "isg_cluster_noalloc"]:
+                 "isg_pq_votes", "isg_select_sample_topp", "isg_cluster_noalloc", "isg_pq_codebooks"]:
         getattr(L, name).restype = _i
 
 
@@ -329,37 +333,27 @@ def isg_unpermute(o_p, lse_p, perm_q, *, out=None, lse_out=None, stream=None):
     return o, lse
 
 
-def pq_codebooks(x, P, Cc, iters, *, stream=None):
-    """Product-quantisation codes [P,B,H,N] and codebooks [P,B,H,Cc,d/P] of x [B,H,N,d]:
-    k-means of every d/P-dim subspace through strided views, writing in place.  With
-    B = 1 the subspaces are the batch dimension of one isg_cluster call (batch stride
-    d/P elements); otherwise one call per subspace."""
+def pq_codebooks_workspace_size(dtype, B, H, N, d, P, Cc) -> int:
+    dt = ISG_BF16 if dtype == torch.bfloat16 else ISG_F32
+    return int(lib().isg_pq_codebooks_workspace_size(dt, B, H, N, d, P, Cc))
+
+
+def pq_codebooks(x, P, Cc, iters, *, workspace=None, stream=None):
+    """Product-quantisation codes [P,B,H,N] and codebooks [P,B,H,Cc,d/P] of x [B,H,N,d]
+    (isg_pq_codebooks: k-means of every d/P-dim subspace)."""
     _dev(x, "x")
     B, H, N, d = x.shape
-    if x.stride(3) != 1 or d % P:
-        raise IsgError("x must have a contiguous last dimension divisible into P subspaces")
+    if P < 1 or d % P:
+        raise IsgError(f"P={P} must divide d={d}")
     ds = d // P
     dev = x.device
     codes = torch.empty((P, B, H, N), device=dev, dtype=torch.int32)
     cbs = torch.empty((P, B, H, Cc, ds), device=dev, dtype=torch.float32)
-    if B == 1:
-        perm = torch.empty((P, H, N), device=dev, dtype=torch.int32)
-        offsets = torch.empty((P, H, Cc + 1), device=dev, dtype=torch.int32)
-        ws = torch.empty(max(cluster_workspace_size(P, H, N, ds, Cc), 1), device=dev, dtype=torch.uint8)
-        st = lib().isg_cluster(_stream(stream), _ptr(x), _dtype(x), _i64x3((ds, x.stride(1), x.stride(2))), P, H, N,
-                               ds, Cc, iters, 0, None, _ptr(cbs), _ptr(codes), _ptr(perm), _ptr(offsets), None,
-                               None, None, _ptr(ws), ws.numel())
-        _check(st, "isg_cluster (subspaces)")
-        return codes, cbs
-    perm = torch.empty((B, H, N), device=dev, dtype=torch.int32)
-    offsets = torch.empty((B, H, Cc + 1), device=dev, dtype=torch.int32)
-    ws = torch.empty(max(cluster_workspace_size(B, H, N, ds, Cc), 1), device=dev, dtype=torch.uint8)
-    for s in range(P):
-        xs = x[..., s * ds:(s + 1) * ds]
-        st = lib().isg_cluster(_stream(stream), _ptr(xs), _dtype(x), _i64x3(xs.stride()[:3]), B, H, N, ds, Cc,
-                               iters, 0, None, _ptr(cbs[s]), _ptr(codes[s]), _ptr(perm), _ptr(offsets), None, None,
-                               None, _ptr(ws), ws.numel())
-        _check(st, "isg_cluster (subspace)")
+    need = pq_codebooks_workspace_size(x.dtype, B, H, N, d, P, Cc)
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), device=dev, dtype=torch.uint8)
+    st = lib().isg_pq_codebooks(_stream(stream), _ptr(x), _dtype(x), _i64x3(x.stride()[:3]), B, H, N, d, P, Cc,
+                                iters, _ptr(codes), _ptr(cbs), _ptr(ws), ws.numel())
+    _check(st, "isg_pq_codebooks")
     return codes, cbs
 
 

@@ -272,6 +272,35 @@ isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, cons
                          const int64_t o_strides[3], float *lse);
 
 /* ------------------------------------------------------------------------ */
+/* isg_pq_codebooks -- product-quantisation codes and codebooks of x.
+ * Pages: InstaGen, acceptodds.com page, abstract (queries and keys are product-
+ * quantised).  The pages do not say how the codebooks are trained; the reading
+ * taken: subspace s of x (dims [s*ds, (s+1)*ds), ds = d/P) is clustered by the
+ * same k-means as isg_cluster (init_mode 0, iters rounds, Cc centroids), its
+ * centroids are the subspace-s codebook and its labels the codes.  The result is
+ * the one isg_cluster gives on each subspace (a strided view) alone: the call
+ * first copies x into subspace-major order in the workspace, so every subspace's
+ * rows are dense, then clusters all P*B*H (subspace, batch, head) triples in one
+ * run.
+ *
+ * x          device, dt (ISG_BF16 or ISG_F32), element (b,h,t,k) at
+ *            b*x_strides[0] + h*x_strides[1] + t*x_strides[2] + k (strides in
+ *            elements, multiples of 8, x_strides[2] >= d; 16-byte aligned);
+ * codes      device int32 [P,B,H,N] (written): the code of token t in subspace s;
+ * codebooks  device fp32 [P,B,H,Cc,ds] (written);
+ * workspace  device, >= isg_pq_codebooks_workspace_size(dt, B, H, N, d, P, Cc)
+ *            bytes (the subspace-major copy, the clustering's permutation and
+ *            offsets, and isg_cluster's own workspace); caller-owned, no state
+ *            kept between calls.
+ * Needs P | d, d/P in {16, 64, 128}, P*B*H <= 65535, 1 <= Cc <= min(N, 4096),
+ * iters >= 1; else ISG_E_ARG / ISG_E_UNSUPPORTED / ISG_E_DTYPE / ISG_E_WORKSPACE
+ * with nothing launched. */
+size_t isg_pq_codebooks_workspace_size(isg_dtype dt, int B, int H, int N, int d, int P, int Cc);
+isg_status isg_pq_codebooks(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3], int B, int H,
+                            int N, int d, int P, int Cc, int iters, int32_t *codes, float *codebooks,
+                            void *workspace, size_t ws_bytes);
+
+/* ------------------------------------------------------------------------ */
 /* isg_pq_votes -- product-quantised per-query votes for the exact set.
  * Pages: InstaGen, acceptodds.com page, abstract (queries and keys are product-
  * quantised so that block scores are cheap enough for every query; each query
@@ -288,9 +317,9 @@ isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, cons
  *   votes[i][j] = number of queries of group i that voted for j.
  * The votes feed isg_select_sample in ISG_SAMPLE_VOTES mode.
  *
- * q_codes, k_codes   device int32 [P,B,H,N], token order: the labels of
- *                    isg_cluster run on subspace s (dims [s*ds, (s+1)*ds), ds = d/P);
- * q_codebooks, k_codebooks  device fp32 [P,B,H,Cc,ds]: that run's centroids;
+ * q_codes, k_codes   device int32 [P,B,H,N], token order: the codes of
+ *                    isg_pq_codebooks (subspace s = dims [s*ds, (s+1)*ds), ds = d/P);
+ * q_codebooks, k_codebooks  device fp32 [P,B,H,Cc,ds]: its codebooks;
  * perm_q, q_offsets, perm_k, k_offsets  device int32, from isg_cluster on the
  *                    full vectors ([B,H,N] and [B,H,C+1]);
  * kbar    device fp32 [B,H,Ck,d] (written);

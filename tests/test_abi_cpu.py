@@ -231,6 +231,38 @@ def test_pq_votes_rejects(kw):
     assert len(isg.lib().isg_last_error()) > 0
 
 
+def _pqcb(**kw):
+    a = dict(x=FAKE, dt=1, strides=_i64x3(8 * 256 * 128, 256 * 128, 128), B=1, H=8, N=256, d=128, P=8, Cc=64,
+             iters=5, codes=FAKE, cbs=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return isg.lib().isg_pq_codebooks(None, a["x"], a["dt"], a["strides"], a["B"], a["H"], a["N"], a["d"], a["P"],
+                                      a["Cc"], a["iters"], a["codes"], a["cbs"], a["ws"], a["wsb"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(cbs=None), 1), (dict(N=0), 1), (dict(dt=7), 2),
+    (dict(P=3), 1), (dict(P=4), 3), (dict(P=16), 3), (dict(Cc=0), 1), (dict(Cc=257), 1), (dict(iters=0), 1),
+    (dict(H=8192), 1), (dict(strides=_i64x3(8 * 256 * 128, 256 * 128, 100)), 1),
+    (dict(strides=_i64x3(8 * 256 * 128, 256 * 128, 120)), 1), (dict(x=C.c_void_p(264)), 1),
+    (dict(ws=None), 4), (dict(wsb=1024), 4)])
+def test_pq_codebooks_rejects(kw, status):
+    assert _pqcb(**kw) == status
+    assert len(isg.lib().isg_last_error()) > 0
+
+
+def test_pq_codebooks_workspace_holds_the_copy_and_the_clustering():
+    L = isg.lib()
+    B, H, N, d, P, Cc = 1, 40, 75600, 128, 8, 256
+    bf = L.isg_pq_codebooks_workspace_size(1, B, H, N, d, P, Cc)
+    f32 = L.isg_pq_codebooks_workspace_size(0, B, H, N, d, P, Cc)
+    cl = L.isg_cluster_workspace_size(P * B, H, N, d // P, Cc)
+    copy_bf = B * H * N * d * 2
+    assert bf >= cl + copy_bf + P * B * H * N * 4
+    assert f32 - bf >= B * H * N * d * 2 - 256
+    for bad in [(1, B, H, N, d, 3, Cc), (1, B, H, N, d, P, 0), (7, B, H, N, d, P, Cc), (1, 0, H, N, d, P, Cc)]:
+        assert L.isg_pq_codebooks_workspace_size(*bad) == 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 16, 16)

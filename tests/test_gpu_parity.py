@@ -907,17 +907,26 @@ def test_pq_votes_all_scores_tied(orc):
         assert np.array_equal(npy(g["votes"]), votes), E
 
 
-def test_pq_codebooks_strided_and_vs_oracle(orc):
-    """Subspace codes through strided views equal isg_cluster on contiguous copies;
-    agreement with the oracle's own k-means of each subspace is reported."""
-    H, N, d, P, Cc = 2, 3000, 128, 8, 64
-    q, k, v = _inputs(H, N, d, "bf16", seed=21)
-    qg = q.to(DEV)
+@pytest.mark.parametrize("B,dtype,P,Cc", [(1, "bf16", 8, 64), (2, "bf16", 8, 256), (1, "f32", 2, 40),
+                                           (2, "bf16", 1, 16)])
+def test_pq_codebooks_strided_and_vs_oracle(orc, B, dtype, P, Cc):
+    """isg_pq_codebooks (subspace-major copy, then one clustering run over every
+    subspace, batch and head) equals isg_cluster on each subspace alone, bit for
+    bit, through a strided view of the input; agreement with the oracle's own
+    k-means of each subspace is reported and bounded."""
+    H, N, d = 2, 3000, 128
+    say(f"pq codebooks B={B} {dtype} P={P} Cc={Cc}")
+    xs = [_inputs(H, N, d, dtype, seed=21 + b)[0] for b in range(B)]
+    q = torch.stack([x[0] for x in xs])  # [B, H, N, d]
+    # a strided view: every token row padded to 2 d elements
+    big = torch.zeros((B, H, N, 2 * d), dtype=q.dtype, device=DEV)
+    big[..., :d] = q.to(DEV)
+    qg = big[..., :d]
     codes, cbs = isg.pq_codebooks(qg, P, Cc, 3)
     ds = d // P
-    for s in (0, 5):
+    for s in sorted({0, P // 2, P - 1}):
         r = isg.isg_cluster(qg[..., s * ds:(s + 1) * ds].contiguous(), Cc, 3)
-        assert torch.equal(r["labels"], codes[s]) and torch.equal(r["centroids"], cbs[s])
+        assert torch.equal(r["labels"], codes[s]) and torch.equal(r["centroids"], cbs[s]), s
     oc, ocb = orc.pq_codebooks(f32(q), P, Cc, 3)
     agree = (oc == npy(codes)).mean()
     say(f"  PQ code agreement with the oracle's own k-means: {agree:.5f}")
