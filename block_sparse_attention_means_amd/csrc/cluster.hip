@@ -564,9 +564,11 @@ __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent,
 // distance with the low bits replaced by the centroid index.  Positive floats
 // order like their bit patterns, so unsigned min/med3 on keys order by distance
 // (up to the dropped bits, a resolution of 2^bits ulps) and carry the index
-// along.  The K = 4 smallest keys are kept sorted: one min and K-1 med3 per
-// candidate.  (Two would halve the epilogue, but at d = 16 with 256 codewords
-// close pairs are common and each would cost a full rescan.)
+// along.  The K smallest keys are kept sorted: one min and K-1 med3 per
+// candidate.  K = 4, or 3 at d = 16 (a codebook assign that is bound by this
+// epilogue; a token with all K kept candidates inside the decision window is
+// rescanned in full, about 0.1 % of tokens with three and 0.003 % with four on
+// 16-dim subspaces; with two, every close pair, about 3 %, would be).
 template <int K>
 struct TopK {
     uint32_t k[K];
@@ -589,7 +591,7 @@ __device__ __forceinline__ void top_insert(TopK<K> &t, uint32_t key)
 }
 
 template <int D>
-constexpr int topk_of() { return 4; }
+constexpr int topk_of() { return D == 16 ? 3 : 4; }
 
 // fp64 partial sum of (x_k - c_k)^2 over the DPL dims of one lane (x bf16, c fp32;
 // both 8/16-byte aligned at these offsets).

@@ -62,7 +62,8 @@ def _near_tie_ok(orc, x, cent, lab_gpu, lab_orc, tol=1e-5):
 
 @pytest.mark.parametrize("dtype,d,N,C", [("f32", 64, 2048, 8), ("f32", 64, 2048, 32), ("bf16", 128, 3000, 50),
                                          ("bf16", 16, 1500, 256), ("bf16", 64, 777, 13), ("bf16", 128, 300, 2),
-                                         ("bf16", 128, 8192, 4096)])
+                                         ("bf16", 128, 8192, 4096), ("bf16", 16, 500, 2), ("bf16", 16, 2000, 3),
+                                         ("bf16", 16, 4000, 33), ("bf16", 16, 6000, 300)])
 def test_cluster_one_round_stagewise(orc, dtype, d, N, C):
     """Assign given identical centroids (near-tie rule); update given identical labels;
     stable permutation and offsets bit-exact given the labels; gathers exact."""
@@ -111,7 +112,7 @@ def test_cluster_large_norms_first_round(orc, factor):
         assert all(own[j] == j or orc.sqdist(x[0, h][src[j]], init[own[j]]) == 0.0 for j in range(C))
 
 
-@pytest.mark.parametrize("dtype,d,N,C", [("f32", 64, 2048, 8), ("bf16", 128, 4096, 100)])
+@pytest.mark.parametrize("dtype,d,N,C", [("f32", 64, 2048, 8), ("bf16", 128, 4096, 100), ("bf16", 16, 8192, 256)])
 def test_cluster_five_rounds(orc, dtype, d, N, C):
     """End to end after 5 rounds: every round's labels checked against the oracle's
     assignment from the GPU's previous centroids (near-tie rule); final agreement with
