@@ -40,7 +40,8 @@ def parse():
                     help="sampling mode (default: votes for a workload with product quantisation, else importance)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip timing the attention at every budget of the workload (on by default)")
+                    help="skip timing the attention at every budget of the workload and, on the default workload, "
+                         "the PQ stress step and the N sweep (all on by default)")
     ap.add_argument("--sweep", action="store_true", help=argparse.SUPPRESS)  # the default; kept for old commands
     ap.add_argument("--serial-cluster", action="store_true",
                     help="cluster Q, then K, on one stream (profiling aid: per-kernel durations do not overlap)")
@@ -51,7 +52,8 @@ def parse():
                          "uniform calls across the budget sweep (standard and high-entropy generators)")
     ap.add_argument("--study-heads", type=int, default=4, help="heads used by --density-study and --n-sweep")
     ap.add_argument("--n-sweep", action="store_true",
-                    help="also time the step and the attention at N = 75600 x 1, 2, 4, 8 (more latent frames)")
+                    help="also time the step and the attention at N = 75600 x 1, 2, 4, 8 (more latent frames; "
+                         "part of the default run on the default workload)")
     ap.add_argument("--attention-only", type=int, default=0, metavar="K",
                     help="profiling aid: after one full step, run only K attention calls and exit")
     ap.add_argument("--unpermute-calls", type=int, default=0, metavar="K",
@@ -314,6 +316,68 @@ def n_sweep(args, w, isg, make_workload, budget_keys, dev):
     return out
 
 
+def stress_pq_step(args, isg, make_workload, WORKLOADS, budget_keys, dev, steps=3):
+    """The whole step of the PQ stress workload (high-entropy 14B-shaped 720p, votes
+    mode: clustering, scores, PQ codes and votes, selection, attention), timed over
+    `steps` steps after one warm-up, with per-stage HIP-event times."""
+    import numpy as np
+    import torch
+    w = dict(WORKLOADS["wan14b_720p_stress_pq"])
+    H, N, d = w["H"], w["N"], w["d"]
+    E, m = budget_keys(args.exact, N), budget_keys(args.sample, N)
+    q, k, v, _ = make_workload(w, seed=args.seed)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    scale = isg.default_scale(d)
+    P, Cc = w["pq"]
+    stream = torch.cuda.current_stream()
+    ws_q = torch.empty(isg.cluster_workspace_size(1, H, N, d, w["Cq"]), device=dev, dtype=torch.uint8)
+    ws_k = torch.empty(isg.cluster_workspace_size(1, H, N, d, w["Ck"]), device=dev, dtype=torch.uint8)
+    ws_p = torch.empty(isg.pq_codebooks_workspace_size(qg.dtype, 1, H, N, d, P, Cc), device=dev, dtype=torch.uint8)
+    ws_a = torch.empty(isg.attention_workspace_size(1, H, N, w["Cq"], w["Ck"], m), device=dev, dtype=torch.uint8)
+    stages = ["cluster_q_and_k", "probs", "pq_codes", "pq_votes", "select_sample", "attention_and_unpermute"]
+    ev = {s: [] for s in stages}
+
+    def step(record):
+        mk = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+        mk[0].record(stream)
+        cq, ck = isg.cluster_qk(qg, kg, vg, w["Cq"], w["Ck"], w["iters"], ws_q=ws_q, ws_k=ws_k, stream=stream)
+        mk[1].record(stream)
+        S, pi = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=True)
+        mk[2].record(stream)
+        qc, qcb = isg.pq_codebooks(qg, P, Cc, w["iters"], workspace=ws_p)
+        kc, kcb = isg.pq_codebooks(kg, P, Cc, w["iters"], workspace=ws_p)
+        mk[3].record(stream)
+        votes = isg.isg_pq_votes(qc, qcb, kc, kcb, cq["perm"], cq["offsets"], ck["perm"], ck["offsets"], E,
+                                 scale)["votes"]
+        mk[4].record(stream)
+        sel = isg.isg_select_sample(S, ck["offsets"], N, E, m, mode="votes", seed=args.seed, votes=votes)
+        mk[5].record(stream)
+        isg.isg_attention(cq["x_perm"], ck["x_perm"], ck["companion_perm"], cq["offsets"], ck["offsets"], sel, scale,
+                          k_max_sqnorm=ck["max_sqnorm"], perm_q=cq["perm"], workspace=ws_a)
+        mk[6].record(stream)
+        if record:
+            for si, st in enumerate(stages):
+                ev[st].append((mk[si], mk[si + 1]))
+        return cq, ck, sel
+
+    step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        cq, ck, sel = step(True)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    flops, _ = attention_flops(d, cq["offsets"], ck["offsets"], sel["exact_groups"], sel["n_exact"], sel["n_sample"])
+    stage_ms = {st: round(float(np.mean([a.elapsed_time(b) for a, b in ev[st]])), 3) for st in stages}
+    out = {"workload": "wan14b_720p_stress_pq", "mode": "votes", "pq": [P, Cc], "steps": steps,
+           "ms_per_step": round(ms_step, 3), "value_tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+           "attention_tflop_per_call": round(flops / 1e12, 4), "stage_ms": stage_ms}
+    del qg, kg, vg, ws_q, ws_k, ws_p, ws_a
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -514,7 +578,15 @@ def main():
     if args.density_study:
         print("# density study", file=sys.stderr, flush=True)
         result["density_study"] = density_study(args, w, isg, make_workload, WORKLOADS, budget_keys, dev)
-    if args.n_sweep:
+    extras = not args.no_sweep and args.workload == "wan14b_720p" and args.top_p is None and args.mode is None
+    if extras:
+        # the other headline numbers, measured by every default run: the PQ stress
+        # step and the attention / step time as the sequence grows
+        del qg, kg, vg, ws_q, ws_k, ws_a
+        torch.cuda.empty_cache()
+        print("# PQ stress step", file=sys.stderr, flush=True)
+        result["stress_pq"] = stress_pq_step(args, isg, make_workload, WORKLOADS, budget_keys, dev)
+    if args.n_sweep or extras:
         print("# N sweep", file=sys.stderr, flush=True)
         result["n_sweep"] = n_sweep(args, w, isg, make_workload, budget_keys, dev)
     if not args.no_cpu_baseline:

@@ -17,6 +17,7 @@ namespace {
 
 constexpr int kSortChunk = 1024;  // tokens per histogram / scatter chunk
 constexpr int kMaxC = 4096;
+constexpr int kMaxLabelBits = 12;  // labels below kMaxC
 constexpr int kAssignTile = 32;   // centroids per LDS tile in the assign kernel
 // Rows per piece of the centroid update: 16 rows for each of the work-group's row
 // slots (256 threads, d/8 per row), so 256 at d = 128 and 2048 at d = 16.
@@ -227,6 +228,25 @@ __global__ __launch_bounds__(256) void scan_kernel(int32_t *hist, int nchunks, i
     }
 }
 
+// Lanes of the wave whose label equals this lane's: those that differ from it
+// in no label bit, i.e. not in the OR over the bits of (ballot of the bit) XOR
+// (this lane's bit as all ones / zeros).  NB covers every label bit (bits above
+// the labels' width are zero in every lane and change nothing); the bits are
+// independent, so their ballots overlap instead of forming one serial chain.
+template <int NB>
+__device__ __forceinline__ uint64_t same_label(int lab)
+{
+    uint32_t dlo = 0, dhi = 0;
+#pragma unroll
+    for (int bt = 0; bt < NB; ++bt) {
+        const uint64_t bal = __ballot((lab >> bt) & 1);
+        const uint32_t own = 0u - (uint32_t)((lab >> bt) & 1);
+        dlo |= (uint32_t)bal ^ own;
+        dhi |= (uint32_t)(bal >> 32) ^ own;
+    }
+    return ~(((uint64_t)dhi << 32) | dlo);
+}
+
 // One wave per chunk.  It first turns the label counts into label offsets (the
 // exclusive prefix over labels, lane l taking a contiguous run of labels) and
 // adds the chunk's per-label base, so run[c] is the first sorted row of
@@ -272,7 +292,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
         for (int u = 0; u < kB; ++u)
             if (c0 + 64 * u < C) run[c0 + 64 * u] = v[u];
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();  // one wave: LDS order is program order
     {
         const int S = (C + 63) / 64, l0 = min(C, lane * S), l1 = min(C, l0 + S);
         int ls = 0, lp = 0;
@@ -313,7 +333,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
             pb[C] = op;
         }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();  // one wave: LDS order is program order
 #pragma unroll
     for (int u = 0; u < kB; ++u)
         if (lane + 64 * u < C) run[lane + 64 * u] += bv[u];
@@ -325,29 +345,28 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, cons
         for (int u = 0; u < kB; ++u)
             if (c0 + 64 * u < C) run[c0 + 64 * u] += v[u];
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();  // one wave: LDS order is program order
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int step = 0; step < kSortChunk / 64; ++step) {
         const int t = t0 + step * 64 + lane;
         const bool valid = t < N;
         const int lab = labs[step];
-        uint64_t m = __ballot(valid);
-        for (int bt = 0; bt < bits; ++bt) {
-            const bool one = (lab >> bt) & 1;
-            const uint64_t bal = __ballot(one);
-            m &= one ? bal : ~bal;
-        }
+        const uint64_t m = __ballot(valid) & (bits <= 8 ? same_label<8>(lab) : same_label<kMaxLabelBits>(lab));
         const int rank = __popcll(m & below);
         const int cnt = __popcll(m);
         int pos = 0;
         if (valid) pos = run[lab] + rank;
-        __syncthreads();
+        // The work-group is one wave, whose LDS accesses take effect in program
+        // order: the next step's reads see this step's writes with no barrier
+        // (a work-group barrier here would also wait for every perm store to
+        // complete, twice per step).
+        __builtin_amdgcn_wave_barrier();
         if (valid) {
             perm[(int64_t)bh * N + pos] = t;
             if (rank == cnt - 1) run[lab] = pos + 1;
         }
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
