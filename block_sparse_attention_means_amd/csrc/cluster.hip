@@ -386,10 +386,14 @@ __global__ __launch_bounds__(256) void update_piece_kernel(const T *x, Strides x
     constexpr int PR = piece_rows(D);
     constexpr int RPT = PR / RP;   // rows per slot: all indices, then all rows, in flight at once
     __shared__ double red[RP][D];
-    // XCD-aware order: each XCD (launch id mod 8) walks a contiguous range of
-    // (head, piece) pairs, so the heads it works on at a time are few and their
-    // rows, read at random positions, stay in that XCD's L2
-    const int64_t lb = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    // At D = 16 (one head of 32-byte rows is 2.4 MB at N = 75,600) the order is
+    // XCD-aware: each XCD (launch id mod 8) walks a contiguous range of (head,
+    // piece) pairs, so the heads it works on at a time are few and their rows,
+    // read at random positions, stay in that XCD's L2.  Wider rows do not fit an
+    // L2 per head; there the launch order stays head-major (both orders time the
+    // same at D = 128).
+    const int64_t lb = D == 16 ? (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)
+                               : (int64_t)blockIdx.x;
     if (lb >= nblocks) return;
     const int q = (int)(lb % maxp), bh = (int)(lb / maxp), b = bh / H, h = bh % H;
     // the piece's row range comes from the table the scatter wrote (entries past
