@@ -894,6 +894,25 @@ def test_pq_votes_stagewise(orc, H, N, d, P, Cc, Cq, Ck, E):
     assert (votes.sum(-1) >= np.diff(npy(cq["offsets"]), axis=-1)).all()
 
 
+@pytest.mark.parametrize("N,E", [(1_100_000, 200_000), (20_000, 19_999)])
+def test_pq_votes_unequal_groups_and_long_rows(orc, N, E):
+    """Query groups of very unequal size (Zipf component prior), so the fixed query
+    chunks of the votes kernel cross group boundaries (and skip any empty group); at
+    N = 1.1 million tokens the group sizes no longer fit the packed 20-bit sums and
+    the search runs without its early exit; E = N - 1 leaves one key out."""
+    H, d, P, Cc, Cq, Ck = 1, 16, 1, 16, 40, 32
+    say(f"pq votes unequal groups N={N} E={E}")
+    (q, k, v), cq, ck = _clustered(H, N, d, "bf16", Cq, Ck, seed=17, q_scale=0.3, zipf=1.2)
+    nq = np.diff(npy(cq["offsets"])[0, 0])
+    say(f"  query group sizes: max {nq.max()}, mean {nq.mean():.0f}, empty {(nq == 0).sum()}")
+    qc, qcb = isg.pq_codebooks(q.to(DEV), P, Cc, 3)
+    kc, kcb = isg.pq_codebooks(k.to(DEV), P, Cc, 3)
+    scale = isg.default_scale(d)
+    g, kbar, tables, votes = _pq_stage(orc, qc, qcb, kc, kcb, cq, ck, E, scale)
+    assert np.array_equal(npy(g["tables"]), tables)
+    assert np.array_equal(npy(g["votes"]), votes)
+
+
 def test_pq_votes_all_scores_tied(orc):
     """Every key has the same codes, so every group mean (and score) is equal: the
     ranking is by group id alone, and the exact-set rule stops part-way."""
