@@ -1,10 +1,10 @@
 // isg_attention: one flash-style attention over the exact and sampled columns of
 // every query group.
 //
-// Pages: InstaGen, acceptodds.com page, abstract (the sampled tokens are computed
-// together with the top blocks in a single attention kernel, their scores
-// reweighted for the whole skipped region); thelatestinai.com page, Figure 3(d)
-// (the queries of a group share keys, so attention runs over dense blocks).
+// Pages: InstaGen, acceptodds.com page, abstract (exact blocks and sampled
+// tokens go through one attention kernel, the sampled scores adjusted to stand
+// for every skipped key); thelatestinai.com page, Figure 3(d) (one key set per
+// query group, so the work is dense blocks).
 //
 // Structure:
 //   1. columns_kernel   per query group: the column list (row of K_p/V_p, offset

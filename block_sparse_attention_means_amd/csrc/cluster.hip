@@ -1,7 +1,7 @@
 // isg_cluster: Lloyd k-means per head + stable counting sort + coalesced gather.
 //
-// Pages: InstaGen, thelatestinai.com page, Figure 3(a) (queries and keys are
-// clustered into groups) and Figure 2 (Cq = 100, Ck = 500).  Reading: Euclidean
+// Pages: InstaGen, thelatestinai.com page, Figure 3(a) (Q and K partitioned by
+// clustering) and Figure 2 (Cq = 100, Ck = 500).  Reading: Euclidean
 // k-means on the raw vectors, strided init, ties to the lowest index, empty
 // clusters keep their centroid; the permutation is the stable sort by label.
 //

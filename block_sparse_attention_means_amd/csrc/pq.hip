@@ -1,9 +1,8 @@
 // isg_pq_votes: product-quantised per-query voting for the exact set.
 //
-// Pages: InstaGen, acceptodds.com page, abstract (queries and keys are product-
-// quantised so that block scores are cheap enough for every query rather than
-// only the centroid; each query votes for its top blocks; the cluster attends to
-// the blocks with the most votes).  The pages give no formula; the reading:
+// Pages: InstaGen, acceptodds.com page, abstract (product-quantised Q and K make
+// block scores affordable for every query, not only the centroid; each query
+// picks its own top blocks and the group keeps the blocks picked most often).  The pages give no formula; the reading:
 //   Kbar_{j,s} = mean over the keys of group j of their subspace-s codeword
 //                (fp64 sum in permuted row order, one division, rounded to fp32),
 //   M_s[a][j]  = scale * <cw^q_{s,a}, Kbar_{j,s}>   (fp32 fma chain over the dims),

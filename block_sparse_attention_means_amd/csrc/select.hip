@@ -1,12 +1,12 @@
 // isg_probs and isg_select_sample.
 //
-// Pages: InstaGen, thelatestinai.com page, Figure 3(b)-(c) (centroid scores give
-// each key group a probability pi per query group; the top key group is always
-// kept; the rest is sampled in proportion to pi and weighted by 1/pi); Paper
-// Reading AI Learner page, abstract (exact set of the top-scoring keys plus a
-// sample drawn in proportion to estimated attention, reweighted by the inverse
-// sampling probability, one sample per query cluster); acceptodds.com page,
-// abstract (the sample size is a direct budget).
+// Pages: InstaGen, thelatestinai.com page, Figure 3(b)-(c) (centroid scores
+// turned into a per-(query group, key group) probability pi; the best key group
+// never dropped; other keys drawn with probability pi and weight 1/pi); Paper
+// Reading AI Learner page, abstract (an exactly computed set of high-scoring
+// keys, the rest estimated from a sample drawn by estimated attention, each term
+// divided by its draw probability, one sample per query cluster);
+// acceptodds.com page, abstract (the number of sampled tokens is the budget).
 //
 // Everything that decides an integer (scores, ranking, proposal weights, draws)
 // uses explicitly rounded fp32 operations or integers, so the lists and sample

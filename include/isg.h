@@ -3,13 +3,13 @@
  * block-sparse attention (InstaGen) on AMD Instinct MI355X (gfx950).
  *
  * The method (InstaGen, thelatestinai.com page, Figure 3; Paper Reading AI
- * Learner page, abstract): cluster queries and keys of each head, permute the
- * tokens so every cluster is contiguous, turn centroid scores into a
- * probability pi per (query group, key group), compute the top key groups of
- * every query group exactly, represent the remaining keys by one sample per
- * query group drawn in proportion to the estimated attention and reweighted by
- * the inverse sampling probability, and run one attention over the exact and
- * sampled keys.  The entry points below are the steps of that path, in order:
+ * Learner page, abstract), in this header's words: cluster the queries and keys
+ * of each head, permute the tokens so every cluster is contiguous, turn
+ * centroid scores into a probability pi per (query group, key group), compute
+ * each query group's best key groups exactly, stand in for the other keys with
+ * one sample per query group whose draw probabilities follow the estimated
+ * attention (each sampled term divided by its draw probability), and run one
+ * attention over the exact and sampled keys.  The entry points below are the steps of that path, in order:
  *
  *   isg_cluster (Q)  isg_cluster (K, companion V)  isg_probs
  *   isg_select_sample  isg_attention  isg_unpermute
@@ -82,8 +82,8 @@ void isg_proposal_table(uint32_t out[256]);
 
 /* ------------------------------------------------------------------------ */
 /* isg_cluster -- k-means (Lloyd) per head, then a stable permutation.
- * Pages: InstaGen, thelatestinai.com page, Figure 3(a) (queries and keys are
- * clustered into groups) and Figure 2 (Cq = 100, Ck = 500).  The pages do not
+ * Pages: InstaGen, thelatestinai.com page, Figure 3(a) (Q and K partitioned by
+ * clustering) and Figure 2 (Cq = 100, Ck = 500).  The pages do not
  * fix the algorithm; this is Euclidean Lloyd k-means on the raw vectors:
  *   init (init_mode 0): c_j = x_{floor(j*N/C)}; init_mode 1: centroids as given;
  *   `iters` rounds of: label_t = argmin_j |x_t - c_j|^2 (ties -> lowest j),
@@ -149,9 +149,9 @@ isg_status isg_cluster_noalloc(void *stream, const void *x, isg_dtype dt, const 
 
 /* ------------------------------------------------------------------------ */
 /* isg_probs -- centroid scores and pi.
- * Pages: InstaGen, thelatestinai.com page, Figure 3(b) (centroid scores give
- * each key group a probability pi of being used by each query group); Paper
- * Reading AI Learner page, abstract (in proportion to estimated attention).
+ * Pages: InstaGen, thelatestinai.com page, Figure 3(b) (centroid scores turned
+ * into the probability pi that a query group uses a key group); Paper Reading
+ * AI Learner page, abstract (draws follow the estimated attention).
  *   S_ij  = (fp32 fused multiply-add chain over k = 0..d-1 of cq_ik*ck_jk) * scale
  *           -- this exact fp32 order is part of the contract;
  *   pi_ij = n_j e^{S_ij} / sum_j' n_j' e^{S_ij'} over non-empty groups (0 if empty),
@@ -164,12 +164,12 @@ isg_status isg_probs(void *stream, const float *cq, const float *ck, const int32
 
 /* ------------------------------------------------------------------------ */
 /* isg_select_sample -- exact set and the shared sample of each query group.
- * Pages: Paper Reading AI Learner page, abstract (the top-scoring keys form an
- * exact set computed in full; the rest is represented by a sample drawn in
- * proportion to estimated attention, reweighted by the inverse sampling
- * probability; one sample per query cluster shared by its queries);
- * thelatestinai.com page, Figure 3(c) (the top key group is always kept);
- * acceptodds.com page, abstract (the sample size is a direct budget).
+ * Pages: Paper Reading AI Learner page, abstract (high-scoring keys computed
+ * exactly; the rest estimated from a sample drawn by estimated attention, each
+ * term divided by its draw probability; one sample per query cluster, used by
+ * all of its queries); thelatestinai.com page, Figure 3(c) (the best key group
+ * is never dropped); acceptodds.com page, abstract (the number of sampled
+ * tokens is the budget).
  *
  * Exact set of query group i: non-empty key groups ordered by (S_ij desc,
  * j asc) -- in ISG_SAMPLE_VOTES mode by (votes desc, S desc, j asc) -- the
@@ -220,10 +220,10 @@ isg_status isg_select_sample_topp(void *stream, const float *scores, const float
 
 /* ------------------------------------------------------------------------ */
 /* isg_attention -- one attention over the exact and sampled keys.
- * Pages: acceptodds.com page, abstract (the sample is computed together with
- * the top blocks in a single attention kernel, sampled scores reweighted to
- * account for the whole skipped region); thelatestinai.com page, Figure 3(d)
- * (a group's queries share the same keys, so attention runs over dense blocks).
+ * Pages: acceptodds.com page, abstract (exact blocks and sampled tokens go
+ * through one attention kernel, the sampled scores adjusted to stand for every
+ * skipped key); thelatestinai.com page, Figure 3(d) (one key set per query
+ * group, so the work is dense blocks).
  * For query row r of group i the columns are every row of every exact group
  * (offset 0) followed by the n_sample samples (row sample_idx[t], offset
  * sample_bias[t]):
@@ -302,10 +302,9 @@ isg_status isg_pq_codebooks(void *stream, const void *x, isg_dtype dt, const int
 
 /* ------------------------------------------------------------------------ */
 /* isg_pq_votes -- product-quantised per-query votes for the exact set.
- * Pages: InstaGen, acceptodds.com page, abstract (queries and keys are product-
- * quantised so that block scores are cheap enough for every query; each query
- * votes for its top blocks; a query group's exact set is the blocks with the
- * most votes).  The pages give no formula; the reading taken:
+ * Pages: InstaGen, acceptodds.com page, abstract (product-quantised Q and K
+ * make block scores affordable for every query; each query picks its own top
+ * blocks; a query group's exact set is the blocks picked most often).  The pages give no formula; the reading taken:
  *   Kbar_{j,s} = mean over the rows of key group j of their subspace-s codeword
  *                (fp64 sum in permuted row order, one division, fp32 result;
  *                0 for an empty group);

@@ -7,18 +7,20 @@
  * table or helper with the HIP library; it is written from the method as the
  * InstaGen pages describe it:
  *
- *   [A] InstaGen, acceptodds.com page, abstract (product-quantised per-query
- *       voting; one shared random sample of skipped tokens per query cluster,
- *       reweighted to stand for the whole skipped region; one attention kernel).
- *   [B] InstaGen, Paper Reading AI Learner page, abstract (exact set of the
- *       top-scoring keys plus a sample drawn in proportion to estimated
- *       attention, reweighted by the inverse sampling probability; one sample per
- *       query cluster shared by its queries).
- *   [F3] InstaGen, thelatestinai.com page, Figure 3 (a) cluster Q and K,
- *       (b) centroid scores give each key group a probability pi per query
- *       group, (c) the top key group is always kept, the rest is sampled in
- *       proportion to pi with weight 1/pi, (d) a group's queries share keys, so
- *       attention runs over dense blocks.
+ *   [A] InstaGen, acceptodds.com page, abstract (block choice by per-query
+ *       votes on product-quantised scores; a random sample of the skipped
+ *       tokens, one per query cluster, scaled to stand in for everything
+ *       skipped; exact and sampled keys in one attention kernel).
+ *   [B] InstaGen, Paper Reading AI Learner page, abstract (block selection as
+ *       importance sampling: an exactly computed set of high-scoring keys, the
+ *       rest estimated from a sample whose draw probabilities follow the
+ *       estimated attention, each term divided by its draw probability; one
+ *       sample per query cluster, used by all of its queries).
+ *   [F3] InstaGen, thelatestinai.com page, Figure 3: (a) Q and K partitioned
+ *       by clustering, (b) centroid scores turned into a per-(query group,
+ *       key group) probability pi, (c) the best key group never dropped and
+ *       the other keys drawn with probability pi and weight 1/pi, (d) one key
+ *       set per query group, so the work is dense blocks.
  *   [F2] same page, Figure 2: Cq = 100 / Ck = 500, budgets E+S from 4+4 % to
  *       32+32 % of the keys.
  *
@@ -221,7 +223,7 @@ void orc_probs(const float *cq, const float *ck, const int32_t *k_offsets, int B
  *
  * Exact set: non-empty key groups ordered by (score desc, j asc) -- by
  * (votes desc, score desc, j asc) in votes mode -- the first is always taken
- * (the top group is always kept), the following ones while the running key
+ * (the best group is never dropped), the following ones while the running key
  * count stays <= exact_keys; the walk stops at the first group that would
  * exceed it.  Output: group ids ascending.
  *
@@ -504,8 +506,9 @@ void orc_unpermute(const double *o_p, const double *lse_p, const int32_t *perm_q
 
 /* ------------------------------------------------------------------------- */
 /* Product-quantised per-query voting, [A] (queries and keys are product-
- * quantised so block scores are cheap per query; each query votes for its top
- * blocks; the cluster attends to the blocks with the most votes).  The pages
+ * quantised so that every query, not only the centroid, can afford its own
+ * block scores; each query picks its top blocks and the group keeps the blocks
+ * picked most often).  The pages
  * give no formula; the reading taken (parity unpinned by the pages):
  *   codes: k-means of each d/P-dim subspace into Cc codewords (as orc_cluster);
  *   Kbar_{j,s} = mean over the keys of group j of their subspace-s codeword;
