@@ -256,11 +256,18 @@ __device__ __forceinline__ uint64_t same_label(int lab)
 // ballots over the label bits.
 __global__ __launch_bounds__(64) void scatter_kernel(const int32_t *labels, const int32_t *base,
                                                      const int32_t *tot, int N, int C, int nchunks, int bits,
-                                                     int prow, int maxp, int32_t *perm, int32_t *offsets,
-                                                     int32_t *poff, int4 *ptab)
+                                                     int prow, int maxp, int64_t nblocks, int32_t *perm,
+                                                     int32_t *offsets, int32_t *poff, int4 *ptab)
 {
     extern __shared__ int run[];  // C entries (dynamic, so small C lets more waves share a CU)
-    const int chunk = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+    // XCD-aware order: each XCD (launch id mod 8) takes a contiguous range of
+    // (head, chunk) pairs, so all chunks of a head run on one XCD.  A chunk
+    // writes a short run of each label's rows (1,024 / C tokens on average);
+    // the runs of neighbouring chunks are adjacent in perm, and on one L2 their
+    // partial-line stores merge before they reach memory.
+    const int64_t lb = (int64_t)(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (lb >= nblocks) return;
+    const int chunk = (int)(lb % nchunks), bh = (int)(lb / nchunks), lane = threadIdx.x;
     const int32_t *bb = base + ((int64_t)bh * nchunks + chunk) * C;
     const int32_t *tb = tot + (int64_t)bh * C;
     // Loads in issue order: the first batch of label counts and of the chunk's
@@ -1052,6 +1059,8 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
     int bits = 1;
     while ((1 << bits) < C) ++bits;
     const int64_t upd_n = (int64_t)w.maxp * BH;         // (piece, head) work-groups
+    const int64_t sc_n = (int64_t)nchunks * BH;          // (chunk, head) scatter waves
+    const unsigned sc_blocks = (unsigned)((sc_n + 7) & ~(int64_t)7);
     const unsigned upd_blocks = (unsigned)((upd_n + 7) & ~(int64_t)7);
     if (init_mode == 0) {
         const int64_t total = (int64_t)BH * C * D;
@@ -1063,9 +1072,9 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         launch_assign<T, D>(st, x, xs, B, H, N, C, cent, labels, ws, w);
         hist_kernel<<<dim3(nchunks, BH), 256, 0, st>>>(labels, N, C, nchunks, hist);
         scan_kernel<<<dim3((C + 63) / 64, BH), 256, 0, st>>>(hist, nchunks, C, tot);
-        scatter_kernel<<<dim3(nchunks, BH), 64, C * sizeof(int32_t), st>>>(labels, hist, tot, N, C, nchunks, bits,
-                                                                           piece_rows(D), w.maxp, perm, offsets,
-                                                                           poff, ptab);
+        scatter_kernel<<<sc_blocks, 64, C * sizeof(int32_t), st>>>(labels, hist, tot, N, C, nchunks, bits,
+                                                                   piece_rows(D), w.maxp, sc_n, perm, offsets,
+                                                                   poff, ptab);
         // the last iteration's update also writes the permuted copy of x
         update_piece_kernel<T, D><<<upd_blocks, 256, 0, st>>>(x, xs, H, N, C, perm, poff, ptab, w.maxp, upd_n,
                                                               partial, it + 1 == iters ? x_perm : nullptr,
