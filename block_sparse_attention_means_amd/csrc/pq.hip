@@ -9,14 +9,14 @@
 //   score(q,j) = sum_s M_s[code_s(q)][j]            (fp32, s ascending),
 //   every query takes the exact-set rule over its own ranking (score desc, j asc)
 //   and votes for the groups it takes; votes[i][j] counts the votes of group i.
-// Codes come from isg_cluster on each d/P-dim subspace (Cc codewords).
+// Codes come from isg_pq_codebooks: k-means of each d/P-dim subspace (Cc codewords).
 //
 // The per-query rule is evaluated without sorting: with C(u) = sum of n_j over
 // groups whose order-preserving score bits are >= u, the groups strictly above
 // u* = max{u : C(u) > E} are all taken (their total is <= E), and the groups at
 // u* are then taken in ascending j while the running count stays <= E (the first
-// group of the ranking always).  u* is found by bisection over the 32-bit key
-// space with one wave-wide sum per step.
+// group of the ranking always).  u* is found by a radix selection over the 32-bit
+// keys (radix_threshold below).
 #include <algorithm>
 #include <cmath>
 
@@ -140,11 +140,6 @@ constexpr int kVoteQPW = 16;  // queries per wave
 constexpr int kVoteChunk = kVoteWaves * kVoteQPW;
 constexpr int kPBatch = 8;  // subspaces whose table rows are in flight together
 
-__device__ __forceinline__ float key_to_float(uint32_t k)
-{
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
 __device__ __forceinline__ uint32_t wave_min(uint32_t v)
 {
     v = min(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
@@ -167,11 +162,85 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v)
 
 constexpr int kCountBits = 20;  // sizes below 2^20, counts up to 1024: sums stay below 2^31
 constexpr int kCountMask = (1 << kCountBits) - 1;
-constexpr int kFloatSteps = 6;
 
 __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *p, int64_t n)
 {
     for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256) p[e] = 0;
+}
+
+// The exact-set threshold of one query: with C(u) = sum of n_j over the
+// non-empty groups whose order-preserving score key is >= u, find u* = max{u :
+// C(u) > E} (C(min key) = total > E) and C(u* + 1).  Radix selection from the
+// highest bit in which the keys differ, 8 bits a pass: each pass sums n_j per
+// digit over the groups that still match the digits chosen so far (LDS atomics
+// into this wave's 256-bin histogram), and the digit taken is the largest whose
+// suffix sum, plus the sizes already above, exceeds E -- so the chosen prefix is
+// always the largest u with C(u) > E among the keys decided so far.  With packed
+// sizes (total < 2^kCountBits) every bin also counts its groups, and a pass that
+// leaves one group in the chosen bin ends the search: u* is that group's key.
+template <int KPL>
+__device__ __forceinline__ void radix_threshold(const uint32_t (&ok)[KPL], const int (&nk)[KPL],
+                                                const int (&nkp)[KPL], bool packed, int E, int *hist, int lane,
+                                                uint32_t &thr, int &above)
+{
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int k = 0; k < KPL; ++k)
+        if (nk[k] > 0) {
+            kmin = min(kmin, ok[k]);
+            kmax = max(kmax, ok[k]);
+        }
+    kmin = wave_min(kmin);
+    kmax = wave_max(kmax);
+    const uint32_t diff = kmin ^ kmax;
+    int pos = diff == 0u ? 0 : 32 - __builtin_clz(diff);  // bits [0, pos) are undecided
+    uint32_t prefix = pos == 32 ? 0u : (kmin >> pos) << pos;
+    int ab = 0;  // packed sum of the groups above the prefix's range
+    while (pos > 0) {
+        const int nb = min(8, pos), shift = pos - nb;
+        // clear, count (one wave: its LDS operations take effect in program order)
+        *reinterpret_cast<int4 *>(&hist[4 * lane]) = make_int4(0, 0, 0, 0);
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int k = 0; k < KPL; ++k) {
+            const bool alive = nk[k] > 0 && ((uint64_t)ok[k] >> pos) == ((uint64_t)prefix >> pos);
+            if (alive) atomicAdd(&hist[(ok[k] >> shift) & ((1u << nb) - 1u)], nkp[k]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        const int4 h = *reinterpret_cast<const int4 *>(&hist[4 * lane]);
+        // suffix sums over the bins: s_i = bins >= 4 lane + i of this lane, plus the lanes above
+        const int s3 = h.w, s2 = s3 + h.z, s1 = s2 + h.y, s0 = s1 + h.x;
+        const int incl = wave_inclusive_scan(s0);
+        const int rest = __builtin_amdgcn_readlane(incl, 63) - incl;  // bins of the lanes above
+        const int c0 = ab + rest + s0, c1 = ab + rest + s1, c2 = ab + rest + s2, c3 = ab + rest + s3;
+        auto wt = [&](int v) { return packed ? (v & kCountMask) : v; };
+        // C is non-increasing in the digit, so the digits with C > E are 0 .. d*
+        const int dstar = __popcll(__ballot(wt(c0) > E)) + __popcll(__ballot(wt(c1) > E)) +
+                          __popcll(__ballot(wt(c2) > E)) + __popcll(__ballot(wt(c3) > E)) - 1;
+        // C(prefix . d*) and C(prefix . (d* + 1)) (the latter is ab when d* is the last bin)
+        const int ls = dstar >> 2, is = dstar & 3;
+        const int cs = is == 0 ? __builtin_amdgcn_readlane(c0, ls) : is == 1 ? __builtin_amdgcn_readlane(c1, ls)
+                     : is == 2 ? __builtin_amdgcn_readlane(c2, ls) : __builtin_amdgcn_readlane(c3, ls);
+        const int ln = (dstar + 1) >> 2, in = (dstar + 1) & 3;
+        int cn = ab;
+        if (dstar + 1 < (1 << nb))
+            cn = in == 0 ? __builtin_amdgcn_readlane(c0, ln) : in == 1 ? __builtin_amdgcn_readlane(c1, ln)
+               : in == 2 ? __builtin_amdgcn_readlane(c2, ln) : __builtin_amdgcn_readlane(c3, ln);
+        prefix |= (uint32_t)dstar << shift;
+        ab = cn;
+        pos = shift;
+        if (packed && pos > 0 && ((cs - cn) >> kCountBits) == 1) {
+            // one group left in the chosen bin: its key is the threshold
+#pragma unroll
+            for (int k = 0; k < KPL; ++k) {
+                const uint64_t m = __ballot(nk[k] > 0 && ((uint64_t)ok[k] >> pos) == ((uint64_t)prefix >> pos));
+                if (m) prefix = __builtin_amdgcn_readlane(ok[k], __builtin_ctzll(m));
+            }
+            pos = 0;
+        }
+    }
+    thr = prefix;
+    above = packed ? (ab & kCountMask) : ab;
 }
 
 template <int KPL>
@@ -192,6 +261,7 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
                                                        int nblocks, int32_t *votes)
 {
     __shared__ int nsz[KPL * 64];
+    __shared__ __attribute__((aligned(16))) int vhist[kVoteWaves][256];  // one radix histogram per wave
     const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
     if (lb >= nblocks) return;
     const int bh = lb / chunks, b = bh / H, h = bh % H;
@@ -209,17 +279,13 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
         part += nk[k];
     }
     const int total = wave_sum(part);
-    // packed per-group term of the bisection sums: size in the low kCountBits
-    // bits, one count per non-empty group above them (needs total < 2^kCountBits)
+    // packed per-group term of the threshold search's sums: size in the low
+    // kCountBits bits, one count per non-empty group above them (needs total <
+    // 2^kCountBits)
     const bool packed = total < (1 << kCountBits);
     int nkp[KPL];
-    int gpart = 0;
 #pragma unroll
-    for (int k = 0; k < KPL; ++k) {
-        nkp[k] = nk[k] + (packed && nk[k] > 0 ? (1 << kCountBits) : 0);
-        gpart += nk[k] > 0;
-    }
-    const int groups = wave_sum(gpart);
+    for (int k = 0; k < KPL; ++k) nkp[k] = nk[k] + (packed && nk[k] > 0 ? (1 << kCountBits) : 0);
     const int E = exact_keys;
     const int32_t *qo = q_offsets + (int64_t)bh * (Cq + 1);
     const float *tb = tables + (int64_t)bh * P * Cc * Ck;
@@ -302,56 +368,9 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
         uint32_t ok[KPL];
 #pragma unroll
         for (int k = 0; k < KPL; ++k) ok[k] = orderable(sc[k]);
-        // Bisection: lo keeps C(lo) > E, hi keeps C(hi) <= E.  It starts on the
-        // keys' own range [min, max + 1) of the non-empty groups (C(min) = total >
-        // E, C(max + 1) = 0).  The first kFloatSteps steps halve the score
-        // interval, later ones the key interval, so at most kFloatSteps + 32 steps
-        // are taken (any point strictly inside the interval is a correct step).
-        // With packed counts (total < 2^20) each step also counts the groups at or
-        // above mid, so it stops as soon as one group is left in [lo, hi): that
-        // group's key is the largest u with C(u) > E, exactly where the full
-        // bisection would end.
-        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-        for (int k = 0; k < KPL; ++k)
-            if (nk[k] > 0) {
-                kmin = min(kmin, ok[k]);
-                kmax = max(kmax, ok[k]);
-            }
-        uint32_t lo = wave_min(kmin);
-        uint64_t hi = (uint64_t)wave_max(kmax) + 1u;
-        int above = 0;  // C(hi)
-        int g_lo = groups, g_hi = 0;  // groups with key >= lo, >= hi
-        for (int it = 0; hi - lo > 1 && (!packed || g_lo - g_hi > 1); ++it) {
-            uint32_t mid = lo + (uint32_t)((hi - lo) >> 1);
-            if (it < kFloatSteps) {
-                const float a = key_to_float(lo), b = key_to_float((uint32_t)(hi - 1));
-                const uint32_t fm = __builtin_amdgcn_readfirstlane(orderable(0.5f * a + 0.5f * b));
-                if (fm > lo && (uint64_t)fm < hi) mid = fm;
-            }
-            int p = 0;
-#pragma unroll
-            for (int k = 0; k < KPL; ++k) p += ok[k] >= mid ? nkp[k] : 0;
-            const int sum = wave_sum(p);
-            const int c = packed ? (sum & kCountMask) : sum;
-            const int g = packed ? (sum >> kCountBits) : 0;
-            if (c > E) {
-                lo = mid;
-                g_lo = g;
-            } else {
-                hi = mid;
-                above = c;
-                g_hi = g;
-            }
-        }
-        if (hi - lo > 1) {
-            // one non-empty group left in [lo, hi): lo moves up to its key
-#pragma unroll
-            for (int k = KPL - 1; k >= 0; --k) {
-                const uint64_t m = __ballot(nk[k] > 0 && ok[k] >= lo && (uint64_t)ok[k] < hi);
-                if (m) lo = __builtin_amdgcn_readlane(ok[k], __builtin_ctzll(m));
-            }
-        }
+        uint32_t lo = 0;  // the threshold: the largest key u with C(u) > E
+        int above = 0;    // C(lo + 1): the size of the groups strictly above it
+        radix_threshold<KPL>(ok, nk, nkp, packed, E, vhist[wave], lane, lo, above);
         uint64_t take[KPL], tie[KPL];
 #pragma unroll
         for (int k = 0; k < KPL; ++k) {
