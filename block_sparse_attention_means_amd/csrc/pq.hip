@@ -138,7 +138,8 @@ __device__ __forceinline__ int wave_sum(int v)
 constexpr int kVoteWaves = 8;
 constexpr int kVoteQPW = 16;  // queries per wave
 constexpr int kVoteChunk = kVoteWaves * kVoteQPW;
-constexpr int kPBatch = 8;  // subspaces whose table rows are in flight together
+constexpr int kPBatch = 8;  // subspaces whose codes are fetched together
+constexpr int kRowSplit = 2;  // parts of a batch whose table rows are in flight together
 
 __device__ __forceinline__ uint32_t wave_min(uint32_t v)
 {
@@ -344,21 +345,30 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
 #pragma unroll
                 for (int s = 0; s < kPBatch; ++s) codes[s] = s0 + s < P ? qcode[(s0 + s) * sstride + t] : 0;
             }
-            float rv[kPBatch][KPL];
+            // rows in kRowSplit parts of kPBatch / kRowSplit subspaces: fewer
+            // registers in flight, so more waves per SIMD hide the latency; each
+            // part is issued after the one before is summed
 #pragma unroll
-            for (int s = 0; s < kPBatch; ++s) {
-                const float *row = tb + ((int64_t)(s0 + s) * Cc + codes[s]) * Ck + lane;
+            for (int hb = 0; hb < kRowSplit; ++hb) {
+                constexpr int HB = kPBatch / kRowSplit;
+                float rv[HB][KPL];
 #pragma unroll
-                for (int k = 0; k < KPL; ++k)
-                    rv[s][k] = (s0 + s < P && k * 64 + lane < Ck) ? row[k * 64] : 0.0f;
-            }
-#pragma unroll
-            for (int s = 0; s < kPBatch; ++s)
-                if (s0 + s < P) {
+                for (int s = 0; s < HB; ++s) {
+                    const int ss = hb * HB + s;
+                    const float *row = tb + ((int64_t)(s0 + ss) * Cc + codes[ss]) * Ck + lane;
 #pragma unroll
                     for (int k = 0; k < KPL; ++k)
-                        if (k * 64 + lane < Ck) sc[k] = __fadd_rn(sc[k], rv[s][k]);
+                        rv[s][k] = (s0 + ss < P && k * 64 + lane < Ck) ? row[k * 64] : 0.0f;
                 }
+#pragma unroll
+                for (int s = 0; s < HB; ++s)
+                    if (s0 + hb * HB + s < P) {
+#pragma unroll
+                        for (int k = 0; k < KPL; ++k)
+                            if (k * 64 + lane < Ck) sc[k] = __fadd_rn(sc[k], rv[s][k]);
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if (r + 1 < r_stop) {
             const int tn = perm_q[(int64_t)bh * N + r + 1];
