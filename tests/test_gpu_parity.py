@@ -913,6 +913,24 @@ def test_pq_votes_unequal_groups_and_long_rows(orc, N, E):
     assert np.array_equal(npy(g["votes"]), votes)
 
 
+def test_pq_votes_sixteen_subspaces(orc):
+    """P = 16 subspaces of 16 dims (d = 256), more than one batch of table rows per
+    query: codes and codebooks are given directly (random), the group structure
+    comes from a real clustering; Kbar, tables and votes bit-exact."""
+    H, N, Cq, Ck, P, Cc, ds, E = 1, 3000, 8, 100, 16, 32, 16, 300
+    (q, k, v), cq, ck = _clustered(H, N, 128, "bf16", Cq, Ck, seed=33)
+    g = torch.Generator().manual_seed(33)
+    qc = torch.randint(0, Cc, (P, 1, H, N), generator=g, dtype=torch.int32).to(DEV)
+    kc = torch.randint(0, Cc, (P, 1, H, N), generator=g, dtype=torch.int32).to(DEV)
+    qcb = torch.randn((P, 1, H, Cc, ds), generator=g).to(DEV)
+    kcb = torch.randn((P, 1, H, Cc, ds), generator=g).to(DEV)
+    scale = isg.default_scale(P * ds)
+    gv, kbar, tables, votes = _pq_stage(orc, qc, qcb, kc, kcb, cq, ck, E, scale)
+    assert np.array_equal(npy(gv["kbar"]), kbar)
+    assert np.array_equal(npy(gv["tables"]), tables)
+    assert np.array_equal(npy(gv["votes"]), votes)
+
+
 def test_pq_votes_all_scores_tied(orc):
     """Every key has the same codes, so every group mean (and score) is equal: the
     ranking is by group id alone, and the exact-set rule stops part-way."""
