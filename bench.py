@@ -335,18 +335,25 @@ def stress_pq_step(args, isg, make_workload, WORKLOADS, budget_keys, dev, steps=
     ws_k = torch.empty(isg.cluster_workspace_size(1, H, N, d, w["Ck"]), device=dev, dtype=torch.uint8)
     ws_p = torch.empty(isg.pq_codebooks_workspace_size(qg.dtype, 1, H, N, d, P, Cc), device=dev, dtype=torch.uint8)
     ws_a = torch.empty(isg.attention_workspace_size(1, H, N, w["Cq"], w["Ck"], m), device=dev, dtype=torch.uint8)
-    stages = ["cluster_q_and_k", "probs", "pq_codes", "pq_votes", "select_sample", "attention_and_unpermute"]
+    # the PQ codes of Q and K run on a third stream beside the clustering (the
+    # codebook assign is VALU-bound, K's assign matrix-core bound); pq_codes_exposed
+    # is the main stream's wait for them after the scores
+    stages = ["cluster_q_and_k", "probs", "pq_codes_exposed", "pq_votes", "select_sample", "attention_and_unpermute"]
     ev = {s: [] for s in stages}
+    s_pq = torch.cuda.Stream()
 
     def step(record):
         mk = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
         mk[0].record(stream)
+        s_pq.wait_stream(stream)
+        with torch.cuda.stream(s_pq):
+            qc, qcb = isg.pq_codebooks(qg, P, Cc, w["iters"], workspace=ws_p, stream=s_pq)
+            kc, kcb = isg.pq_codebooks(kg, P, Cc, w["iters"], workspace=ws_p, stream=s_pq)
         cq, ck = isg.cluster_qk(qg, kg, vg, w["Cq"], w["Ck"], w["iters"], ws_q=ws_q, ws_k=ws_k, stream=stream)
         mk[1].record(stream)
         S, pi = isg.isg_probs(cq["centroids"], ck["centroids"], ck["offsets"], scale, want_pi=True)
         mk[2].record(stream)
-        qc, qcb = isg.pq_codebooks(qg, P, Cc, w["iters"], workspace=ws_p)
-        kc, kcb = isg.pq_codebooks(kg, P, Cc, w["iters"], workspace=ws_p)
+        stream.wait_stream(s_pq)
         mk[3].record(stream)
         votes = isg.isg_pq_votes(qc, qcb, kc, kcb, cq["perm"], cq["offsets"], ck["perm"], ck["offsets"], E,
                                  scale)["votes"]
@@ -431,7 +438,13 @@ def main():
     ws_a = torch.empty(isg.attention_workspace_size(B, H, N, w["Cq"], w["Ck"], m_max), device=dev,
                        dtype=torch.uint8)
     # the attention writes O and LSE in token order itself (the un-permute step fused)
-    stages = ["cluster_q_and_k", "probs"] + (["pq_codes", "pq_votes"] if mode == "votes" else []) + [
+    # votes mode: the PQ codes of Q and K run on a third stream beside the
+    # clustering (serially on the main stream with --serial-cluster); the stage then
+    # records only the main stream's wait for them
+    pq_side = mode == "votes" and not args.serial_cluster
+    s_pq = torch.cuda.Stream() if pq_side else None
+    stages = ["cluster_q_and_k", "probs"] + (
+        ["pq_codes_exposed" if pq_side else "pq_codes", "pq_votes"] if mode == "votes" else []) + [
         "select_sample", "attention_and_unpermute"]
     ev = {s: [] for s in stages}
 
@@ -439,6 +452,12 @@ def main():
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
         if record:
             marks[0].record(stream)
+        if pq_side:
+            P, Cc = w["pq"]
+            s_pq.wait_stream(stream)
+            with torch.cuda.stream(s_pq):
+                qc, qcb = isg.pq_codebooks(qg, P, Cc, w["iters"], stream=s_pq)
+                kc, kcb = isg.pq_codebooks(kg, P, Cc, w["iters"], stream=s_pq)
         if args.serial_cluster:
             cq = isg.isg_cluster(qg, w["Cq"], w["iters"], workspace=ws_q, stream=stream)
             ck = isg.isg_cluster(kg, w["Ck"], w["iters"], companion=vg, want_max_sqnorm=True, workspace=ws_k,
@@ -455,8 +474,11 @@ def main():
         votes = None
         if mode == "votes":
             P, Cc = w["pq"]
-            qc, qcb = isg.pq_codebooks(qg, P, Cc, w["iters"])
-            kc, kcb = isg.pq_codebooks(kg, P, Cc, w["iters"])
+            if pq_side:
+                stream.wait_stream(s_pq)
+            else:
+                qc, qcb = isg.pq_codebooks(qg, P, Cc, w["iters"])
+                kc, kcb = isg.pq_codebooks(kg, P, Cc, w["iters"])
             mi += 1
             if record:
                 marks[mi].record(stream)
