@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const T *x, Strides xs, con
 // |x|^2 + M are each split exactly into three bf16 parts (24 significant bits),
 // paired with ones, so the accumulator holds |x - c|^2 + M itself, M a per-token
 // margin above the screening error (so the accumulator stays positive).  Per
-// token the four best candidates are kept; whenever a rival lies within
+// token the best candidates are kept (four; three at D = 16); whenever a rival lies within
 // tau = 1e-4 (|x|^2 + max_j |c_j|^2) -- several times the worst-case error of the
 // split and of fp32 accumulation -- the decision is re-taken on fp64 distances
 // (the close candidates, or every centroid when all kept candidates are close),
@@ -709,7 +709,7 @@ __device__ __forceinline__ void planes_direct(uint8_t *buf, const uint16_t *pb, 
 
 // One tile of 32 centroids against the 64 tokens of this wave: the accumulators
 // end as |x - c|^2 + 1 (norm step first, then the -2 <x, c> steps), and every
-// (token, centroid) key goes into the token's top four.  The key's index bits
+// (token, centroid) key goes into the token's kept candidates.  The key's index bits
 // hold the centroid's row in the tile without the half-wave's offset of 4 rows;
 // the caller adds it once per token.
 template <int D, bool BYTEKEY>
@@ -867,7 +867,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void a
 
     // Decisions.  Close calls go to a work list: 16 lanes per (token, candidate)
     // entry evaluate |x - c|^2 in fp64 and the token takes the smallest (ties to
-    // the lower index).  A token with four candidates within tau is rescanned in
+    // the lower index).  A token whose kept candidates are all within tau is rescanned in
     // fp64 over all C, again 16 lanes per candidate.
     constexpr int kRQ = 3 * 256;
     constexpr int DPL = D / 16;  // dims per lane

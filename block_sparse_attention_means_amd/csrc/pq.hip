@@ -321,7 +321,7 @@ __global__ __launch_bounds__(64 * kVoteWaves) void pq_votes_kernel(const int32_t
         flush_votes<KPL>(vb + (int64_t)i * Ck, Ck, lane, vk);
         return;
     }
-    // codes of the next query are fetched while the current one runs its bisection
+    // codes of the next query are fetched while the current one runs its threshold search
     int codes[kPBatch];
     {
         const int t = perm_q[(int64_t)bh * N + r];

@@ -92,10 +92,10 @@ void isg_proposal_table(uint32_t out[256]);
  *   x_perm[r] = x[perm[r]], companion_perm[r] = companion[perm[r]].
  * The labels are the assignment of the last round and the centroids are the
  * means of those groups.  For bf16 x the argmin is screened on fp32 distances
- * (bf16 hi/lo centroid planes on the matrix cores) and the four best are kept;
- * whenever other kept candidates lie within the screening error bound of the
- * best, it is re-decided on fp64 distances among the four, or over all C when
- * all four are that close.  For fp32 x the argmin is taken on fp32 distances
+ * (bf16 hi/lo centroid planes on the matrix cores) and the four best are kept
+ * (three at d = 16); whenever other kept candidates lie within the screening
+ * error bound of the best, it is re-decided on fp64 distances among them, or
+ * over all C when all kept candidates are that close.  For fp32 x the argmin is taken on fp32 distances
  * (sequential fused sums) and stands unless the runner-up lies within 4e-5
  * relative of the best; then every centroid is re-compared in fp64.  Either way
  * a label differs from the fp64 argmin only at fp64-level ties (the re-decisions
