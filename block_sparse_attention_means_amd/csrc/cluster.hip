@@ -490,13 +490,17 @@ __global__ __launch_bounds__(128) void update_final_kernel(int C, const int32_t 
         __syncthreads();
         if (threadIdx.x == 0) max_sqnorm[bh] = fmaxf(wmax[0], wmax[1]);
     }
+    // 128 / D centroids per work-group (one for D >= 128), D threads each
+    constexpr int CPW = D >= 128 ? 1 : 128 / D;
+    const int jc = j * CPW + (D >= 128 ? 0 : (int)threadIdx.x / D);
+    if (jc >= C) return;
     const int32_t *ob = offsets + (int64_t)bh * (C + 1);
-    const int n = ob[j + 1] - ob[j];
+    const int n = ob[jc + 1] - ob[jc];
     if (n == 0) return;  // empty: keep the centroid
-    for (int k = threadIdx.x; k < D; k += 128) {
+    for (int k = D >= 128 ? (int)threadIdx.x : (int)threadIdx.x % D; k < D; k += 128) {
         double sum = 0.0;
-        for (int q = pb[j]; q < pb[j + 1]; ++q) sum += partial[((int64_t)bh * maxp + q) * D + k];
-        cent[((int64_t)bh * C + j) * D + k] = (float)(sum / (double)n);
+        for (int q = pb[jc]; q < pb[jc + 1]; ++q) sum += partial[((int64_t)bh * maxp + q) * D + k];
+        cent[((int64_t)bh * C + jc) * D + k] = (float)(sum / (double)n);
     }
 }
 
@@ -555,13 +559,16 @@ template <int D>
 __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent, int C, int Cpad, uint16_t *planes,
                                                               float *norms, uint16_t *aug)
 {
-    const int bh = blockIdx.y, lane = threadIdx.x & 63;
-    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    // LPC lanes per centroid (D of them for D < 64): the fp64 norm is the same
+    // butterfly either way, since lanes past D only ever added zeros
+    constexpr int LPC = D < 64 ? D : 64, CPB = 256 / LPC;
+    const int bh = blockIdx.y, lane = threadIdx.x % LPC;
+    const int j = blockIdx.x * CPB + threadIdx.x / LPC;
     if (j >= Cpad) return;
     uint16_t *hi = planes + ((int64_t)bh * 2 * Cpad + j) * D;
     uint16_t *lo = planes + ((int64_t)bh * 2 * Cpad + Cpad + j) * D;
     double nn = 0.0;
-    for (int k = lane; k < D; k += 64) {
+    for (int k = lane; k < D; k += LPC) {
         if (j < C) {
             const float v = cent[((int64_t)bh * C + j) * D + k];
             const uint16_t hb = f32_to_bf16_bits(-2.0f * v);
@@ -575,7 +582,7 @@ __global__ __launch_bounds__(256) void centroid_planes_kernel(const float *cent,
         }
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) nn += __shfl_xor(nn, off);
+    for (int off = LPC / 2; off > 0; off >>= 1) nn += __shfl_xor(nn, off);
     if (lane == 0) {
         const float nf = j < C ? (float)nn : 1e30f;  // padded: never wins
         norms[(int64_t)bh * Cpad + j] = nf;
@@ -1006,7 +1013,8 @@ void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, 
         uint16_t *planes = (uint16_t *)(ws + w.off_planes);
         float *norms = (float *)(ws + w.off_norms);
         uint16_t *aug = (uint16_t *)(ws + w.off_aug);
-        centroid_planes_kernel<D><<<dim3(w.Cpad / 4, BH), 256, 0, st>>>(cent, C, w.Cpad, planes, norms, aug);
+        centroid_planes_kernel<D><<<dim3(w.Cpad / (D < 64 ? 256 / D : 4), BH), 256, 0, st>>>(cent, C, w.Cpad, planes,
+                                                                                          norms, aug);
         const dim3 grid((N + 255) / 256, BH);
         if (w.Cpad <= 256)
             assign_mfma_kernel<D, true><<<grid, 256, 0, st>>>(x, xs, H, N, C, w.Cpad, planes, norms, aug, cent,
@@ -1079,7 +1087,7 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         update_piece_kernel<T, D><<<upd_blocks, 256, 0, st>>>(x, xs, H, N, C, perm, poff, ptab, w.maxp, upd_n,
                                                               partial, it + 1 == iters ? x_perm : nullptr,
                                                               last_norms ? pmax : nullptr);
-        update_final_kernel<D><<<dim3(C, BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent,
+        update_final_kernel<D><<<dim3((C + (D >= 128 ? 1 : 128 / D) - 1) / (D >= 128 ? 1 : 128 / D), BH), 128, 0, st>>>(C, offsets, poff, w.maxp, partial, cent,
                                                             last_norms ? pmax : nullptr, max_sqnorm);
     }
     if (comp_perm) {
