@@ -388,7 +388,7 @@ def stress_pq_step(args, isg, make_workload, WORKLOADS, budget_keys, dev, steps=
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark runs on one GPU; --gpus {args.gpus} is not supported "
               "(heads shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
