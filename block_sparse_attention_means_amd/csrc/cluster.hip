@@ -756,8 +756,11 @@ __device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, int C,
     }
 }
 
+// At D = 16 the epilogue (key packing and top-k insertion on the VALU) outweighs the
+// MFMA work and hides latency only through occupancy: six waves per SIMD (80 VGPRs)
+// beat four; asking for seven spills to scratch and is slower again.
 template <int D, bool BYTEKEY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void assign_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6 : 2))) void assign_mfma_kernel(
     const uint16_t *__restrict__ x, Strides xs, int H, int N, int C, int Cpad, const uint16_t *__restrict__ planes,
     const float *__restrict__ norms, const uint16_t *__restrict__ aug, const float *__restrict__ cent,
     int32_t *__restrict__ labels)
