@@ -17,7 +17,11 @@ namespace {
 
 constexpr int kSortChunk = 1024;  // tokens per histogram / scatter chunk
 constexpr int kMaxC = 4096;
-constexpr int kMaxLabelBits = 12;  // labels below kMaxC
+constexpr int kMaxLabelBits = 12;
+constexpr int kPqMaxP = 64;       // subspaces per row the split kernel tracks exponents for
+constexpr int kPqIntMaxC = 256;   // codewords up to which the PQ update sums integers in LDS
+constexpr int kPqAccTok = 8192;   // tokens per work-group of that update
+constexpr int kPqPitch = 17;      // int64 words per codeword in its LDS sums (16 dims + 1)  // labels below kMaxC
 constexpr int kAssignTile = 32;   // centroids per LDS tile in the assign kernel
 // Rows per piece of the centroid update: 16 rows for each of the work-group's row
 // slots (256 threads, d/8 per row), so 256 at d = 128 and 2048 at d = 16.
@@ -1034,23 +1038,144 @@ void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, 
 // out[s][b][h][t][e].  A work-group moves 64 tokens: it reads their rows whole
 // (coalesced) and writes P runs of 64*ds contiguous elements, so each subspace's
 // k-means then reads dense ds-element rows instead of ds-element pieces of longer
-// rows (a 32-byte piece costs a 128-byte line fetch).
+// rows (a 32-byte piece costs a 128-byte line fetch).  With emax non-null (bf16,
+// ds = 16) it also raises emax[s*B*H + bh] to the largest exponent field among
+// the subspace's values (sign dropped), which the integer update scales by.
 template <typename T>
 __global__ __launch_bounds__(256) void pq_split_kernel(const T *x, Strides xs, int B, int H, int N, int d, int ds,
-                                                       T *out)
+                                                       T *out, int32_t *emax)
 {
+    __shared__ int smax[kPqMaxP];
     const int cpr = d / 8;  // 8-element chunks per row
     const int bh = blockIdx.y, b = bh / H, h = bh % H;
     const int t0 = blockIdx.x * 64;
     const int nt = min(64, N - t0);
     const int64_t plane = (int64_t)B * H * N * ds;
+    if (emax) {
+        for (int s = threadIdx.x; s < d / ds; s += 256) smax[s] = 0;
+        __syncthreads();
+    }
+    int ps = -1;   // this thread's subspace so far and its largest exponent field
+    uint32_t pm = 0;
     for (int q = threadIdx.x; q < nt * cpr; q += 256) {
         const int tt = q / cpr, c = q % cpr;
         const int s = (c * 8) / ds, e0 = (c * 8) % ds;
         const T *src = x + b * xs.b + h * xs.h + (int64_t)(t0 + tt) * xs.t + c * 8;
         T *dst = out + s * plane + ((int64_t)bh * N + t0 + tt) * ds + e0;
         copy8(dst, src);
+        if constexpr (std::is_same<T, uint16_t>::value) {
+            if (emax) {
+                if (s != ps) {
+                    if (ps >= 0) atomicMax(&smax[ps], (int)pm);
+                    ps = s;
+                    pm = 0;
+                }
+                const uint4 w = *reinterpret_cast<const uint4 *>(src);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) pm = max(pm, max((w[k] >> 7) & 0xFFu, (w[k] >> 23) & 0xFFu));
+            }
+        }
     }
+    if (emax) {
+        if (ps >= 0) atomicMax(&smax[ps], (int)pm);
+        __syncthreads();
+        for (int s = threadIdx.x; s < d / ds; s += 256) atomicMax(&emax[(int64_t)s * B * H + bh], smax[s]);
+    }
+}
+
+// ---------------------------------------------------------------- PQ update from integer sums
+// The k-means update of 16-dim bf16 subspaces with at most kPqIntMaxC codewords
+// needs no sorted order: every row is added into its codeword's sum as an exact
+// integer.  A subspace whose largest exponent field is E holds values below
+// 2^(E-126); times 2^s, s = 126 - E + lim, each is below 2^lim and is rounded to
+// an integer (exact unless its exponent lies more than lim - 8 below E), and any
+// sum of N of them stays below 2^62 (lim = min(62 - ceil(log2(N+1)), 51); 51 keeps
+// the rounding trick below exact).  Integer sums do not depend on the order of
+// the additions, so work-groups add a chunk of tokens each in LDS with atomics,
+// and the result is the same on every run.  The mean, (sum * 2^-s) / n in fp64
+// rounded to fp32, equals the sorted fp64 sum's whenever that sum is exact.
+__host__ __device__ constexpr int pq_int_lim(int N)
+{
+    int L = 0;
+    while (L < 31 && (1LL << L) <= (long long)N) ++L;  // N < 2^L
+    return 62 - L < 51 ? 62 - L : 51;
+}
+
+__device__ __forceinline__ int pq_int_shift(int32_t e, int N) { return 126 - max(e, 1) + pq_int_lim(N); }
+
+// The chunk's sums in LDS ([codeword][17]: 16 dims and a pad word, so that the
+// atomics of one instruction spread over the banks) and counts; two lanes per
+// token, 8 dims each.  Then the chunk's partial, [C][16] int64 and [C] int32,
+// goes to acc.
+__global__ __launch_bounds__(256) void pq_accum16_kernel(const uint16_t *__restrict__ xc,
+                                                         const int32_t *__restrict__ labels, int N, int C,
+                                                         const int32_t *__restrict__ emax, int nchunk,
+                                                         size_t chunk_bytes, uint8_t *__restrict__ acc)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned long long lsum[];
+    unsigned *lcnt = reinterpret_cast<unsigned *>(lsum + C * kPqPitch);
+    const int pair = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x, hl = tid & 1;
+    for (int i = tid; i < C * kPqPitch; i += 256) lsum[i] = 0ull;
+    for (int i = tid; i < C; i += 256) lcnt[i] = 0u;
+    __syncthreads();
+    const double sc = ldexp(1.0, pq_int_shift(emax[pair], N));
+    const double magic = 6755399441055744.0;  // 1.5 * 2^52: adding it rounds |y| < 2^51 to an integer
+    const long long mbits = __double_as_longlong(magic);
+    const int t0 = chunk * kPqAccTok, t1 = min(N, t0 + kPqAccTok);
+    const uint16_t *xb = xc + (int64_t)pair * N * 16 + hl * 8;
+    const int32_t *lb = labels + (int64_t)pair * N;
+    constexpr int U = 4;  // tokens per lane in flight
+    for (int tb = t0 + (tid >> 1); tb < t1; tb += 128 * U) {
+        int lab[U];
+        uint4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int t = tb + u * 128;
+            lab[u] = t < t1 ? lb[t] : -1;
+            if (t < t1) w[u] = *reinterpret_cast<const uint4 *>(xb + (int64_t)t * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (lab[u] < 0) continue;
+            unsigned long long *row = lsum + lab[u] * kPqPitch + hl * 8;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float lo = __uint_as_float(w[u][k] << 16), hi = __uint_as_float(w[u][k] & 0xFFFF0000u);
+                const long long il = __double_as_longlong(fma((double)lo, sc, magic)) - mbits;
+                const long long ih = __double_as_longlong(fma((double)hi, sc, magic)) - mbits;
+                atomicAdd(row + 2 * k, (unsigned long long)il);
+                atomicAdd(row + 2 * k + 1, (unsigned long long)ih);
+            }
+            if (hl == 0) atomicAdd(lcnt + lab[u], 1u);
+        }
+    }
+    __syncthreads();
+    uint8_t *dst = acc + ((int64_t)pair * nchunk + chunk) * chunk_bytes;
+    unsigned long long *ds = reinterpret_cast<unsigned long long *>(dst);
+    for (int i = tid; i < C * 16; i += 256) ds[i] = lsum[(i >> 4) * kPqPitch + (i & 15)];
+    unsigned *dc = reinterpret_cast<unsigned *>(dst + (size_t)C * 16 * 8);
+    for (int i = tid; i < C; i += 256) dc[i] = lcnt[i];
+}
+
+// Adds the chunks' partials of one (subspace, batch, head) triple and divides:
+// one thread per (codeword, dim); an empty codeword keeps its value.
+__global__ __launch_bounds__(256) void pq_final16_kernel(const uint8_t *__restrict__ acc, int nchunk,
+                                                         size_t chunk_bytes, int N, int C,
+                                                         const int32_t *__restrict__ emax, float *__restrict__ cent)
+{
+    const int pair = blockIdx.y, k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= C * 16) return;
+    const int j = k >> 4;
+    long long S = 0;
+    long long n = 0;
+    for (int c = 0; c < nchunk; ++c) {
+        const uint8_t *src = acc + ((int64_t)pair * nchunk + c) * chunk_bytes;
+        S += reinterpret_cast<const long long *>(src)[k];
+        n += reinterpret_cast<const unsigned *>(src + (size_t)C * 16 * 8)[j];
+    }
+    if (n == 0) return;
+    const double sum = ldexp((double)S, -pq_int_shift(emax[pair], N));
+    cent[((int64_t)pair * C + j) * 16 + (k & 15)] = (float)(sum / (double)n);
 }
 
 template <typename T, int D>
@@ -1099,6 +1224,37 @@ isg_status run_cluster(hipStream_t st, const T *x, Strides xs, int B, int H, int
         gather_kernel<T, D><<<grid, 256, 0, st>>>(x, xs, comp, H, N, perm, nullptr, comp_perm, total);
     }
     return isg_check_launch("isg_cluster");
+}
+
+// Lloyd rounds of 16-dim bf16 subspaces with at most kPqIntMaxC codewords on the
+// dense subspace-major copy (PB = P*B batches): run_cluster's init and assign,
+// then the integer-sum update; no sorted order is built (the codes are the last
+// round's labels and the codebooks the means of those groups, as there).
+isg_status run_pq16(hipStream_t st, const uint16_t *xc, int PB, int H, int N, int C, int iters,
+                    const int32_t *emax, float *cent, int32_t *labels, uint8_t *acc, size_t chunk_bytes,
+                    uint8_t *ws)
+{
+    const int pairs = PB * H;
+    const Strides cs{(int64_t)H * N * 16, (int64_t)N * 16, 16};
+    const ClusterWs w = cluster_ws(PB, H, N, 16, C);
+    const int nchunk = (N + kPqAccTok - 1) / kPqAccTok;
+    const int64_t total = (int64_t)pairs * C * 16;
+    init_centroids_kernel<uint16_t><<<(int)std::min<int64_t>((total + 255) / 256, 65536), 256, 0, st>>>(
+        xc, cs, H, N, C, 16, cent, total);
+    const size_t lds = (size_t)C * kPqPitch * sizeof(unsigned long long) + (size_t)C * sizeof(unsigned);
+    for (int it = 0; it < iters; ++it) {
+        launch_assign<uint16_t, 16>(st, xc, cs, PB, H, N, C, cent, labels, ws, w);
+        pq_accum16_kernel<<<dim3(nchunk, pairs), 256, lds, st>>>(xc, labels, N, C, emax, nchunk, chunk_bytes, acc);
+        pq_final16_kernel<<<dim3((C * 16 + 255) / 256, pairs), 256, 0, st>>>(acc, nchunk, chunk_bytes, N, C, emax,
+                                                                            cent);
+    }
+    return isg_check_launch("isg_pq_codebooks");
+}
+
+__global__ void pq_zero_i32_kernel(int32_t *p, int n)
+{
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
 }
 
 template <typename T>
@@ -1269,8 +1425,15 @@ extern "C" isg_status isg_cluster_noalloc(void *stream, const void *x, isg_dtype
 // ---------------------------------------------------------------- product-quantisation codebooks
 namespace {
 
+// The integer-sum update serves bf16 16-dim subspaces with at most kPqIntMaxC
+// codewords (its LDS sums grow with Cc); anything else runs isg_cluster's rounds.
+bool pq_int_path(isg_dtype dt, int d, int P, int Cc)
+{
+    return dt == ISG_BF16 && d / P == 16 && P <= kPqMaxP && Cc <= kPqIntMaxC;
+}
+
 struct PqWs {
-    size_t off_copy, off_perm, off_offsets, off_cluster, total;
+    size_t off_copy, off_perm, off_offsets, off_emax, off_acc, chunk_bytes, off_cluster, total;
 };
 
 PqWs pq_ws(isg_dtype dt, int B, int H, int N, int d, int P, int Cc)
@@ -1278,11 +1441,17 @@ PqWs pq_ws(isg_dtype dt, int B, int H, int N, int d, int P, int Cc)
     const int ds = d / P;
     const size_t esz = dt == ISG_F32 ? sizeof(float) : sizeof(uint16_t);
     const size_t rows = (size_t)P * B * H * N;
+    const size_t pairs = (size_t)P * B * H;
+    const bool ip = pq_int_path(dt, d, P, Cc);
     PqWs w;
     size_t o = 0;
     w.off_copy = o; o += isg_align256(rows * ds * esz);
-    w.off_perm = o; o += isg_align256(rows * sizeof(int32_t));
-    w.off_offsets = o; o += isg_align256((size_t)P * B * H * (Cc + 1) * sizeof(int32_t));
+    w.off_perm = o; o += ip ? 0 : isg_align256(rows * sizeof(int32_t));
+    w.off_offsets = o; o += ip ? 0 : isg_align256(pairs * (Cc + 1) * sizeof(int32_t));
+    w.off_emax = o; o += ip ? isg_align256(pairs * sizeof(int32_t)) : 0;
+    // per (triple, chunk of kPqAccTok tokens): Cc*16 int64 sums, then Cc int32 counts
+    w.chunk_bytes = isg_align256((size_t)Cc * 16 * sizeof(int64_t) + (size_t)Cc * sizeof(int32_t));
+    w.off_acc = o; o += ip ? pairs * (size_t)((N + kPqAccTok - 1) / kPqAccTok) * w.chunk_bytes : 0;
     w.off_cluster = o; o += cluster_ws(P * B, H, N, ds, Cc).total;
     w.total = o;
     return w;
@@ -1327,11 +1496,22 @@ extern "C" isg_status isg_pq_codebooks(void *stream, const void *x, isg_dtype dt
     uint8_t *ws = (uint8_t *)workspace;
     const Strides xs{x_strides[0], x_strides[1], x_strides[2]};
     const dim3 grid((N + 63) / 64, B * H);
+    if (pq_int_path(dt, d, P, Cc)) {
+        // subspace s of batch b is batch s*B + b of the rounds on the dense copy
+        const int pairs = P * B * H;
+        int32_t *emax = (int32_t *)(ws + w.off_emax);
+        pq_zero_i32_kernel<<<(pairs + 255) / 256, 256, 0, st>>>(emax, pairs);
+        pq_split_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t *)x, xs, B, H, N, d, ds,
+                                                        (uint16_t *)(ws + w.off_copy), emax);
+        return run_pq16(st, (const uint16_t *)(ws + w.off_copy), P * B, H, N, Cc, iters, emax, codebooks, codes,
+                        ws + w.off_acc, w.chunk_bytes, ws + w.off_cluster);
+    }
     if (dt == ISG_F32)
-        pq_split_kernel<float><<<grid, 256, 0, st>>>((const float *)x, xs, B, H, N, d, ds, (float *)(ws + w.off_copy));
+        pq_split_kernel<float><<<grid, 256, 0, st>>>((const float *)x, xs, B, H, N, d, ds, (float *)(ws + w.off_copy),
+                                                     nullptr);
     else
         pq_split_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t *)x, xs, B, H, N, d, ds,
-                                                        (uint16_t *)(ws + w.off_copy));
+                                                        (uint16_t *)(ws + w.off_copy), nullptr);
     // subspace s of batch b is batch s*B + b of one clustering call on the dense copy
     const int64_t cs[3] = {(int64_t)H * N * ds, (int64_t)N * ds, ds};
     return run_checked(st, ws + w.off_copy, dt, cs, P * B, H, N, ds, Cc, iters, 0, nullptr, codebooks, codes,

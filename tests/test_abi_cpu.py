@@ -250,15 +250,21 @@ def test_pq_codebooks_rejects(kw, status):
     assert len(isg.lib().isg_last_error()) > 0
 
 
-def test_pq_codebooks_workspace_holds_the_copy_and_the_clustering():
+def test_pq_codebooks_workspace_holds_every_region():
     L = isg.lib()
     B, H, N, d, P, Cc = 1, 40, 75600, 128, 8, 256
     bf = L.isg_pq_codebooks_workspace_size(1, B, H, N, d, P, Cc)
     f32 = L.isg_pq_codebooks_workspace_size(0, B, H, N, d, P, Cc)
     cl = L.isg_cluster_workspace_size(P * B, H, N, d // P, Cc)
-    copy_bf = B * H * N * d * 2
-    assert bf >= cl + copy_bf + P * B * H * N * 4
-    assert f32 - bf >= B * H * N * d * 2 - 256
+    # bf16 16-dim subspaces: the copy, the clustering's own workspace and, per
+    # (subspace, head) and chunk of 8192 tokens, Cc*16 int64 sums and Cc counts
+    chunks = P * B * H * -(-N // 8192)
+    assert bf >= cl + B * H * N * d * 2 + chunks * (Cc * 16 * 8 + Cc * 4)
+    # fp32: the copy, the clustering's workspace, the permutation and offsets
+    assert f32 >= cl + B * H * N * d * 4 + P * B * H * (N + Cc + 1) * 4
+    # more than 256 codewords: the sorted update, as for fp32
+    big = L.isg_pq_codebooks_workspace_size(1, B, H, N, d, P, 300)
+    assert big >= L.isg_cluster_workspace_size(P * B, H, N, d // P, 300) + B * H * N * d * 2 + P * B * H * N * 4
     for bad in [(1, B, H, N, d, 3, Cc), (1, B, H, N, d, P, 0), (7, B, H, N, d, P, Cc), (1, 0, H, N, d, P, Cc)]:
         assert L.isg_pq_codebooks_workspace_size(*bad) == 0
 

@@ -946,12 +946,15 @@ def test_pq_votes_all_scores_tied(orc):
 
 
 @pytest.mark.parametrize("B,dtype,P,Cc", [(1, "bf16", 8, 64), (2, "bf16", 8, 256), (1, "f32", 2, 40),
-                                           (2, "bf16", 1, 16)])
+                                           (2, "bf16", 1, 16), (1, "bf16", 8, 300)])
 def test_pq_codebooks_strided_and_vs_oracle(orc, B, dtype, P, Cc):
-    """isg_pq_codebooks (subspace-major copy, then one clustering run over every
-    subspace, batch and head) equals isg_cluster on each subspace alone, bit for
-    bit, through a strided view of the input; agreement with the oracle's own
-    k-means of each subspace is reported and bounded."""
+    """isg_pq_codebooks (subspace-major copy, then the rounds over every subspace,
+    batch and head at once) equals isg_cluster on each subspace alone, bit for
+    bit, through a strided view of the input.  For bf16 16-dim subspaces with at
+    most 256 codewords the means come from exact integer sums, isg_cluster's from
+    fp64 sums in sorted order: on these inputs both sums are exact, so the two
+    agree bit for bit.  Agreement with the oracle's own k-means of each subspace
+    is reported and bounded."""
     H, N, d = 2, 3000, 128
     say(f"pq codebooks B={B} {dtype} P={P} Cc={Cc}")
     xs = [_inputs(H, N, d, dtype, seed=21 + b)[0] for b in range(B)]
@@ -969,6 +972,49 @@ def test_pq_codebooks_strided_and_vs_oracle(orc, B, dtype, P, Cc):
     agree = (oc == npy(codes)).mean()
     say(f"  PQ code agreement with the oracle's own k-means: {agree:.5f}")
     assert agree > 0.97
+
+
+@pytest.mark.parametrize("N,Cc", [(700, 256), (3000, 64), (20000, 200)])
+def test_pq_codebooks_integer_means_wide_span(N, Cc):
+    """The integer-sum update of bf16 16-dim subspaces on values spread over 2^60
+    (each element times 2^u, u uniform in [-60, 0]): the fixed-point grid then
+    drops the low bits of the smallest values, so the means are checked against
+    the exact mean of each group (math.fsum, fp64), within one fp32 ulp plus the
+    grid's bound, with the labels of one round (from the data-point start, the
+    same assign as isg_cluster) equal to isg_cluster's.  Two calls agree bit for
+    bit: integer sums do not depend on the order of the atomics."""
+    say(f"pq integer means wide span N={N} Cc={Cc}")
+    H, d, P = 2, 64, 4
+    g = np.random.default_rng(N + Cc)
+    x = g.standard_normal((1, H, N, d)) * np.exp2(g.uniform(-60, 0, (1, H, N, d)))
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    xg = xb.to(DEV)
+    codes, cbs = isg.pq_codebooks(xg, P, Cc, 1)
+    codes2, cbs2 = isg.pq_codebooks(xg, P, Cc, 1)
+    assert torch.equal(codes, codes2) and torch.equal(cbs, cbs2)
+    xv = xb.to(torch.float64).numpy()
+    L = 0
+    while (1 << L) <= N:
+        L += 1
+    lim = min(62 - L, 51)
+    c_np, cb_np = npy(codes), npy(cbs)
+    for s in range(P):
+        sub = xg[..., s * 16:(s + 1) * 16]
+        r = isg.isg_cluster(sub.contiguous(), Cc, 1)
+        assert torch.equal(r["labels"], codes[s]), s
+        for h in range(H):
+            xs = xv[0, h, :, s * 16:(s + 1) * 16]
+            bits = xb[0, h, :, s * 16:(s + 1) * 16].contiguous().view(torch.int16).numpy().astype(np.int64)
+            E = max(int(((bits >> 7) & 0xFF).max()), 1)
+            grid = 2.0 ** -(126 - E + lim)
+            lab = c_np[s, 0, h]
+            for j in np.unique(lab):
+                rows = xs[lab == j]
+                n = len(rows)
+                exact = np.array([math.fsum(rows[:, e]) / n for e in range(16)])
+                got = cb_np[s, 0, h, j].astype(np.float64)
+                ulp = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64)
+                assert np.all(np.abs(got - exact) <= ulp + grid * (n / 2 + 1) / n), (s, h, j)
 
 
 def test_pipeline_votes_mode_vs_oracle(orc):
