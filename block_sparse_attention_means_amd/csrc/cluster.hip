@@ -1038,12 +1038,13 @@ void launch_assign(hipStream_t st, const T *x, Strides xs, int B, int H, int N, 
 // out[s][b][h][t][e].  A work-group moves 64 tokens: it reads their rows whole
 // (coalesced) and writes P runs of 64*ds contiguous elements, so each subspace's
 // k-means then reads dense ds-element rows instead of ds-element pieces of longer
-// rows (a 32-byte piece costs a 128-byte line fetch).  With emax non-null (bf16,
-// ds = 16) it also raises emax[s*B*H + bh] to the largest exponent field among
-// the subspace's values (sign dropped), which the integer update scales by.
+// rows (a 32-byte piece costs a 128-byte line fetch).  With wmax non-null (bf16)
+// it also writes, per subspace, the largest exponent field among the work-group's
+// values (sign dropped) to wmax[(s*B*H + bh) * gridDim.x + blockIdx.x]; the
+// integer update scales by the maximum of these over a subspace.
 template <typename T>
 __global__ __launch_bounds__(256) void pq_split_kernel(const T *x, Strides xs, int B, int H, int N, int d, int ds,
-                                                       T *out, int32_t *emax)
+                                                       T *out, int32_t *wmax)
 {
     __shared__ int smax[kPqMaxP];
     const int cpr = d / 8;  // 8-element chunks per row
@@ -1051,36 +1052,53 @@ __global__ __launch_bounds__(256) void pq_split_kernel(const T *x, Strides xs, i
     const int t0 = blockIdx.x * 64;
     const int nt = min(64, N - t0);
     const int64_t plane = (int64_t)B * H * N * ds;
-    if (emax) {
+    if (wmax) {
         for (int s = threadIdx.x; s < d / ds; s += 256) smax[s] = 0;
         __syncthreads();
     }
-    int ps = -1;   // this thread's subspace so far and its largest exponent field
+    int ps = -1;  // this thread's subspace so far and its largest exponent field
     uint32_t pm = 0;
     for (int q = threadIdx.x; q < nt * cpr; q += 256) {
         const int tt = q / cpr, c = q % cpr;
         const int s = (c * 8) / ds, e0 = (c * 8) % ds;
         const T *src = x + b * xs.b + h * xs.h + (int64_t)(t0 + tt) * xs.t + c * 8;
         T *dst = out + s * plane + ((int64_t)bh * N + t0 + tt) * ds + e0;
-        copy8(dst, src);
         if constexpr (std::is_same<T, uint16_t>::value) {
-            if (emax) {
+            const uint4 w = *reinterpret_cast<const uint4 *>(src);
+            *reinterpret_cast<uint4 *>(dst) = w;
+            if (wmax) {
                 if (s != ps) {
                     if (ps >= 0) atomicMax(&smax[ps], (int)pm);
                     ps = s;
                     pm = 0;
                 }
-                const uint4 w = *reinterpret_cast<const uint4 *>(src);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) pm = max(pm, max((w[k] >> 7) & 0xFFu, (w[k] >> 23) & 0xFFu));
             }
+        } else {
+            copy8(dst, src);
         }
     }
-    if (emax) {
+    if (wmax) {
         if (ps >= 0) atomicMax(&smax[ps], (int)pm);
         __syncthreads();
-        for (int s = threadIdx.x; s < d / ds; s += 256) atomicMax(&emax[(int64_t)s * B * H + bh], smax[s]);
+        for (int s = threadIdx.x; s < d / ds; s += 256)
+            wmax[((int64_t)s * B * H + bh) * gridDim.x + blockIdx.x] = smax[s];
     }
+}
+
+// emax[p] = the largest of the split's per-work-group exponent fields of triple p.
+__global__ __launch_bounds__(256) void pq_emax_kernel(const int32_t *wmax, int nwg, int32_t *emax)
+{
+    __shared__ int part[4];
+    const int p = blockIdx.x;
+    int m = 0;
+    for (int i = threadIdx.x; i < nwg; i += 256) m = max(m, wmax[(int64_t)p * nwg + i]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) emax[p] = max(max(part[0], part[1]), max(part[2], part[3]));
 }
 
 // ---------------------------------------------------------------- PQ update from integer sums
@@ -1249,12 +1267,6 @@ isg_status run_pq16(hipStream_t st, const uint16_t *xc, int PB, int H, int N, in
                                                                             cent);
     }
     return isg_check_launch("isg_pq_codebooks");
-}
-
-__global__ void pq_zero_i32_kernel(int32_t *p, int n)
-{
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) p[i] = 0;
 }
 
 template <typename T>
@@ -1433,7 +1445,7 @@ bool pq_int_path(isg_dtype dt, int d, int P, int Cc)
 }
 
 struct PqWs {
-    size_t off_copy, off_perm, off_offsets, off_emax, off_acc, chunk_bytes, off_cluster, total;
+    size_t off_copy, off_perm, off_offsets, off_emax, off_wmax, off_acc, chunk_bytes, off_cluster, total;
 };
 
 PqWs pq_ws(isg_dtype dt, int B, int H, int N, int d, int P, int Cc)
@@ -1449,6 +1461,8 @@ PqWs pq_ws(isg_dtype dt, int B, int H, int N, int d, int P, int Cc)
     w.off_perm = o; o += ip ? 0 : isg_align256(rows * sizeof(int32_t));
     w.off_offsets = o; o += ip ? 0 : isg_align256(pairs * (Cc + 1) * sizeof(int32_t));
     w.off_emax = o; o += ip ? isg_align256(pairs * sizeof(int32_t)) : 0;
+    // the split's exponent field per (triple, work-group of 64 tokens)
+    w.off_wmax = o; o += ip ? isg_align256(pairs * (size_t)((N + 63) / 64) * sizeof(int32_t)) : 0;
     // per (triple, chunk of kPqAccTok tokens): Cc*16 int64 sums, then Cc int32 counts
     w.chunk_bytes = isg_align256((size_t)Cc * 16 * sizeof(int64_t) + (size_t)Cc * sizeof(int32_t));
     w.off_acc = o; o += ip ? pairs * (size_t)((N + kPqAccTok - 1) / kPqAccTok) * w.chunk_bytes : 0;
@@ -1499,10 +1513,10 @@ extern "C" isg_status isg_pq_codebooks(void *stream, const void *x, isg_dtype dt
     if (pq_int_path(dt, d, P, Cc)) {
         // subspace s of batch b is batch s*B + b of the rounds on the dense copy
         const int pairs = P * B * H;
-        int32_t *emax = (int32_t *)(ws + w.off_emax);
-        pq_zero_i32_kernel<<<(pairs + 255) / 256, 256, 0, st>>>(emax, pairs);
+        int32_t *emax = (int32_t *)(ws + w.off_emax), *wmax = (int32_t *)(ws + w.off_wmax);
         pq_split_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t *)x, xs, B, H, N, d, ds,
-                                                        (uint16_t *)(ws + w.off_copy), emax);
+                                                        (uint16_t *)(ws + w.off_copy), wmax);
+        pq_emax_kernel<<<pairs, 256, 0, st>>>(wmax, (int)grid.x, emax);
         return run_pq16(st, (const uint16_t *)(ws + w.off_copy), P * B, H, N, Cc, iters, emax, codebooks, codes,
                         ws + w.off_acc, w.chunk_bytes, ws + w.off_cluster);
     }
