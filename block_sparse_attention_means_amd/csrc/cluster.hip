@@ -21,6 +21,7 @@ constexpr int kMaxLabelBits = 12;
 constexpr int kPqMaxP = 64;       // subspaces per row the split kernel tracks exponents for
 constexpr int kPqIntMaxC = 256;   // codewords up to which the PQ update sums integers in LDS
 constexpr int kPqAccTok = 8192;   // tokens per work-group of that update
+constexpr int kPqAccThreads = 256; // its threads (two per token)
 constexpr int kPqPitch = 17;      // int64 words per codeword in its LDS sums (16 dims + 1)  // labels below kMaxC
 constexpr int kAssignTile = 32;   // centroids per LDS tile in the assign kernel
 // Rows per piece of the centroid update: 16 rows for each of the work-group's row
@@ -674,6 +675,35 @@ __device__ __forceinline__ double seg_sqdist(const uint16_t *xr, const float *cr
     return part;
 }
 
+// |x - c|^2 over 16 dims in fp64: the terms in the order k = 0..15, each squared
+// difference rounded before it is added (no fused multiply-add), as in the exact
+// definition (x bf16, c fp32; 16-byte aligned).
+__device__ __forceinline__ double seq_sqdist16(const uint16_t *xr, const float *cr)
+{
+#pragma clang fp contract(off)
+    double s = 0.0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(xr + 8 * h);
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cr + 8 * h);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cr + 8 * h + 4);
+        float xv[8], cv[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            xv[2 * q] = __uint_as_float(w[q] << 16);
+            xv[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+            cv[q] = c0[q];
+            cv[4 + q] = c1[q];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const double a = (double)xv[e] - (double)cv[e];
+            s += a * a;
+        }
+    }
+    return s;
+}
+
 __device__ __forceinline__ double sum16(double v)
 {
     v += __shfl_xor(v, 8);
@@ -879,10 +909,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6
                 if (top[tb].k[c] != 0xFFFFFFFFu) top[tb].k[c] += 4u;
     }
 
-    // Decisions.  Close calls go to a work list: 16 lanes per (token, candidate)
-    // entry evaluate |x - c|^2 in fp64 and the token takes the smallest (ties to
-    // the lower index).  A token whose kept candidates are all within tau is rescanned in
-    // fp64 over all C, again 16 lanes per candidate.
+    // Decisions.  Close calls go to a work list of (token, candidate) entries whose
+    // |x - c|^2 is evaluated in fp64, and the token takes the smallest (ties to the
+    // lower index).  A token whose kept candidates are all within tau is rescanned
+    // in fp64 over all C.  At D = 16 one lane takes a whole entry (or centroid of a
+    // rescan) and sums in the exact definition's order and rounding; wider rows
+    // spread an entry over 16 lanes (a fused fp64 chain per lane, then a butterfly),
+    // which keeps the few entries of a work-group short.
     constexpr int kRQ = 3 * 256;
     constexpr int DPL = D / 16;  // dims per lane
     __shared__ int rq_n, full_n;
@@ -933,6 +966,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6
         }
     }
     __syncthreads();
+    if constexpr (D == 16) {
+        const int nq = rq_n;
+        for (int e = tid; e < nq; e += 256) {
+            const int t = blockIdx.x * 256 + rq_slot[e];
+            rq_dist[e] = seq_sqdist16(xb + (int64_t)t * xs.t, cb + (int64_t)rq_cand[e] * 16);
+        }
+        const int nf = full_n;
+        for (int f = 0; f < nf; ++f) {
+            const int t = blockIdx.x * 256 + full_slot[f];
+            const uint16_t *xr = xb + (int64_t)t * xs.t;
+            double bd = INFINITY;
+            int bj = 0;
+            for (int j = tid; j < C; j += 256) {
+                const double dd = seq_sqdist16(xr, cb + (int64_t)j * 16);
+                if (dd < bd) { bd = dd; bj = j; }
+            }
+            // smallest distance, ties to the lower index: over the wave, then the waves
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const double od = __shfl_xor(bd, off);
+                const int oj = __shfl_xor(bj, off);
+                if (od < bd || (od == bd && oj < bj)) { bd = od; bj = oj; }
+            }
+            if (lane == 0) { grp_d[wave] = bd; grp_j[wave] = bj; }
+            __syncthreads();
+            if (tid == 0) {
+                double b = grp_d[0];
+                int jb = grp_j[0];
+                for (int g = 1; g < 4; ++g)
+                    if (grp_d[g] < b || (grp_d[g] == b && grp_j[g] < jb)) { b = grp_d[g]; jb = grp_j[g]; }
+                full_best[f] = jb;
+            }
+            __syncthreads();
+        }
+    } else {
     const int sub = tid & 15, grp = tid >> 4;
     {
         const int nq = rq_n;
@@ -963,6 +1031,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6
             full_best[f] = jb;
         }
         __syncthreads();
+    }
     }
     __syncthreads();
 #pragma unroll
@@ -1125,7 +1194,7 @@ __device__ __forceinline__ int pq_int_shift(int32_t e, int N) { return 126 - max
 // atomics of one instruction spread over the banks) and counts; two lanes per
 // token, 8 dims each.  Then the chunk's partial, [C][16] int64 and [C] int32,
 // goes to acc.
-__global__ __launch_bounds__(256) void pq_accum16_kernel(const uint16_t *__restrict__ xc,
+__global__ __launch_bounds__(kPqAccThreads) void pq_accum16_kernel(const uint16_t *__restrict__ xc,
                                                          const int32_t *__restrict__ labels, int N, int C,
                                                          const int32_t *__restrict__ emax, int nchunk,
                                                          size_t chunk_bytes, uint8_t *__restrict__ acc)
@@ -1133,8 +1202,8 @@ __global__ __launch_bounds__(256) void pq_accum16_kernel(const uint16_t *__restr
     extern __shared__ __attribute__((aligned(16))) unsigned long long lsum[];
     unsigned *lcnt = reinterpret_cast<unsigned *>(lsum + C * kPqPitch);
     const int pair = blockIdx.y, chunk = blockIdx.x, tid = threadIdx.x, hl = tid & 1;
-    for (int i = tid; i < C * kPqPitch; i += 256) lsum[i] = 0ull;
-    for (int i = tid; i < C; i += 256) lcnt[i] = 0u;
+    for (int i = tid; i < C * kPqPitch; i += kPqAccThreads) lsum[i] = 0ull;
+    for (int i = tid; i < C; i += kPqAccThreads) lcnt[i] = 0u;
     __syncthreads();
     const double sc = ldexp(1.0, pq_int_shift(emax[pair], N));
     const double magic = 6755399441055744.0;  // 1.5 * 2^52: adding it rounds |y| < 2^51 to an integer
@@ -1143,12 +1212,12 @@ __global__ __launch_bounds__(256) void pq_accum16_kernel(const uint16_t *__restr
     const uint16_t *xb = xc + (int64_t)pair * N * 16 + hl * 8;
     const int32_t *lb = labels + (int64_t)pair * N;
     constexpr int U = 4;  // tokens per lane in flight
-    for (int tb = t0 + (tid >> 1); tb < t1; tb += 128 * U) {
+    for (int tb = t0 + (tid >> 1); tb < t1; tb += kPqAccThreads / 2 * U) {
         int lab[U];
         uint4 w[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int t = tb + u * 128;
+            const int t = tb + u * (kPqAccThreads / 2);
             lab[u] = t < t1 ? lb[t] : -1;
             if (t < t1) w[u] = *reinterpret_cast<const uint4 *>(xb + (int64_t)t * 16);
         }
@@ -1170,9 +1239,9 @@ __global__ __launch_bounds__(256) void pq_accum16_kernel(const uint16_t *__restr
     __syncthreads();
     uint8_t *dst = acc + ((int64_t)pair * nchunk + chunk) * chunk_bytes;
     unsigned long long *ds = reinterpret_cast<unsigned long long *>(dst);
-    for (int i = tid; i < C * 16; i += 256) ds[i] = lsum[(i >> 4) * kPqPitch + (i & 15)];
+    for (int i = tid; i < C * 16; i += kPqAccThreads) ds[i] = lsum[(i >> 4) * kPqPitch + (i & 15)];
     unsigned *dc = reinterpret_cast<unsigned *>(dst + (size_t)C * 16 * 8);
-    for (int i = tid; i < C; i += 256) dc[i] = lcnt[i];
+    for (int i = tid; i < C; i += kPqAccThreads) dc[i] = lcnt[i];
 }
 
 // Adds the chunks' partials of one (subspace, batch, head) triple and divides:
@@ -1262,7 +1331,7 @@ isg_status run_pq16(hipStream_t st, const uint16_t *xc, int PB, int H, int N, in
     const size_t lds = (size_t)C * kPqPitch * sizeof(unsigned long long) + (size_t)C * sizeof(unsigned);
     for (int it = 0; it < iters; ++it) {
         launch_assign<uint16_t, 16>(st, xc, cs, PB, H, N, C, cent, labels, ws, w);
-        pq_accum16_kernel<<<dim3(nchunk, pairs), 256, lds, st>>>(xc, labels, N, C, emax, nchunk, chunk_bytes, acc);
+        pq_accum16_kernel<<<dim3(nchunk, pairs), kPqAccThreads, lds, st>>>(xc, labels, N, C, emax, nchunk, chunk_bytes, acc);
         pq_final16_kernel<<<dim3((C * 16 + 255) / 256, pairs), 256, 0, st>>>(acc, nchunk, chunk_bytes, N, C, emax,
                                                                             cent);
     }

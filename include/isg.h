@@ -277,11 +277,21 @@ isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, cons
  * quantised).  The pages do not say how the codebooks are trained; the reading
  * taken: subspace s of x (dims [s*ds, (s+1)*ds), ds = d/P) is clustered by the
  * same k-means as isg_cluster (init_mode 0, iters rounds, Cc centroids), its
- * centroids are the subspace-s codebook and its labels the codes.  The result is
- * the one isg_cluster gives on each subspace (a strided view) alone: the call
- * first copies x into subspace-major order in the workspace, so every subspace's
- * rows are dense, then clusters all P*B*H (subspace, batch, head) triples in one
- * run.
+ * centroids are the subspace-s codebook and its labels the codes.  The call first
+ * copies x into subspace-major order in the workspace, so every subspace's rows
+ * are dense, then runs the rounds for all P*B*H (subspace, batch, head) triples at
+ * once.  The labels of each round are isg_cluster's on that subspace alone.  The
+ * means: for bf16 x with d/P = 16 and Cc <= 256 each codeword's rows are added as
+ * exact integers: a fixed point of 2^-s per triple, s set by the triple's largest
+ * exponent so that each value is below 2^lim and N of them below 2^62
+ * (lim = min(62 - ceil(log2(N+1)), 51), 45 at N = 75,600); values whose exponent
+ * lies more than lim - 8 below the largest are rounded to that grid.  The result
+ * then does not depend on the order of the additions; the mean is that sum over
+ * the count in fp64, rounded to fp32.  It equals isg_cluster's fp64 mean whenever
+ * both sums are exact (a group's values spanning fewer than 45 - log2(N) binary
+ * orders, 28 at N = 75,600, for isg_cluster's) and is otherwise within the grid's
+ * rounding of the exact mean.  Other cases run isg_cluster's rounds and give its
+ * result on each subspace alone.
  *
  * x          device, dt (ISG_BF16 or ISG_F32), element (b,h,t,k) at
  *            b*x_strides[0] + h*x_strides[1] + t*x_strides[2] + k (strides in
@@ -289,9 +299,10 @@ isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, cons
  * codes      device int32 [P,B,H,N] (written): the code of token t in subspace s;
  * codebooks  device fp32 [P,B,H,Cc,ds] (written);
  * workspace  device, >= isg_pq_codebooks_workspace_size(dt, B, H, N, d, P, Cc)
- *            bytes (the subspace-major copy, the clustering's permutation and
- *            offsets, and isg_cluster's own workspace); caller-owned, no state
- *            kept between calls.
+ *            bytes (the subspace-major copy, isg_cluster's own workspace, and
+ *            either the integer sums per chunk of 8192 tokens or the sorted
+ *            update's permutation and offsets); caller-owned, no state kept
+ *            between calls.
  * Needs P | d, d/P in {16, 64, 128}, P*B*H <= 65535, 1 <= Cc <= min(N, 4096),
  * iters >= 1; else ISG_E_ARG / ISG_E_UNSUPPORTED / ISG_E_DTYPE / ISG_E_WORKSPACE
  * with nothing launched. */
