@@ -95,11 +95,13 @@ void isg_proposal_table(uint32_t out[256]);
  * (bf16 hi/lo centroid planes on the matrix cores) and the four best are kept
  * (three at d = 16); whenever other kept candidates lie within the screening
  * error bound of the best, it is re-decided on fp64 distances among them, or
- * over all C when all kept candidates are that close.  For fp32 x the argmin is taken on fp32 distances
- * (sequential fused sums) and stands unless the runner-up lies within 4e-5
- * relative of the best; then every centroid is re-compared in fp64.  Either way
- * a label differs from the fp64 argmin only at fp64-level ties (the re-decisions
- * sum in another order than a plain sequential fp64 sum).
+ * over all C when all kept candidates are that close.  At d = 16 these fp64
+ * distances are sequential unfused sums over k = 0..15, so the labels are the
+ * fp64 argmin of the definition exactly; at larger d they sum per-lane pieces in
+ * another order.  For fp32 x the argmin is taken on fp32 distances (sequential
+ * fused sums) and stands unless the runner-up lies within 4e-5 relative of the
+ * best; then every centroid is re-compared in fp64.  Outside bf16 at d = 16 a
+ * label differs from the fp64 argmin only at fp64-level ties.
  *
  * x           device, dtype dt, element (b,h,t,k) at x[b*xs[0] + h*xs[1] + t*xs[2] + k]
  *             (xs = x_strides, in elements; k contiguous).  [B,N,H,d] and
