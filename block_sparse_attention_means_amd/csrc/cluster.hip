@@ -17,12 +17,12 @@ namespace {
 
 constexpr int kSortChunk = 1024;  // tokens per histogram / scatter chunk
 constexpr int kMaxC = 4096;
-constexpr int kMaxLabelBits = 12;
-constexpr int kPqMaxP = 64;       // subspaces per row the split kernel tracks exponents for
-constexpr int kPqIntMaxC = 256;   // codewords up to which the PQ update sums integers in LDS
-constexpr int kPqAccTok = 8192;   // tokens per work-group of that update
+constexpr int kMaxLabelBits = 12;  // labels below kMaxC
+constexpr int kPqMaxP = 64;        // subspaces per row the split kernel tracks exponents for
+constexpr int kPqIntMaxC = 256;    // codewords up to which the PQ update sums integers in LDS
+constexpr int kPqAccTok = 8192;    // tokens per work-group of that update
 constexpr int kPqAccThreads = 256; // its threads (two per token)
-constexpr int kPqPitch = 17;      // int64 words per codeword in its LDS sums (16 dims + 1)  // labels below kMaxC
+constexpr int kPqPitch = 17;       // int64 words per codeword in its LDS sums (16 dims + 1)
 constexpr int kAssignTile = 32;   // centroids per LDS tile in the assign kernel
 // Rows per piece of the centroid update: 16 rows for each of the work-group's row
 // slots (256 threads, d/8 per row), so 256 at d = 128 and 2048 at d = 16.
