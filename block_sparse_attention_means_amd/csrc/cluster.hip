@@ -636,15 +636,18 @@ template <int D>
 constexpr int topk_of() { return D == 16 ? 3 : 4; }
 
 // fp64 partial sum of (x_k - c_k)^2 over the DPL dims of one lane (x bf16, c fp32;
-// both 8/16-byte aligned at these offsets).
+// 16-byte aligned; DPL a multiple of 8), one fused chain in the order of k.
 template <int DPL>
 __device__ __forceinline__ double seg_sqdist(const uint16_t *xr, const float *cr)
 {
-    float xv[DPL], cv[DPL];
-    if constexpr (DPL == 8) {
-        const u32x4 w = *reinterpret_cast<const u32x4 *>(xr);
-        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cr);
-        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cr + 4);
+    static_assert(DPL % 8 == 0, "whole 16-byte chunks of x");
+    double part = 0.0;
+#pragma unroll
+    for (int k0 = 0; k0 < DPL; k0 += 8) {
+        const u32x4 w = *reinterpret_cast<const u32x4 *>(xr + k0);
+        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cr + k0);
+        const f32x4 c1 = *reinterpret_cast<const f32x4 *>(cr + k0 + 4);
+        float xv[8], cv[8];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             xv[2 * q] = __uint_as_float(w[q] << 16);
@@ -652,25 +655,11 @@ __device__ __forceinline__ double seg_sqdist(const uint16_t *xr, const float *cr
             cv[q] = c0[q];
             cv[4 + q] = c1[q];
         }
-    } else if constexpr (DPL == 4) {
-        const u32x2 w = *reinterpret_cast<const u32x2 *>(xr);
-        const f32x4 c0 = *reinterpret_cast<const f32x4 *>(cr);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            xv[2 * q] = __uint_as_float(w[q] << 16);
-            xv[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        for (int q = 0; q < 8; ++q) {
+            const double a = (double)xv[q] - (double)cv[q];
+            part = fma(a, a, part);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cv[q] = c0[q];
-    } else {
-#pragma unroll
-        for (int q = 0; q < DPL; ++q) { xv[q] = bf16_bits_to_f32(xr[q]); cv[q] = cr[q]; }
-    }
-    double part = 0.0;
-#pragma unroll
-    for (int q = 0; q < DPL; ++q) {
-        const double a = (double)xv[q] - (double)cv[q];
-        part = fma(a, a, part);
     }
     return part;
 }
@@ -704,10 +693,9 @@ __device__ __forceinline__ double seq_sqdist16(const uint16_t *xr, const float *
     return s;
 }
 
-__device__ __forceinline__ double sum16(double v)
+// the sum over the 4 lanes of an aligned group
+__device__ __forceinline__ double sum4(double v)
 {
-    v += __shfl_xor(v, 8);
-    v += __shfl_xor(v, 4);
     v += __shfl_xor(v, 2);
     v += __shfl_xor(v, 1);
     return v;
@@ -914,18 +902,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6
     // lower index).  A token whose kept candidates are all within tau is rescanned
     // in fp64 over all C.  At D = 16 one lane takes a whole entry (or centroid of a
     // rescan) and sums in the exact definition's order and rounding; wider rows
-    // spread an entry over 16 lanes (a fused fp64 chain per lane, then a butterfly),
-    // which keeps the few entries of a work-group short.
+    // spread an entry over 4 lanes (a fused fp64 chain over D/4 dims per lane, then
+    // a butterfly), so that one pass of loads covers a work-group's entries.
     constexpr int kRQ = 3 * 256;
-    constexpr int DPL = D / 16;  // dims per lane
+    constexpr int DPL = D / 4;  // dims per lane of a 4-lane distance (rows wider than 16)
     __shared__ int rq_n, full_n;
     __shared__ int rq_slot[kRQ];
     __shared__ int rq_cand[kRQ];
     __shared__ double rq_dist[kRQ];
     __shared__ int full_slot[256];
     __shared__ int full_best[256];
-    __shared__ double grp_d[16];
-    __shared__ int grp_j[16];
+    __shared__ double grp_d[4];
+    __shared__ int grp_j[4];
     if (tid == 0) { rq_n = 0; full_n = 0; }
     __syncthreads();
     const float *cb = cent + (int64_t)bh * C * D;
@@ -1001,13 +989,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6
             __syncthreads();
         }
     } else {
-    const int sub = tid & 15, grp = tid >> 4;
+    const int sub = tid & 3, grp = tid >> 2;
     {
         const int nq = rq_n;
-        for (int e = grp; e < nq; e += 16) {
+        for (int e = grp; e < nq; e += 64) {
             const int t = blockIdx.x * 256 + rq_slot[e];
-            const double dd = sum16(seg_sqdist<DPL>(xb + (int64_t)t * xs.t + sub * DPL,
-                                                    cb + (int64_t)rq_cand[e] * D + sub * DPL));
+            const double dd = sum4(seg_sqdist<DPL>(xb + (int64_t)t * xs.t + sub * DPL,
+                                                   cb + (int64_t)rq_cand[e] * D + sub * DPL));
             if (sub == 0) rq_dist[e] = dd;
         }
     }
@@ -1017,16 +1005,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6
         const uint16_t *xr = xb + (int64_t)t * xs.t + sub * DPL;
         double bd = INFINITY;
         int bj = 0;
-        for (int j = grp; j < C; j += 16) {
-            const double dd = sum16(seg_sqdist<DPL>(xr, cb + (int64_t)j * D + sub * DPL));
+        for (int j = grp; j < C; j += 64) {
+            const double dd = sum4(seg_sqdist<DPL>(xr, cb + (int64_t)j * D + sub * DPL));
             if (dd < bd) { bd = dd; bj = j; }
         }
-        if (sub == 0) { grp_d[grp] = bd; grp_j[grp] = bj; }
+        // smallest distance, ties to the lower index: over the wave, then the waves
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const double od = __shfl_xor(bd, off);
+            const int oj = __shfl_xor(bj, off);
+            if (od < bd || (od == bd && oj < bj)) { bd = od; bj = oj; }
+        }
+        if (lane == 0) { grp_d[wave] = bd; grp_j[wave] = bj; }
         __syncthreads();
         if (tid == 0) {
             double b = grp_d[0];
             int jb = grp_j[0];
-            for (int g = 1; g < 16; ++g)
+            for (int g = 1; g < 4; ++g)
                 if (grp_d[g] < b || (grp_d[g] == b && grp_j[g] < jb)) { b = grp_d[g]; jb = grp_j[g]; }
             full_best[f] = jb;
         }
