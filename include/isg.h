@@ -307,7 +307,9 @@ isg_status isg_unpermute(void *stream, const void *o_p, const float *lse_p, cons
  *            between calls.
  * Needs P | d, d/P in {16, 64, 128}, P*B*H <= 65535, 1 <= Cc <= min(N, 4096),
  * iters >= 1; else ISG_E_ARG / ISG_E_UNSUPPORTED / ISG_E_DTYPE / ISG_E_WORKSPACE
- * with nothing launched. */
+ * with nothing launched.  x is expected finite: with an infinity or NaN in it the
+ * codes and codebooks are unspecified (every code still lies in [0, Cc) and every
+ * access stays inside the buffers). */
 size_t isg_pq_codebooks_workspace_size(isg_dtype dt, int B, int H, int N, int d, int P, int Cc);
 isg_status isg_pq_codebooks(void *stream, const void *x, isg_dtype dt, const int64_t x_strides[3], int B, int H,
                             int N, int d, int P, int Cc, int iters, int32_t *codes, float *codebooks,
