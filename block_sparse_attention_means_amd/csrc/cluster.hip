@@ -766,7 +766,8 @@ __device__ __forceinline__ void assign_tile(const uint8_t *cur, int tile, int C,
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const uint32_t j = jb + (r >> 2) * 8 + (r & 3);
-        // rows j and j + 4 both padding (norm 1e30, never kept): skip (a scalar branch)
+        // rows j and j + 4 both padding: skip (a scalar branch; a padding row j + 4
+        // alone is inserted, and the decisions below keep it out)
         if (j >= (uint32_t)C) continue;
         // indices below 256: the key is the distance's upper three bytes and the
         // index byte (one byte permute); else the distance with its low bits
@@ -934,10 +935,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 16 ? 6
         const float res = __uint_as_float((__float_as_uint(lim0) & 0x7F800000u)) * ldexpf(1.0f, ibits - 23);
         const float lim = lim0 + 2.0f * res;
         const int slot = wave * 64 + tb * 32 + l32;
+        // The second half-wave's rows j + 4 of the last tile can be padding while
+        // rows j are not; their keys (norm 1e30) lose to every real distance below
+        // that, but with extreme magnitudes or infinities one could be kept first
+        // or inside the window.  Such a token is rescanned over the real centroids.
         int n = 1;
+        bool pad = (T.k[0] & imask) >= (uint32_t)C;
 #pragma unroll
-        for (int c = 1; c < TK; ++c) n += __uint_as_float(T.k[c] & hi_mask) < lim;
-        if (n == TK) {  // every kept candidate is close: all centroids in fp64
+        for (int c = 1; c < TK; ++c) {
+            const bool in = __uint_as_float(T.k[c] & hi_mask) < lim;
+            n += in;
+            pad = pad || (in && (T.k[c] & imask) >= (uint32_t)C);
+        }
+        if (n == TK || pad) {  // every kept candidate is close: all centroids in fp64
             const int f = atomicAdd(&full_n, 1);
             full_slot[f] = slot;
             fpos[tb] = f;

@@ -91,6 +91,33 @@ def test_cluster_one_round_stagewise(orc, dtype, d, N, C):
         assert torch.equal(r["companion_perm"][0, h].cpu(), v[0, h][torch.from_numpy(perm_o).long()])
 
 
+@pytest.mark.parametrize("d,C", [(16, 30), (16, 29), (16, 285), (128, 30), (128, 61), (128, 285)])
+def test_cluster_padding_rows_never_kept(orc, d, C):
+    """Centroid counts that leave the last 32-row tile partly padding (C mod 32 in
+    28..31: the second half-wave's rows j + 4 fall past C while rows j do not),
+    on zero-mean keys of magnitude ~3e15: most tokens then have every real
+    centroid farther than |x|^2 + 1e30, the padding rows' screening value.  The
+    labels must still be real centroids and the oracle's fp64 argmin (exactly at
+    d = 16, up to fp64 near-ties wider)."""
+    N = 2000
+    say(f"cluster padding rows d={d} C={C}")
+    g = np.random.default_rng(C + d)
+    xb = torch.from_numpy(g.standard_normal((1, 2, N, d)) * 3e15).to(torch.bfloat16)
+    x = f32(xb)
+    src = (np.arange(C) * N) // C
+    r = isg.isg_cluster(xb.to(DEV), C, 1, want_perm=False)
+    torch.cuda.synchronize()
+    for h in range(2):
+        lab_g = npy(r["labels"][0, h])
+        assert lab_g.min() >= 0 and lab_g.max() < C
+        init = x[0, h][src]
+        lab_o = orc.kmeans_assign(x[0, h], init)
+        if d == 16:
+            assert np.array_equal(lab_g, lab_o)
+        else:
+            assert _near_tie_ok(orc, x[0, h], init, lab_g, lab_o)
+
+
 @pytest.mark.parametrize("factor", [100.0, 300.0])
 def test_cluster_large_norms_first_round(orc, factor):
     """Keys scaled by 100-300 (|x|^2 up to ~1e7, so the fp32 screening error of a
