@@ -40,16 +40,6 @@ __device__ __forceinline__ void load8(const float *p, float out[8])
     out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
     out[4] = c.x; out[5] = c.y; out[6] = c.z; out[7] = c.w;
 }
-__device__ __forceinline__ void load8(const uint16_t *p, float out[8])
-{
-    uint4 a = *reinterpret_cast<const uint4 *>(p);
-    uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        out[2 * k] = __uint_as_float(w[k] << 16);
-        out[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-    }
-}
 // 8 elements as loaded (bf16: one 16-byte word; fp32: two), widened when used.
 template <typename T>
 struct Raw8;
