@@ -1009,7 +1009,7 @@ def test_pq_codebooks_strided_and_vs_oracle(orc, B, dtype, P, Cc):
         assert agree == 1.0 and np.array_equal(npy(cbs), ocb)
 
 
-@pytest.mark.parametrize("N,Cc", [(700, 256), (3000, 64), (20000, 200), (5, 3), (8193, 256)])
+@pytest.mark.parametrize("N,Cc", [(700, 256), (3000, 64), (20000, 200), (5, 3), (8193, 256), (140000, 256)])
 def test_pq_codebooks_integer_means_wide_span(N, Cc):
     """The integer-sum update of bf16 16-dim subspaces on values spread over 2^60
     (each element times 2^u, u uniform in [-60, 0]): the fixed-point grid then
