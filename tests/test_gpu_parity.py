@@ -767,15 +767,15 @@ def _lse_report(tag, lg, lo):
 
 
 def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode="importance", max_rows=None,
-                     all_groups_head=None, expect_fallback=None):
+                     all_groups_head=None, expect_fallback=None, top_p=None):
     w = WORKLOADS[name]
     N, d, Cq, Ck = w["N"], w["d"], w["Cq"], w["Ck"]
     say(f"full size {name}: inputs")
     q, k, v = _workload_inputs(name)
     E, m = budget_keys(E_share, N), budget_keys(S_share, N)
-    say(f"full size {name}: pipeline E={E} m={m} mode={mode}")
+    say(f"full size {name}: pipeline E={E} m={m} mode={mode} top_p={top_p}")
     qg, kg, vg = q.to(DEV), k.to(DEV), v.to(DEV)
-    r = isg.pipeline(qg, kg, vg, Cq, Ck, w["iters"], E, m, seed=0, mode=mode, pq=w.get("pq"))
+    r = isg.pipeline(qg, kg, vg, Cq, Ck, w["iters"], E, m, seed=0, mode=mode, pq=w.get("pq"), top_p=top_p)
     torch.cuda.synchronize()
     qo_all = npy(r["cq"]["offsets"])
     ko_all = npy(r["ck"]["offsets"])
@@ -796,8 +796,13 @@ def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode
             assert np.array_equal(perm_o, npy(r[c]["perm"][0, h]))
             assert np.array_equal(off_o, npy(r[c]["offsets"][0, h]))
     # every head: scores, lists, sample indices bit-exact and offsets within 1e-6, from the GPU's centroids
-    S, _ = orc.probs(npy(r["cq"]["centroids"]), npy(r["ck"]["centroids"]), ko_all, r["scale"])
+    S, pi_o = orc.probs(npy(r["cq"]["centroids"]), npy(r["ck"]["centroids"]), ko_all, r["scale"])
     assert np.array_equal(S, npy(r["scores"]))
+    if top_p is not None:
+        # the exact set's size is decided on pi, so both sides decide on the GPU's
+        # pi, which itself is checked against the oracle's
+        pi_g = npy(r["pi"])
+        assert np.abs(pi_g.astype(np.float64) - pi_o).max() <= 1e-6
     votes = None
     if mode == "votes":
         pq = r["pq"]
@@ -815,7 +820,11 @@ def _full_size_check(orc, name, E_share, S_share, heads, groups_per_head=3, mode
                               qo_all[:, hs, i0:i0 + 4], ko_all[:, hs], E)
             say(f"  head {h}: PQ votes of groups {i0}..{i0 + 2} vs the oracle")
             assert np.array_equal(vo[0, 0], votes[0, h, i0:i0 + 3])
-    sel = orc.select_sample(S, ko_all, N, E, m, seed=0, mode=isg.MODES[mode], votes=votes)
+    if top_p is not None:
+        sel = orc.select_sample_topp(S, pi_g, ko_all, N, top_p, m, seed=0, mode=isg.MODES[mode])
+        say(f"  top-p {top_p}: exact key groups per query group {int(np.median(sel['n_exact']))} (median)")
+    else:
+        sel = orc.select_sample(S, ko_all, N, E, m, seed=0, mode=isg.MODES[mode], votes=votes)
     for key in ("exact_groups", "n_exact", "n_sample"):
         assert np.array_equal(sel[key], npy(r["sel"][key])), key
     written = np.arange(max(m, 1))[None, None, None, :] < sel["n_sample"][..., None]
@@ -872,6 +881,11 @@ def test_full_size_14b_720p_sweep(orc, share):
     """The budget sweep's ends at the headline shape: 4+4 % (m = 3,024) and 32+32 %
     (m = 24,192 draws per query group)."""
     _full_size_check(orc, "wan14b_720p", share, share, heads=[0, 20, 39], groups_per_head=4)
+
+
+def test_full_size_14b_720p_topp(orc):
+    """Top-p sizing (p = 0.9) with an 8 % sample at the headline shape."""
+    _full_size_check(orc, "wan14b_720p", 0.0, 0.08, heads=[0, 39], groups_per_head=4, top_p=0.9)
 
 
 def test_full_size_14b_720p_wide_norms(orc):
