@@ -883,6 +883,11 @@ def test_full_size_14b_720p_sweep(orc, share):
     _full_size_check(orc, "wan14b_720p", share, share, heads=[0, 20, 39], groups_per_head=4)
 
 
+def test_full_size_14b_720p_uniform(orc):
+    """The uniform variant (every skipped key equally likely) at the headline shape, 8+8 %."""
+    _full_size_check(orc, "wan14b_720p", 0.08, 0.08, heads=[0, 39], groups_per_head=4, mode="uniform")
+
+
 def test_full_size_14b_720p_topp(orc):
     """Top-p sizing (p = 0.9) with an 8 % sample at the headline shape."""
     _full_size_check(orc, "wan14b_720p", 0.0, 0.08, heads=[0, 39], groups_per_head=4, top_p=0.9)
