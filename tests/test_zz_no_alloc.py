@@ -61,3 +61,38 @@ def test_noalloc_given_centroids_and_strided_input():
         isg.isg_cluster_noalloc(xs, C, 2, out, init_given=True)
         torch.cuda.synchronize()
         _compare(ref, out, ("centroids", "labels", "perm", "offsets"))
+
+
+def test_noalloc_under_graph_capture():
+    """A caller under graph capture: isg_cluster_noalloc recorded into a HIP graph
+    (the call only launches kernels: no allocation, copy or memset), replayed three
+    times.  Before each replay the outputs are overwritten and an eager call on
+    another shape leaves other contents in the shared scratch; every replay equals
+    the workspace call bit for bit."""
+    keys = ("centroids", "labels", "perm", "offsets", "x_perm", "companion_perm", "max_sqnorm")
+    H, N, C, iters = 2, 6000, 64, 3
+    say(f"noalloc graph capture H={H} N={N} C={C} iters={iters}")
+    x, v = _inputs(H, N, 128, "bf16", 7)
+    ref = isg.isg_cluster(x, C, iters, companion=v, want_max_sqnorm=True)
+    out = isg.cluster_outputs(x, C, companion=v, want_max_sqnorm=True)
+    isg.isg_cluster_noalloc(x, C, iters, out, companion=v)  # eager first: the scratch address is looked up
+    torch.cuda.synchronize()
+    _compare(ref, out, keys)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        isg.isg_cluster_noalloc(x, C, iters, out, companion=v)
+    torch.cuda.synchronize()
+    x2, v2 = _inputs(1, 2500, 128, "bf16", 8)
+    out2 = isg.cluster_outputs(x2, 20, companion=v2, want_max_sqnorm=True)
+    for rep in range(3):
+        for t in out.values():
+            if t is not None:
+                t.fill_(3)
+        isg.isg_cluster_noalloc(x2, 20, 2, out2, companion=v2)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        _compare(ref, out, keys)
